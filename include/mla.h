@@ -1,0 +1,256 @@
+/*
+ * mla.h -- C ABI of the MLA latent-KV decode library (MI355X / gfx950).
+ *
+ * Single-token decode of Multi-head Latent Attention with weight absorption,
+ * split into the four calls the source pages' per-layer flow is made of:
+ *
+ *   mla_cache_append  kv_a projection -> RMSNorm of the latent half -> YaRN
+ *                     RoPE of k_pe (consecutive pairs) -> one rounded row
+ *                     written into a paged cache slot.
+ *   mla_absorb_q      optional q chain (q_a -> RMSNorm -> q_b), then
+ *                     q' = W_UK^T q_nope per head and RoPE of q_pe, packed
+ *                     as q_abs = [q' ; q_pe] rows.
+ *   mla_decode_attn   scores of q_abs against every cached row [c_kv ; k_pe],
+ *                     scaled softmax, v_combine = sum_t p_t c_kv[t]; split-K
+ *                     over rows with an online-softmax combine.
+ *   mla_out_proj      out_h = W_UV_h v_combine_h, then optionally o_proj.
+ *
+ * Sources (page title and item):
+ *   moeflux 0.1.0-pre.3, src/riir/attn/mla_attn_forward.rs --
+ *     mla_attn_layer_forward_gpu (the step order, one command buffer, the
+ *     caller owns the pre-norm and the residual, len bumped after append),
+ *     MlaForwardGpuError (error taxonomy), MlaYarnTables (YaRN table + mscale).
+ *   turbospark-runtime 0.3.0, src/families/deepseek2/attn.rs --
+ *     encode_mla_attention_block (fused cache row [latent ; k_pe], in-place
+ *     norm and rope, absorb into fused q_abs rows, MQA decode over pos+1 rows,
+ *     v-combine, o_proj), validate_q8_0_matrix (validate before any kernel
+ *     receives a raw offset).
+ *   moeflux 0.1.0-pre.3, src/riir/backend/gpu/gpu_matvec.rs -- MatvecSpec
+ *     (4-bit affine weights: packed nibbles, bf16 scales and biases, group 64;
+ *     caller-owned input/output buffers).
+ *
+ * Conventions for every call
+ *   - Pointers marked "device" are HIP device addresses; "host" are CPU
+ *     addresses read before the call returns.  The caller owns every buffer
+ *     (inputs, outputs, the cache pool, block table, lengths and workspace);
+ *     the library allocates nothing, keeps no state and never synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     Device buffers must stay valid until that work completes.
+ *   - Every argument is validated on the host first.  On any error the call
+ *     returns a negative MLA_ERR_* code and enqueues nothing, except
+ *     MLA_ERR_HIP, which reports a launch failure after validation passed.
+ *   - Layouts are row-major and dense.  bf16 values are raw 16-bit patterns.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes (MlaForwardGpuError, mapped to integers) ---- */
+enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL (CacheNotReady, MissingTensor) */
+  MLA_ERR_DIMS = -2,        /* inconsistent or out-of-range sizes (shape checks) */
+  MLA_ERR_DTYPE = -3,       /* a dtype code this call does not take */
+  MLA_ERR_UNSUPPORTED = -4, /* valid dims with no compiled kernel (NotMlaVariant) */
+  MLA_ERR_CAPACITY = -5,    /* max_seq_len exceeds the block table (CacheFull) */
+  MLA_ERR_WORKSPACE = -6,   /* workspace pointer NULL or smaller than required */
+  MLA_ERR_HIP = -7          /* a kernel launch failed */
+};
+
+/* ---- element types ---- */
+enum {
+  MLA_F32 = 0,   /* IEEE float32 */
+  MLA_BF16 = 1,  /* bfloat16 bit patterns (uint16) */
+  MLA_Q4G64 = 2  /* 4-bit affine, group 64 along the input dim (weights only) */
+};
+
+/* ---- device status flags OR-ed by mla_cache_append (dev_status) ---- */
+enum {
+  MLA_DEV_POS_RANGE = 1,  /* positions[b] < 0 or >= max_blocks_per_seq * block_size */
+  MLA_DEV_BAD_BLOCK = 2   /* block_table entry for that row is < 0 or >= num_blocks */
+};
+
+/* Model geometry.  W = kv_lora + qk_rope is the cache row width. */
+typedef struct mla_dims {
+  int32_t num_heads;   /* H: query heads */
+  int32_t qk_nope;     /* N: per-head no-position query/key dims */
+  int32_t qk_rope;     /* R: rotary dims (even) */
+  int32_t v_head;      /* V: per-head value dims */
+  int32_t kv_lora;     /* C: latent (compressed KV) dims */
+  int32_t hidden;      /* model width; 0 = the projections are not used */
+  int32_t q_lora;      /* q LoRA rank; 0 = q is given directly */
+  int32_t block_size;  /* rows per cache block (paged pool) */
+  int32_t cache_dtype; /* MLA_F32 or MLA_BF16: cache rows and q_abs */
+  float rms_eps;       /* RMSNorm epsilon */
+} mla_dims;
+
+/* A weight matrix [rows (outputs), cols (inputs)], row-major.
+ *   MLA_F32 : data = float [rows, cols]
+ *   MLA_BF16: data = uint16 [rows, cols]
+ *   MLA_Q4G64: data = uint32 [rows, cols/8]; element k of a row sits in word
+ *     k/8 at bits 4*(k%8)..+3 (low nibble first); scales, biases = bf16
+ *     [rows, cols/64]; w = scale * nibble + bias.
+ * A norm weight (gamma) is passed as a 1 x n matrix of MLA_F32 or MLA_BF16.
+ * All pointers are device pointers. */
+typedef struct mla_weight {
+  int32_t dtype;
+  int32_t rows;
+  int32_t cols;
+  const void* data;
+  const uint16_t* scales;
+  const uint16_t* biases;
+} mla_weight;
+
+/* RoPE table: inv_freq = device float [qk_rope/2]; the rotation is
+ * multiplied by mscale. */
+typedef struct mla_rope {
+  const float* inv_freq;
+  float mscale;
+} mla_rope;
+
+/* Paged latent cache.  pool = device [num_blocks, block_size, W] of
+ * cache_dtype; block_table = device int32 [batch, max_blocks_per_seq]:
+ * logical row t of sequence b lives at pool[block_table[b][t / block_size]]
+ * [t % block_size].  A contiguous cache is the identity table. */
+typedef struct mla_cache {
+  void* pool;
+  const int32_t* block_table;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+} mla_cache;
+
+/* YaRN parameters (MlaYarnTables): theta, scaling factor, original context,
+ * beta_fast, beta_slow, mscale, mscale_all_dim. */
+typedef struct mla_yarn {
+  double theta;
+  double factor;
+  double original_max_pos;
+  double beta_fast;
+  double beta_slow;
+  double mscale;
+  double mscale_all_dim;
+} mla_yarn;
+
+/* mla_yarn_tables -- host helper: the YaRN inverse frequencies and scalars
+ * (moeflux mla_attn_forward.rs, MlaYarnTables::new; turbospark gptoss/attn.rs
+ * module doc, the ramp between two correction dimensions; turbospark
+ * deepseek2/attn.rs, the softmax scale (1 + 0.1 mscale ln factor)^2 /
+ * sqrt(key_dim)).
+ *   inv_freq_host  host float [qk_rope/2], written
+ *   rope_mscale    host float, written: get(factor, mscale)/get(factor, mscale_all_dim)
+ *   softmax_scale  host float, written: get(factor, mscale_all_dim)^2 / sqrt(qk_head_dim)
+ * where get(s, m) = 1 + 0.1 m ln s for s > 1, else 1.  Any output may be NULL.
+ * Errors: MLA_ERR_NULL (p), MLA_ERR_DIMS (qk_rope odd or < 2, qk_head_dim < 1,
+ * theta <= 1, factor <= 0, original_max_pos <= 0, beta_fast/beta_slow <= 0). */
+int mla_yarn_tables(const mla_yarn* p, int32_t qk_rope, int32_t qk_head_dim,
+                    float* inv_freq_host, float* rope_mscale, float* softmax_scale);
+
+/* mla_cache_append -- write the new row of each sequence into its slot
+ * (moeflux mla_attn_forward.rs: KV-A chain, kv_a_layernorm, YaRN rope on
+ * k_pe, mla_kv_cache_append; turbospark deepseek2/attn.rs: kv_a writes the
+ * fused row, then in-place latent norm and windowed k_pe rope).
+ *   x          device float [batch, hidden]; when dims->hidden == 0 it is the
+ *              pre-norm row itself, float [batch, W]
+ *   kv_a       [W, hidden] weight (F32, BF16 or Q4G64); ignored if hidden == 0
+ *   kv_a_norm  1 x C gamma (F32 or BF16)
+ *   rope       k_pe rotation table and multiplier
+ *   positions  device int32 [batch]: the row written for sequence b
+ *   cache      pool and block table (written: one row per sequence)
+ *   dev_status device int32, may be NULL: rows whose position or block is
+ *              out of range are skipped and MLA_DEV_* flags OR-ed in
+ *   ws         device workspace of at least mla_workspace_bytes() bytes
+ * The row is y = [gamma * c / sqrt(mean(c^2) + eps) ; mscale * RoPE(k_pe, pos)]
+ * with [c ; k_pe] = W_kva x, computed in fp32 (angles in fp64) and rounded
+ * once to cache_dtype (round to nearest even).  The caller advances its
+ * sequence lengths afterwards.
+ * Errors: NULL, DIMS (batch < 0, shapes, block_size < 1), DTYPE, WORKSPACE. */
+int mla_cache_append(const mla_dims* dims, int32_t batch, const float* x,
+                     const mla_weight* kv_a, const mla_weight* kv_a_norm,
+                     const mla_rope* rope, const int32_t* positions,
+                     const mla_cache* cache, int32_t* dev_status,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* mla_absorb_q -- fused latent query rows (moeflux mla_attn_forward.rs: Q
+ * chain, mla_q_prime_4bit; turbospark deepseek2/attn.rs: q_pe roped before
+ * encode_mla_absorb_q gathers [q' ; q_pe]).
+ *   q_in       device float: [batch, H, N+R] when q_a is NULL, else the
+ *              pre-norm hidden state [batch, hidden]
+ *   q_a        [q_lora, hidden] Q-LoRA down projection or NULL
+ *   q_a_norm   1 x q_lora gamma (required with q_a)
+ *   q_b        [H*(N+R), q_lora] up projection (required with q_a)
+ *   kv_b       [H*(N+V), C]: head h owns rows h*(N+V)..+N-1 (W_UK) then V
+ *              rows (W_UV)
+ *   positions  device int32 [batch]: rotation position of each query
+ *   q_abs      device [batch, H, W] of cache_dtype, written:
+ *              q_abs[b,h,:C] = sum_n W_UK[h,n,:] q_nope[b,h,n] (fp32
+ *              accumulate), q_abs[b,h,C:] = mscale * RoPE(q_pe[b,h], pos)
+ * Errors: NULL, DIMS, DTYPE, WORKSPACE. */
+int mla_absorb_q(const mla_dims* dims, int32_t batch, const float* q_in,
+                 const mla_weight* q_a, const mla_weight* q_a_norm,
+                 const mla_weight* q_b, const mla_weight* kv_b,
+                 const mla_rope* rope, const int32_t* positions, void* q_abs,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* mla_decode_attn -- MQA decode over the compressed rows (moeflux
+ * mla_attn_forward.rs: mla_sdpa_folded; turbospark deepseek2/attn.rs:
+ * encode_mla_attention_decode, V = the row's first C values).
+ *   q_abs        device [batch, H, W] of cache_dtype
+ *   cache        pool + block table (read only)
+ *   seq_lens     device int32 [batch]: rows attended per sequence (after
+ *                the append); 0 gives v_combine = 0 and lse = -inf
+ *   max_seq_len  host: upper bound of seq_lens (sizes the split grid);
+ *                values above it are clamped to it on the device
+ *   softmax_scale  multiplies the fp32 scores
+ *   split_rows   rows per split-K partition (multiple of 64), 0 = automatic
+ *   v_combine    device float [batch, H, C], written
+ *   lse          device float [batch, H] or NULL: natural-log sum of exp of
+ *                the scaled scores
+ * bf16 caches run on the MFMA kernel (H = 128, C = 512, R = 64, block_size a
+ * multiple of 32); f32 caches on a VALU kernel of any shape.
+ * Errors: NULL, DIMS (max_seq_len < 0, split_rows), UNSUPPORTED, CAPACITY
+ * (max_seq_len > max_blocks_per_seq * block_size), WORKSPACE. */
+int mla_decode_attn(const mla_dims* dims, int32_t batch, const void* q_abs,
+                    const mla_cache* cache, const int32_t* seq_lens,
+                    int32_t max_seq_len, float softmax_scale, int32_t split_rows,
+                    float* v_combine, float* lse, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* mla_out_proj -- per-head expansion and output projection (moeflux
+ * mla_attn_forward.rs: mla_out_per_head_4bit then o_proj; turbospark
+ * deepseek2/attn.rs: encode_mla_v_combine then O_PROJ; the caller adds the
+ * residual).
+ *   v_combine  device float [batch, H, C]
+ *   kv_b       as in mla_absorb_q (W_UV rows are read)
+ *   o_proj     [hidden, H*V] or NULL
+ *   out        device float: [batch, H, V] when o_proj is NULL, else
+ *              [batch, hidden]
+ * Errors: NULL, DIMS, DTYPE, WORKSPACE. */
+int mla_out_proj(const mla_dims* dims, int32_t batch, const float* v_combine,
+                 const mla_weight* kv_b, const mla_weight* o_proj, float* out,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace that covers every call above for this geometry, batch,
+ * max_seq_len and split_rows (0 = automatic).  Returns 0 for invalid dims. */
+size_t mla_workspace_bytes(const mla_dims* dims, int32_t batch,
+                           int32_t max_seq_len, int32_t split_rows);
+
+/* The split-K plan mla_decode_attn would use: rows per split and splits per
+ * sequence.  Returns MLA_OK or an error code. */
+int mla_attn_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
+                  int32_t split_rows, int32_t* rows_per_split,
+                  int32_t* num_splits);
+
+/* Human-readable text for a status code (static storage). */
+const char* mla_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,428 @@
+// C ABI of the MLA decode library: host-side validation, workspace layout,
+// split-K planning and kernel launches.  Nothing here allocates or
+// synchronises; every check runs before the first launch
+// (turbospark deepseek2/attn.rs, validate_q8_0_matrix: validate before any
+// kernel receives a raw offset; moeflux mla_attn_forward.rs,
+// MlaForwardGpuError: the error taxonomy).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "mla_common.h"
+
+int attn_mfma_max_split_rows();
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDim = 1 << 16;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool dims_ok(const mla_dims* d) {
+  if (!d) return false;
+  if (d->num_heads < 1 || d->qk_nope < 0 || d->qk_rope < 2 || (d->qk_rope & 1) ||
+      d->v_head < 1 || d->kv_lora < 1 || d->hidden < 0 || d->q_lora < 0 || d->block_size < 1)
+    return false;
+  if (d->num_heads > kMaxDim || d->qk_nope > kMaxDim || d->qk_rope > kMaxDim ||
+      d->v_head > kMaxDim || d->kv_lora > kMaxDim || d->hidden > (1 << 20) ||
+      d->q_lora > (1 << 20) || d->block_size > (1 << 20))
+    return false;
+  if (d->cache_dtype != MLA_F32 && d->cache_dtype != MLA_BF16) return false;
+  if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return false;
+  return true;
+}
+
+int dims_status(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->cache_dtype != MLA_F32 && d->cache_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  return dims_ok(d) ? MLA_OK : MLA_ERR_DIMS;
+}
+
+// A weight must be non-null, of an accepted dtype, and exactly [rows, cols].
+int check_weight(const mla_weight* w, int64_t rows, int64_t cols, bool allow_q4) {
+  if (!w || !w->data) return MLA_ERR_NULL;
+  if (w->dtype != MLA_F32 && w->dtype != MLA_BF16 && !(allow_q4 && w->dtype == MLA_Q4G64))
+    return MLA_ERR_DTYPE;
+  if (w->rows != rows || w->cols != cols) return MLA_ERR_DIMS;
+  if (w->dtype == MLA_Q4G64) {
+    if (cols % 64 != 0) return MLA_ERR_DIMS;
+    if (!w->scales || !w->biases) return MLA_ERR_NULL;
+  }
+  return MLA_OK;
+}
+
+WeightView view(const mla_weight* w) {
+  return WeightView{w->dtype, w->rows, w->cols, w->data, w->scales, w->biases};
+}
+
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int max_split_rows(const mla_dims* d) {
+  return d->cache_dtype == MLA_BF16 ? attn_mfma_max_split_rows() : (1 << 30);
+}
+
+// Rows per split and splits per sequence.  Automatic: about one workgroup per
+// compute unit over batch * max_seq_len rows, at least 256 rows per split.
+int plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t req, int32_t* rows,
+         int32_t* splits) {
+  if (max_len < 0 || batch < 0) return MLA_ERR_DIMS;
+  if (req < 0 || (req % 64) != 0) return MLA_ERR_DIMS;
+  const int64_t cap = max_split_rows(d);
+  int64_t r;
+  if (req > 0) {
+    if (req > cap) return MLA_ERR_DIMS;
+    r = req;
+  } else {
+    const int64_t total = (int64_t)(batch > 0 ? batch : 1) * (max_len > 0 ? max_len : 1);
+    const int64_t cus = device_cus();
+    r = (total + cus - 1) / cus;
+    r = (r + 63) / 64 * 64;
+    if (r < 256) r = 256;
+    if (r > cap) r = cap / 64 * 64;
+  }
+  int64_t s = max_len > 0 ? (max_len + r - 1) / r : 1;
+  if (s < 1) s = 1;
+  if (s > (1 << 20)) return MLA_ERR_DIMS;
+  *rows = (int32_t)r;
+  *splits = (int32_t)s;
+  return MLA_OK;
+}
+
+size_t ws_append(const mla_dims* d, int32_t B) {
+  return d->hidden > 0 ? align_up((size_t)B * (d->kv_lora + d->qk_rope) * 4) : 0;
+}
+size_t ws_absorb(const mla_dims* d, int32_t B) {
+  if (d->q_lora <= 0) return 0;
+  return align_up((size_t)B * d->q_lora * 4) +
+         align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4);
+}
+size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
+  if (splits <= 1) return 0;
+  return align_up((size_t)B * splits * d->num_heads * d->kv_lora * 4) +
+         align_up((size_t)B * splits * d->num_heads * 4);
+}
+size_t ws_out(const mla_dims* d, int32_t B) {
+  return d->hidden > 0 ? align_up((size_t)B * d->num_heads * d->v_head * 4) : 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+double yarn_get(double s, double m) { return s <= 1.0 ? 1.0 : 0.1 * m * log(s) + 1.0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(int st) {
+  switch (st) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_DIMS: return "inconsistent or out-of-range dimensions";
+    case MLA_ERR_DTYPE: return "unsupported element type";
+    case MLA_ERR_UNSUPPORTED: return "no kernel for these dimensions";
+    case MLA_ERR_CAPACITY: return "max_seq_len exceeds the block table capacity";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mla_yarn_tables(const mla_yarn* p, int32_t R, int32_t qk_head_dim, float* inv_freq,
+                    float* rope_mscale, float* softmax_scale) {
+  if (!p) return MLA_ERR_NULL;
+  if (R < 2 || (R & 1) || R > kMaxDim || qk_head_dim < 1 || !(p->theta > 1.0) ||
+      !(p->factor > 0.0) || !(p->original_max_pos > 0.0) || !(p->beta_fast > 0.0) ||
+      !(p->beta_slow > 0.0))
+    return MLA_ERR_DIMS;
+  if (inv_freq) {
+    // Correction dimension: the pair index whose rotation count over the
+    // original context equals r.
+    const double two_pi = 6.283185307179586476925;
+    auto corr = [&](double r) {
+      return (double)R * log(p->original_max_pos / (r * two_pi)) / (2.0 * log(p->theta));
+    };
+    double lo = floor(corr(p->beta_fast));
+    double hi = ceil(corr(p->beta_slow));
+    if (lo < 0) lo = 0;
+    if (hi > R - 1) hi = R - 1;
+    if (lo == hi) hi += 0.001;
+    for (int i = 0; i < R / 2; ++i) {
+      const double base = pow(p->theta, -2.0 * i / (double)R);
+      double ramp = (i - lo) / (hi - lo);
+      ramp = ramp < 0 ? 0 : (ramp > 1 ? 1 : ramp);
+      inv_freq[i] = (float)(base * (1.0 - ramp) + (base / p->factor) * ramp);
+    }
+  }
+  const double m = yarn_get(p->factor, p->mscale);
+  const double m_all = yarn_get(p->factor, p->mscale_all_dim);
+  if (rope_mscale) *rope_mscale = (float)(m / m_all);
+  if (softmax_scale) *softmax_scale = (float)(m_all * m_all / sqrt((double)qk_head_dim));
+  return MLA_OK;
+}
+
+size_t mla_workspace_bytes(const mla_dims* d, int32_t B, int32_t max_len, int32_t split_rows) {
+  if (!dims_ok(d) || B < 0) return 0;
+  int32_t rows = 0, splits = 1;
+  if (plan(d, B, max_len, split_rows, &rows, &splits) != MLA_OK) return 0;
+  size_t w = ws_append(d, B);
+  w = w > ws_absorb(d, B) ? w : ws_absorb(d, B);
+  w = w > ws_attn(d, B, splits) ? w : ws_attn(d, B, splits);
+  w = w > ws_out(d, B) ? w : ws_out(d, B);
+  return w + kAlign;
+}
+
+int mla_attn_plan(const mla_dims* d, int32_t B, int32_t max_len, int32_t split_rows,
+                  int32_t* rows_per_split, int32_t* num_splits) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (!rows_per_split || !num_splits) return MLA_ERR_NULL;
+  return plan(d, B, max_len, split_rows, rows_per_split, num_splits);
+}
+
+int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_weight* kv_a,
+                     const mla_weight* kv_a_norm, const mla_rope* rope, const int32_t* positions,
+                     const mla_cache* cache, int32_t* dev_status, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (B < 0) return MLA_ERR_DIMS;
+  const int W = d->kv_lora + d->qk_rope;
+  if (!x || !rope || !rope->inv_freq || !positions || !cache || !cache->pool ||
+      !cache->block_table)
+    return MLA_ERR_NULL;
+  if (cache->num_blocks < 1 || cache->max_blocks_per_seq < 1) return MLA_ERR_DIMS;
+  if ((st = check_weight(kv_a_norm, 1, d->kv_lora, false))) return st;
+  if (d->hidden > 0 && (st = check_weight(kv_a, W, d->hidden, true))) return st;
+  const size_t need = ws_append(d, B);
+  if (need && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (B == 0) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const float* kv_pre = x;
+  if (d->hidden > 0) {
+    GemmArgs g{};
+    g.w = view(kv_a);
+    g.x = x;
+    g.x_b = d->hidden;
+    g.y = static_cast<float*>(ws);
+    g.y_b = W;
+    g.O = W;
+    g.K = d->hidden;
+    g.B = B;
+    g.Z = 1;
+    if ((st = hip_status(launch_gemm_nt(g, s)))) return st;
+    kv_pre = static_cast<const float*>(ws);
+  }
+  AppendArgs a{};
+  a.kv_pre = kv_pre;
+  a.gamma = view(kv_a_norm);
+  a.inv_freq = rope->inv_freq;
+  a.rope_mscale = rope->mscale;
+  a.positions = positions;
+  a.pool = cache->pool;
+  a.table = cache->block_table;
+  a.dev_status = dev_status;
+  a.B = B;
+  a.C = d->kv_lora;
+  a.R = d->qk_rope;
+  a.block = d->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  a.num_blocks = cache->num_blocks;
+  a.cache_dtype = d->cache_dtype;
+  a.eps = d->rms_eps;
+  return hip_status(launch_append_rows(a, s));
+}
+
+int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weight* q_a,
+                 const mla_weight* q_a_norm, const mla_weight* q_b, const mla_weight* kv_b,
+                 const mla_rope* rope, const int32_t* positions, void* q_abs, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (B < 0) return MLA_ERR_DIMS;
+  const int H = d->num_heads, N = d->qk_nope, R = d->qk_rope, V = d->v_head, C = d->kv_lora;
+  if (N < 1 || N > 4096) return MLA_ERR_DIMS;
+  if (!q_in || !rope || !rope->inv_freq || !positions || !q_abs) return MLA_ERR_NULL;
+  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true))) return st;
+  if (q_a) {
+    if (d->q_lora < 1 || d->hidden < 1) return MLA_ERR_DIMS;
+    if ((st = check_weight(q_a, d->q_lora, d->hidden, true))) return st;
+    if ((st = check_weight(q_a_norm, 1, d->q_lora, false))) return st;
+    if ((st = check_weight(q_b, (int64_t)H * (N + R), d->q_lora, true))) return st;
+    const size_t need = ws_absorb(d, B);
+    if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  } else if (q_b) {
+    return MLA_ERR_DIMS;  // q_b without q_a
+  }
+  if (B == 0) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const float* q = q_in;
+  if (q_a) {
+    float* q_lat = static_cast<float*>(ws);
+    float* q_full = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * d->q_lora * 4));
+    GemmArgs g{};
+    g.w = view(q_a);
+    g.x = q_in;
+    g.x_b = d->hidden;
+    g.y = q_lat;
+    g.y_b = d->q_lora;
+    g.O = d->q_lora;
+    g.K = d->hidden;
+    g.B = B;
+    g.Z = 1;
+    if ((st = hip_status(launch_gemm_nt(g, s)))) return st;
+    if ((st = hip_status(launch_rmsnorm_rows(q_lat, B, d->q_lora, d->q_lora, view(q_a_norm),
+                                             d->rms_eps, s))))
+      return st;
+    GemmArgs g2{};
+    g2.w = view(q_b);
+    g2.x = q_lat;
+    g2.x_b = d->q_lora;
+    g2.y = q_full;
+    g2.y_b = (int64_t)H * (N + R);
+    g2.O = H * (N + R);
+    g2.K = d->q_lora;
+    g2.B = B;
+    g2.Z = 1;
+    if ((st = hip_status(launch_gemm_nt(g2, s)))) return st;
+    q = q_full;
+  }
+  AbsorbArgs a{};
+  a.q = q;
+  a.kv_b = view(kv_b);
+  a.inv_freq = rope->inv_freq;
+  a.rope_mscale = rope->mscale;
+  a.positions = positions;
+  a.q_abs = q_abs;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.R = R;
+  a.V = V;
+  a.C = C;
+  a.cache_dtype = d->cache_dtype;
+  return hip_status(launch_absorb(a, s));
+}
+
+int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_cache* cache,
+                    const int32_t* seq_lens, int32_t max_len, float softmax_scale,
+                    int32_t split_rows, float* v_combine, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (B < 0 || max_len < 0) return MLA_ERR_DIMS;
+  if (!q_abs || !cache || !cache->pool || !cache->block_table || !seq_lens || !v_combine)
+    return MLA_ERR_NULL;
+  if (cache->num_blocks < 1 || cache->max_blocks_per_seq < 1) return MLA_ERR_DIMS;
+  if (!isfinite(softmax_scale)) return MLA_ERR_DIMS;
+  if ((int64_t)max_len > (int64_t)cache->max_blocks_per_seq * d->block_size) return MLA_ERR_CAPACITY;
+  const bool bf16 = d->cache_dtype == MLA_BF16;
+  if (bf16) {
+    if (d->num_heads != 128 || d->kv_lora != 512 || d->qk_rope != 64 || (d->block_size % 32) != 0)
+      return MLA_ERR_UNSUPPORTED;
+  } else {
+    if (d->kv_lora > 1024 || d->kv_lora + d->qk_rope > 8192 || (d->kv_lora % 4) != 0)
+      return MLA_ERR_UNSUPPORTED;
+  }
+  int32_t rows = 0, splits = 1;
+  if ((st = plan(d, B, max_len, split_rows, &rows, &splits))) return st;
+  const size_t need = ws_attn(d, B, splits);
+  if (need && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (B == 0) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  AttnArgs a{};
+  a.q_abs = q_abs;
+  a.pool = cache->pool;
+  a.table = cache->block_table;
+  a.seq_lens = seq_lens;
+  a.v_combine = v_combine;
+  a.lse = lse;
+  a.part_o = static_cast<float*>(ws);
+  a.part_lse = splits > 1
+                   ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              align_up((size_t)B * splits * d->num_heads * d->kv_lora * 4))
+                   : nullptr;
+  a.B = B;
+  a.H = d->num_heads;
+  a.C = d->kv_lora;
+  a.R = d->qk_rope;
+  a.block = d->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  a.num_blocks = cache->num_blocks;
+  a.max_len = max_len;
+  a.split_rows = rows;
+  a.num_splits = splits;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  st = hip_status(bf16 ? launch_attn_mfma_bf16(a, s) : launch_attn_generic_f32(a, s));
+  if (st) return st;
+  if (splits > 1) st = hip_status(launch_attn_combine(a, s));
+  return st;
+}
+
+int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla_weight* kv_b,
+                 const mla_weight* o_proj, float* out, void* ws, size_t ws_bytes, void* stream) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (B < 0) return MLA_ERR_DIMS;
+  const int H = d->num_heads, N = d->qk_nope, V = d->v_head, C = d->kv_lora;
+  if (!v_combine || !out) return MLA_ERR_NULL;
+  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true))) return st;
+  if (o_proj) {
+    if (d->hidden < 1) return MLA_ERR_DIMS;
+    if ((st = check_weight(o_proj, d->hidden, (int64_t)H * V, true))) return st;
+    if (!ws || ws_bytes < ws_out(d, B)) return MLA_ERR_WORKSPACE;
+  }
+  if (B == 0) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* heads_out = o_proj ? static_cast<float*>(ws) : out;
+  GemmArgs g{};
+  g.w = view(kv_b);
+  g.w_row0 = N;
+  g.w_zrows = N + V;
+  g.x = v_combine;
+  g.x_b = (int64_t)H * C;
+  g.x_z = C;
+  g.y = heads_out;
+  g.y_b = (int64_t)H * V;
+  g.y_z = V;
+  g.O = V;
+  g.K = C;
+  g.B = B;
+  g.Z = H;
+  if ((st = hip_status(launch_gemm_nt(g, s)))) return st;
+  if (o_proj) {
+    GemmArgs g2{};
+    g2.w = view(o_proj);
+    g2.x = heads_out;
+    g2.x_b = (int64_t)H * V;
+    g2.y = out;
+    g2.y_b = d->hidden;
+    g2.O = d->hidden;
+    g2.K = H * V;
+    g2.B = B;
+    g2.Z = 1;
+    st = hip_status(launch_gemm_nt(g2, s));
+  }
+  return st;
+}
+
+}  // extern "C"

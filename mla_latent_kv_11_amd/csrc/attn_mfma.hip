@@ -1,0 +1,409 @@
+// MLA decode attention over a paged bf16 latent cache, bf16 MFMA on gfx950.
+//
+// Computes, per sequence b and query head h (moeflux mla_attn_forward.rs,
+// mla_sdpa_folded; turbospark deepseek2/attn.rs, encode_mla_attention_decode):
+//   s[t]   = scale * q_abs[b,h,:] . row_t            (row_t = [c_kv ; k_pe], 576 wide)
+//   p      = softmax over t < len_b
+//   v[h,:] = sum_t p[t] * row_t[:512]                (V is the row's first 512)
+// Every head reads the same rows (MQA over the compressed cache), so the 128
+// heads are the MFMA's free dimension: one workgroup of 4 waves streams a range
+// of rows once through LDS and each wave multiplies its 32 heads against it.
+//
+// Per 32-row tile and wave:
+//   S^T[t][h] = K[t][:] . Q^T[:][h]   36 x mfma_f32_32x32x16_bf16 (A = K from LDS,
+//                                      B = the wave's 32 q_abs rows kept in VGPRs)
+//   softmax numerators in fp32, one head per lane, exp2 domain, against a
+//                                      per-head reference max (restart if exceeded)
+//   O^T[c][h] += V^T[c][t] . P^T[t][h] 32 x mfma (A = V^T via LDS transpose
+//                                      reads, B = P^T straight from the S^T registers)
+// The fp32 accumulator O^T (32 heads x 512) lives in the 256 AGPRs of each
+// lane (one head per lane); the resident Q (144 VGPRs), scores and fragments
+// share the 256 VGPRs.  O is only ever touched by MFMAs inside the loop.
+//
+// Tiles stream HBM -> LDS with 16-byte direct-to-LDS loads, three buffers deep.
+// The LDS tile is 32 rows x 72 sixteen-byte granules with an XOR swizzle of the
+// granule index inside each aligned group of 8, chosen so that both the
+// row-wise K reads (16 rows, one granule each) and the transpose V reads (4
+// rows x 4 granules per 32 lanes) hit 16 distinct 16-byte bank groups.
+//
+// Split-K (flash decoding): grid = (splits, batch). A split with a single
+// partition writes v_combine/lse directly; otherwise it writes the normalised
+// partial O and its lse, merged by attn_combine_kernel.
+#include <math.h>
+
+#include <type_traits>
+
+#include "mla_common.h"
+
+// The tile copies set M0 inside inline asm.  No compiler-generated code in this
+// translation unit reads M0 (checked in the generated assembly), so declaring
+// it clobbered is only documentation; silence the reserved-register warning.
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace {
+
+constexpr int kH = 128, kC = 512, kW = 576;
+constexpr int kTile = 32;                     // rows per tile
+constexpr int kGran = kW / 8;                 // 72 granules of 16 B per row
+constexpr int kTileGran = kTile * kGran;      // 2304
+constexpr int kThreads = 256;                 // 4 waves x 32 heads
+constexpr int kLoads = kTileGran / kThreads;  // 9 granules per thread per tile
+constexpr int kBufs = 3;
+constexpr int kTileBytes = kTileGran * 16;    // 36864
+constexpr int kMaxSplitTiles = 4096;          // 131072 rows per split
+constexpr float kRestartLog2 = 32.0f;         // restart when the max grows by > 2^32
+constexpr float kLn2 = 0.69314718055994530942f;
+
+static_assert(kLoads * kThreads == kTileGran, "tile must split evenly over the threads");
+
+// LDS granule slot of (row r, granule g) inside a tile.
+__device__ __forceinline__ int swz(int r, int g) {
+  const int j = (r >> 1) & 7;
+  const int s = ((j & 1) << 2) | (j >> 1);
+  return r * kGran + (g ^ s);
+}
+
+__global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  MLA_LDS char* tiles = (MLA_LDS char*)smem;
+  MLA_LDS int* tile_base = (MLA_LDS int*)(smem + kBufs * kTileBytes);
+  MLA_LDS int* votes = tile_base + kMaxSplitTiles;  // [2][4] restart votes, by tile parity
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hf = lane >> 5;          // which half of the wave
+  const int l32 = lane & 31;
+  const int head = wave * 32 + l32;  // this lane's head in the O^T / S^T layouts
+
+  int len = a.seq_lens[b];
+  len = len < a.max_len ? len : a.max_len;
+  const int row_begin = split * a.split_rows;
+  int row_end = row_begin + a.split_rows;
+  row_end = row_end < len ? row_end : len;
+
+  float* out_o;
+  float* out_lse;
+  if (a.num_splits == 1) {
+    out_o = a.v_combine + ((size_t)b * kH + head) * kC;
+    out_lse = a.lse ? a.lse + (size_t)b * kH + head : nullptr;
+  } else {
+    const size_t bs = (size_t)b * a.num_splits + split;
+    out_o = a.part_o + (bs * kH + head) * kC;
+    out_lse = a.part_lse + bs * kH + head;
+  }
+
+  if (row_begin >= row_end) {  // nothing to attend in this partition
+    if (a.num_splits == 1) {
+      for (int c = hf * 4; c < kC; c += 8)
+        *reinterpret_cast<f32x4_t*>(out_o + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (out_lse && hf == 0) *out_lse = -INFINITY;
+    return;
+  }
+  const int ntiles = (row_end - row_begin + kTile - 1) / kTile;
+
+  // Physical first row of every tile of this split; -1 marks a bad table entry.
+  const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+  for (int i = tid; i < ntiles; i += kThreads) {
+    const int t0 = row_begin + i * kTile;
+    const int blk = trow[t0 / a.block];
+    tile_base[i] = (blk >= 0 && blk < a.num_blocks) ? blk * a.block + (t0 % a.block) : -1;
+  }
+
+  // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
+  // 16*kb + 8*hf .. +7 of the 576.
+  bf16x8_t qf[kW / 16];
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q_abs) + ((size_t)b * kH + head) * kW + 8 * hf;
+#pragma unroll
+    for (int kb = 0; kb < kW / 16; ++kb)
+      qf[kb] = *reinterpret_cast<const bf16x8_t*>(q + 16 * kb);
+  }
+  // Consume the Q loads here, so that the only vector-memory operations in
+  // flight inside the tile loop are the tile copies counted by hand below.
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
+               "v"(qf[6]), "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]),
+               "v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]), "v"(qf[16]), "v"(qf[17]));
+  asm volatile("" ::"v"(qf[18]), "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]),
+               "v"(qf[23]), "v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]),
+               "v"(qf[29]), "v"(qf[30]), "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]),
+               "v"(qf[35]));
+  __syncthreads();
+
+  const char* pool = static_cast<const char*>(a.pool);
+  // Row len-1, which stands in for the rows past the end of the last tile.
+  const int last_tile = ntiles - 1;
+  const int last_base = tile_base[last_tile];
+  const int phys_last = last_base < 0 ? -1 : last_base + ((len - 1) - (row_begin + last_tile * kTile));
+
+  // Issue the 9 direct-to-LDS loads of tile i.  Granule slot p of the LDS tile
+  // holds granule (p % 72) ^ swizzle(row) of row p / 72.
+  auto issue_tile = [&](int i) {
+    MLA_LDS char* dst = tiles + (i % kBufs) * kTileBytes;
+    const int base = tile_base[i];
+    const int t0 = row_begin + i * kTile;
+    int ln = threadIdx.x & 63;
+    asm volatile("" : "+v"(ln));  // recompute per tile: keeps registers free
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int slot0 = (k * 4 + wave) * 64;  // first granule slot of this wave-instruction
+      const int p = slot0 + ln;
+      const int r = p / kGran;
+      const int x = p - r * kGran;
+      const int j = (r >> 1) & 7;
+      const int g = x ^ (((j & 1) << 2) | (j >> 1));
+      int phys = (t0 + r < row_end) ? base + r : phys_last;
+      phys = phys < 0 ? 0 : phys;  // a bad table entry reads row 0; the output becomes NaN
+      const char* src = pool + (size_t)phys * (kW * 2) + g * 16;
+      // 16 bytes per lane straight into LDS at M0 + 16 * lane.  Issued from
+      // asm so the compiler does not treat every later LDS read as aliasing
+      // the in-flight copy (the explicit vmcnt waits order them instead).
+      const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + slot0 * 16));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(lds)
+                   : "memory", "m0");
+    }
+  };
+
+  f32x16_t o[kC / 32];
+#pragma unroll
+  for (int cb = 0; cb < kC / 32; ++cb) o[cb] = f32x16_t{};
+  // p = 2^(s*scale*log2e - m_ref) with a per-head reference m_ref taken from
+  // the first tile.  If a later tile's maximum exceeds it by more than
+  // kRestartLog2 (p would leave the safe range), the workgroup restarts the
+  // split with the largest maximum seen as the new reference.  The restart
+  // never touches O in registers: the next accumulation simply takes C = 0.
+  float m_ref = -INFINITY;
+  float m_seen = -INFINITY;
+  float l_run = 0.f;
+  bool bad = false;
+  bool pending = false;
+  bool fresh = true;     // the next tile is the first since the (re)start
+  int zero_c = 0;        // 1: the next accumulation starts from C = 0
+
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  // Iteration ntiles only collects the last tile's restart vote.
+  for (int i = 0; i <= ntiles; ++i) {
+    if (i + 1 < ntiles) {
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if (lane == 0) votes[(i & 1) * 4 + wave] = __ballot(pending) != 0;
+    __syncthreads();
+    bool restart;
+    {
+      const MLA_LDS int* v = votes + (i & 1) * 4;
+      restart = (v[0] | v[1] | v[2] | v[3]) != 0;
+    }
+    if (restart) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      m_ref = m_seen;
+      l_run = 0.f;
+      pending = false;
+      fresh = true;
+      zero_c = 1;
+      issue_tile(0);
+      if (ntiles > 1) issue_tile(1);
+      i = -1;
+      continue;
+    }
+    if (i == ntiles) break;
+    if (i + 2 < ntiles) issue_tile(i + 2);
+    bad |= tile_base[i] < 0;
+
+    const MLA_LDS char* tile = tiles + (i % kBufs) * kTileBytes;
+    int qk_off[4], pv_off[2][2];
+    {
+      int ln = threadIdx.x & 63;
+      asm volatile("" : "+v"(ln));  // recompute per tile: keeps registers free
+      const int ll = ln & 31, hh = ln >> 5, k16 = ln & 15, g16 = (ln >> 4) & 1;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) qk_off[m] = swz(ll, 2 * m + hh) * 16;
+#pragma unroll
+      for (int c1 = 0; c1 < 2; ++c1)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          pv_off[c1][rr] = swz(8 * rr + 4 * hh + (k16 >> 2), 4 * c1 + 2 * g16 + ((k16 & 3) >> 1)) * 16 +
+                           8 * (k16 & 1);
+    }
+
+    // ---- scores S^T (rows x heads): K fragments read three k-blocks ahead ----
+    f32x16_t s = f32x16_t{};
+    {
+      bf16x8_t kf[3];
+      auto kaddr = [&](int kb) {
+        return (const MLA_LDS bf16x8_t*)(tile + qk_off[kb & 3] + (kb >> 2) * 128);
+      };
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) kf[kb] = *kaddr(kb);
+#pragma unroll
+      for (int kb = 0; kb < kW / 16; ++kb) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 3], qf[kb], s, 0, 0, 0);
+        if (kb + 3 < kW / 16) kf[kb % 3] = *kaddr(kb + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- softmax numerators: lane = head, 16 rows per lane (the rest in lane ^ 32) ----
+    const int t0 = row_begin + i * kTile;
+    const bool tail = t0 + kTile > row_end;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float v = s[j] * a.scale_log2;
+      if (tail) {
+        const int t = t0 + (j >> 2) * 8 + hf * 4 + (j & 3);
+        v = t < row_end ? v : -INFINITY;
+      }
+      s[j] = v;
+      mt = fmaxf(mt, v);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    m_seen = fmaxf(m_seen, mt);
+    if (fresh) m_ref = fmaxf(m_ref, mt);
+    fresh = false;
+    pending = mt > m_ref + kRestartLog2;
+    bf16x8_t pb[2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = __builtin_amdgcn_exp2f(s[j] - m_ref);
+      lsum += p;
+      pb[j >> 3][j & 7] = (__bf16)p;
+    }
+    l_run += lsum;
+
+    // ---- O^T += V^T P^T: per 32-column block, 4 transpose reads one block ahead ----
+    {
+      s16x4_t vf[2][4];
+      auto read_v = [&](int cb, s16x4_t* dst) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const MLA_LDS char* base = tile + kb * (16 * kGran * 16) + (cb >> 1) * 128;
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr)
+            dst[2 * kb + rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (MLA_LDS s16x4_t*)(base + pv_off[cb & 1][rr]));
+        }
+      };
+      read_v(0, vf[0]);
+      // the bf16 P operands were just written by VALU: pad before an MFMA reads them
+      asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
+#pragma unroll
+      for (int cb = 0; cb < kC / 32; ++cb) {
+        if (cb + 1 < kC / 32) read_v(cb + 1, vf[(cb + 1) & 1]);
+        const s16x8_t v0 = __builtin_shufflevector(vf[cb & 1][0], vf[cb & 1][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const s16x8_t v1 = __builtin_shufflevector(vf[cb & 1][2], vf[cb & 1][3], 0, 1, 2, 3, 4, 5, 6, 7);
+        // The accumulator is pinned to AGPRs (the score MFMAs use VGPRs).  The
+        // first k-block takes C = 0 right after a restart.
+        asm volatile(
+            "s_cmp_eq_u32 %4, 0\n\t"
+            "s_cbranch_scc1 1f\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %1, %3, 0\n\t"
+            "s_branch 2f\n"
+            "1:\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %1, %3, %0\n"
+            "2:\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %5, %0"
+            : "+a"(o[cb])
+            : "v"(v0), "v"(v1), "v"(pb[0]), "s"(zero_c), "v"(pb[1])
+            : "scc");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    zero_c = 0;
+  }
+
+  // The last accumulate MFMAs may still be in flight: pad before reading O.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]));
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]),
+                 "+a"(o[14]), "+a"(o[15]));
+
+  // ---- finish: normalise and store this lane's head ----
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv_l = bad ? NAN : 1.0f / l;
+#pragma unroll
+  for (int cb = 0; cb < kC / 32; ++cb) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c = cb * 32 + q4 * 8 + hf * 4;
+      f32x4_t v{o[cb][4 * q4 + 0] * inv_l, o[cb][4 * q4 + 1] * inv_l,
+                o[cb][4 * q4 + 2] * inv_l, o[cb][4 * q4 + 3] * inv_l};
+      *reinterpret_cast<f32x4_t*>(out_o + c) = v;
+    }
+  }
+  if (out_lse && hf == 0) *out_lse = bad ? NAN : (m_ref + log2f(l)) * kLn2;
+}
+
+// Merge the normalised partials of every split: lse = log sum_s exp(lse_s),
+// v = sum_s exp(lse_s - lse) O_s.  One workgroup per (sequence, 2 heads), 128
+// threads per head, 4 consecutive latent columns per thread and step; the max
+// and the weight sum over splits are wavefront reductions.  C % 4 == 0.
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+  const int b = blockIdx.y;
+  const int h = blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int c0 = (threadIdx.x & 127) * 4;
+  const int lane = threadIdx.x & 63;
+  const int S = a.num_splits;
+  if (h >= a.H) return;  // odd head counts: the second half-block is idle (whole waves)
+  const float* lse_s = a.part_lse + (size_t)b * S * a.H + h;  // stride H over s
+
+  float m = -INFINITY;
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, lse_s[(size_t)s * a.H]);
+  m = wave_max(m);
+  float* dst = a.v_combine + ((size_t)b * a.H + h) * a.C;
+  if (m == -INFINITY) {  // empty sequence
+    for (int c = c0; c < a.C; c += 512) *reinterpret_cast<f32x4_t*>(dst + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (a.lse && (threadIdx.x & 127) == 0) a.lse[(size_t)b * a.H + h] = -INFINITY;
+    return;
+  }
+  float wsum = 0.f;
+  for (int s = lane; s < S; s += 64) wsum += expf(lse_s[(size_t)s * a.H] - m);
+  wsum = wave_sum(wsum);
+  const float inv = 1.0f / wsum;
+  for (int c = c0; c < a.C; c += 512) {
+    f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float ls = lse_s[(size_t)s * a.H];
+      if (ls == -INFINITY) continue;
+      const float w = expf(ls - m);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(
+          a.part_o + (((size_t)b * S + s) * a.H + h) * a.C + c);
+      acc += w * v;
+    }
+    *reinterpret_cast<f32x4_t*>(dst + c) = acc * inv;
+  }
+  if (a.lse && (threadIdx.x & 127) == 0) a.lse[(size_t)b * a.H + h] = m + logf(wsum);
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
+  const size_t smem = kBufs * kTileBytes + (kMaxSplitTiles + 8) * sizeof(int);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(attn_mfma_kernel, dim3(a.num_splits, a.B), dim3(kThreads), smem, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+int attn_mfma_max_split_rows() { return kMaxSplitTiles * kTile; }

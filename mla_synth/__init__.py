@@ -214,6 +214,8 @@ def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optiona
          projections 4-bit affine group 64, bf16 norms; YaRN softmax scale.
     """
     seed = 1000 + cfg if seed is None else seed
+    if lens is not None and batch is None:
+        batch = len(lens)
     rng = np.random.default_rng(seed)
     yarn = Yarn()
     if cfg == 1:

@@ -1,0 +1,101 @@
+"""Stage a synthetic case on the GPU as torch tensors and library weight descriptors.
+
+Pure data movement (numpy -> torch device memory); no arithmetic of the method.
+"""
+from __future__ import annotations
+
+import types
+
+import numpy as np
+import torch
+
+import mla_latent_kv_11_amd as mla
+from . import Case, Q4Weight, F32, BF16
+
+
+def t(arr, device="cuda") -> torch.Tensor:
+    """numpy -> device tensor with the same bytes (uint16 -> int16, uint32 -> int32)."""
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(device)
+
+
+def weight(w, rows: int, cols: int, device="cuda") -> mla.Weight:
+    if isinstance(w, Q4Weight):
+        return mla.Weight(mla.MLA_Q4G64, rows, cols, t(w.packed, device), t(w.scales, device),
+                          t(w.biases, device))
+    a = np.asarray(w)
+    dt = mla.MLA_BF16 if a.dtype == np.uint16 else mla.MLA_F32
+    return mla.Weight(dt, rows, cols, t(a.reshape(rows, cols), device))
+
+
+def dims_of(case: Case) -> mla.Dims:
+    d = case.dims
+    return mla.Dims(d.num_heads, d.qk_nope, d.qk_rope, d.v_head, d.kv_lora, d.hidden, d.q_lora,
+                    d.block_size, d.cache_dtype, d.rms_eps)
+
+
+def stage(case: Case, device="cuda") -> types.SimpleNamespace:
+    """Everything a decode step of ``case`` needs, resident in device memory."""
+    d = case.dims
+    H, N, R, V, C = d.num_heads, d.qk_nope, d.qk_rope, d.v_head, d.kv_lora
+    ns = types.SimpleNamespace()
+    ns.dims = dims_of(case)
+    ns.pool = t(case.pool, device)
+    ns.table = t(case.table, device)
+    ns.lens = t(case.lens.astype(np.int32), device)
+    ns.positions = t(case.positions, device)
+    ns.max_len = int(case.lens.max()) if len(case.lens) else 0
+    ns.x = t(case.x, device) if case.x is not None else None
+    ns.kv_a = weight(case.kv_a, d.width, d.hidden, device) if case.kv_a is not None else None
+    ns.kv_a_norm = weight(case.kv_a_norm, 1, C, device) if case.kv_a_norm is not None else None
+    ns.q = t(case.q, device) if case.q is not None else None
+    ns.q_a = weight(case.q_a, d.q_lora, d.hidden, device) if case.q_a is not None else None
+    ns.q_a_norm = weight(case.q_a_norm, 1, d.q_lora, device) if case.q_a_norm is not None else None
+    ns.q_b = weight(case.q_b, H * (N + R), d.q_lora, device) if case.q_b is not None else None
+    ns.kv_b = weight(case.kv_b, H * (N + V), C, device) if case.kv_b is not None else None
+    ns.o_proj = (weight(case.o_proj, d.hidden, H * V, device)
+                 if case.o_proj is not None else None)
+    ns.q_abs_given = t(case.q_abs, device) if case.q_abs is not None else None
+    cdt = torch.float32 if d.cache_dtype == F32 else torch.int16
+    B = case.batch
+    ns.q_abs = torch.empty((B, H, d.width), dtype=cdt, device=device)
+    ns.v_combine = torch.empty((B, H, C), dtype=torch.float32, device=device)
+    ns.lse = torch.empty((B, H), dtype=torch.float32, device=device)
+    out_cols = d.hidden if case.o_proj is not None else H * V
+    ns.out = torch.empty((B, out_cols), dtype=torch.float32, device=device)
+    ns.status = torch.zeros(1, dtype=torch.int32, device=device)
+    y = case.yarn
+    inv, rm, sc = mla.yarn_tables(R, N + R, y.theta, y.factor, y.original_max_pos, y.beta_fast,
+                                  y.beta_slow, y.mscale, y.mscale_all_dim)
+    ns.inv_freq = torch.tensor(inv, dtype=torch.float32, device=device)
+    ns.rope_mscale = rm
+    ns.softmax_scale = float(case.softmax_scale) if case.softmax_scale is not None else sc
+    return ns
+
+
+def workspace(ns, split_rows: int = 0, device="cuda") -> torch.Tensor:
+    n = mla.workspace_bytes(ns.dims, int(ns.lens.shape[0]), ns.max_len, split_rows)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def run_step(case: Case, ns, split_rows: int = 0, ws=None, stream=None) -> None:
+    """append -> absorb -> attention -> out_proj on the staged case (library calls only)."""
+    ws = workspace(ns, split_rows) if ws is None else ws
+    if case.appended:
+        mla.cache_append(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq, ns.rope_mscale,
+                         ns.positions, ns.pool, ns.table, ns.status, ws, stream)
+    if ns.q_abs_given is not None:
+        q_abs = ns.q_abs_given
+    else:
+        q_in = ns.q if ns.q is not None else ns.x
+        mla.absorb_q(ns.dims, q_in, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
+                     ns.q_a, ns.q_a_norm, ns.q_b, ws, stream)
+        q_abs = ns.q_abs
+    mla.decode_attn(ns.dims, q_abs, ns.pool, ns.table, ns.lens, ns.max_len, ns.softmax_scale,
+                    ns.v_combine, ns.lse, split_rows, ws, stream)
+    if ns.kv_b is not None:
+        mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws, stream)

@@ -1,0 +1,155 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, rejects bad arguments before touching the device, and its host YaRN
+helper matches the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_11_amd as mla
+from oracle import mla_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        pytest.fail("libmla.so is not built; run __graft_entry__.build() first")
+    return mla.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mla_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_expected_calls():
+    assert declared_functions() == sorted(mla.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert mla.status_str(code) and "unknown" not in mla.status_str(code)
+    assert "unknown" in mla.status_str(-99)
+
+
+DS = mla.Dims(128, 128, 64, 128, 512, hidden=0, q_lora=0, block_size=64, cache_dtype=mla.MLA_BF16)
+
+
+def _w(dtype, rows, cols, ptr=0x1000, sc=None, bi=None):
+    return mla.CWeight(dtype, rows, cols, ptr, sc, bi)
+
+
+def call_attn(lib, dims=DS, B=2, q=0x1000, pool=0x2000, table=0x3000, lens=0x4000, max_len=100,
+              scale=0.1, split=0, vc=0x5000, lse=None, ws=None, ws_bytes=0, nblocks=4, maxb=2):
+    cache = mla.CCache(pool, table, nblocks, maxb)
+    return lib.mla_decode_attn(ctypes.byref(dims.c()), B, q, ctypes.byref(cache), lens, max_len,
+                               scale, split, vc, lse, ws, ws_bytes, None)
+
+
+def test_attn_validation_before_launch(lib):
+    # every one of these returns before any HIP call (no device here)
+    assert call_attn(lib, q=None) == mla.MLA_ERR_NULL
+    assert call_attn(lib, vc=None) == mla.MLA_ERR_NULL
+    assert call_attn(lib, max_len=-1) == mla.MLA_ERR_DIMS
+    assert call_attn(lib, max_len=129) == mla.MLA_ERR_CAPACITY          # 2 blocks x 64 rows
+    assert call_attn(lib, split=100) == mla.MLA_ERR_DIMS                 # not a multiple of 64
+    assert call_attn(lib, scale=float("inf")) == mla.MLA_ERR_DIMS
+    bad = mla.Dims(**{**DS.__dict__, "num_heads": 64})
+    assert call_attn(lib, dims=bad) == mla.MLA_ERR_UNSUPPORTED
+    odd = mla.Dims(**{**DS.__dict__, "qk_rope": 63})
+    assert call_attn(lib, dims=odd) == mla.MLA_ERR_DIMS
+    dt = mla.Dims(**{**DS.__dict__, "cache_dtype": 7})
+    assert call_attn(lib, dims=dt) == mla.MLA_ERR_DTYPE
+    # two splits of 64 rows need a workspace
+    assert call_attn(lib, split=64, max_len=128) == mla.MLA_ERR_WORKSPACE
+    assert call_attn(lib, split=64, max_len=128, ws=0x9000, ws_bytes=16) == mla.MLA_ERR_WORKSPACE
+    # batch 0 is a no-op success
+    assert call_attn(lib, B=0) == mla.MLA_OK
+
+
+def test_plan_and_workspace(lib):
+    r, s = mla.attn_plan(DS, 4, 131072, 2048)
+    assert (r, s) == (2048, 64)
+    r, s = mla.attn_plan(DS, 1, 100, 0)
+    assert s == 1 and r >= 100
+    need = mla.workspace_bytes(DS, 4, 131072, 2048)
+    assert need >= 4 * 64 * 128 * 512 * 4 + 4 * 64 * 128 * 4
+    assert mla.workspace_bytes(DS, 1, 100, 64 * 3) >= 0
+    with pytest.raises(mla.MLAError):
+        mla.attn_plan(DS, 1, 100, 65)
+
+
+def test_weight_validation(lib):
+    d = mla.Dims(16, 32, 16, 32, 64, hidden=256, q_lora=0, cache_dtype=mla.MLA_F32)
+    rope = mla.CRope(0x100, 1.0)
+    cache = mla.CCache(0x200, 0x300, 2, 2)
+    kv_a = _w(mla.MLA_F32, 80, 256)
+    norm = _w(mla.MLA_F32, 1, 64)
+
+    def app(kv_a=kv_a, norm=norm, ws=0x900, wsb=1 << 20, x=0x400):
+        return lib.mla_cache_append(ctypes.byref(d.c()), 1, x, ctypes.byref(kv_a) if kv_a else None,
+                                    ctypes.byref(norm), ctypes.byref(rope), 0x500,
+                                    ctypes.byref(cache), None, ws, wsb, None)
+    assert app(x=None) == mla.MLA_ERR_NULL
+    assert app(kv_a=None) == mla.MLA_ERR_NULL                     # hidden > 0 needs kv_a
+    assert app(kv_a=_w(mla.MLA_F32, 79, 256)) == mla.MLA_ERR_DIMS  # one row short
+    assert app(kv_a=_w(5, 80, 256)) == mla.MLA_ERR_DTYPE
+    assert app(norm=_w(mla.MLA_Q4G64, 1, 64)) == mla.MLA_ERR_DTYPE
+    assert app(ws=None) == mla.MLA_ERR_WORKSPACE
+    assert app(wsb=10) == mla.MLA_ERR_WORKSPACE
+    # 4-bit weights need group-aligned columns and scale/bias pointers
+    q4 = _w(mla.MLA_Q4G64, 80, 256)
+    assert app(kv_a=q4) == mla.MLA_ERR_NULL
+    d2 = mla.Dims(16, 32, 16, 32, 64, hidden=96, q_lora=0, cache_dtype=mla.MLA_F32)
+    q4b = _w(mla.MLA_Q4G64, 80, 96, sc=0x10, bi=0x20)
+    assert lib.mla_cache_append(ctypes.byref(d2.c()), 1, 0x400, ctypes.byref(q4b),
+                                ctypes.byref(norm), ctypes.byref(rope), 0x500, ctypes.byref(cache),
+                                None, 0x900, 1 << 20, None) == mla.MLA_ERR_DIMS
+
+
+def test_absorb_and_out_proj_validation(lib):
+    d = mla.Dims(16, 32, 16, 32, 64, hidden=256, q_lora=0, cache_dtype=mla.MLA_F32)
+    rope = mla.CRope(0x100, 1.0)
+    kvb = _w(mla.MLA_F32, 16 * 64, 64)
+    assert lib.mla_absorb_q(ctypes.byref(d.c()), 1, 0x10, None, None, None, ctypes.byref(kvb),
+                            ctypes.byref(rope), 0x20, None, None, 0, None) == mla.MLA_ERR_NULL
+    short = _w(mla.MLA_F32, 16 * 64 - 1, 64)
+    assert lib.mla_absorb_q(ctypes.byref(d.c()), 1, 0x10, None, None, None, ctypes.byref(short),
+                            ctypes.byref(rope), 0x20, 0x30, None, 0, None) == mla.MLA_ERR_DIMS
+    # q_a without q_lora in the dims
+    qa = _w(mla.MLA_F32, 8, 256)
+    assert lib.mla_absorb_q(ctypes.byref(d.c()), 1, 0x10, ctypes.byref(qa), None, None,
+                            ctypes.byref(kvb), ctypes.byref(rope), 0x20, 0x30, None, 0,
+                            None) == mla.MLA_ERR_DIMS
+    wo = _w(mla.MLA_F32, 256, 16 * 32)
+    assert lib.mla_out_proj(ctypes.byref(d.c()), 1, 0x10, ctypes.byref(kvb), ctypes.byref(wo),
+                            0x20, None, 0, None) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_out_proj(ctypes.byref(d.c()), 1, None, ctypes.byref(kvb), None, 0x20, None, 0,
+                            None) == mla.MLA_ERR_NULL
+
+
+@pytest.mark.parametrize("R,head", [(64, 192), (16, 48)])
+def test_library_yarn_table_matches_oracle(lib, R, head):
+    inv, rm, sc = mla.yarn_tables(R, head)
+    ref = O.yarn_inv_freq(R, 1e4, 40.0, 4096.0, 32.0, 1.0)
+    assert np.array_equal(np.array(inv, dtype=np.float32), ref.astype(np.float32))
+    orm, osc = O.yarn_scalars(40.0, 1.0, 1.0, head)
+    assert rm == np.float32(orm) and sc == np.float32(osc)
+
+
+def test_yarn_validation(lib):
+    y = mla.CYarn(1e4, 40, 4096, 32, 1, 1, 1)
+    assert lib.mla_yarn_tables(ctypes.byref(y), 63, 192, None, None, None) == mla.MLA_ERR_DIMS
+    assert lib.mla_yarn_tables(None, 64, 192, None, None, None) == mla.MLA_ERR_NULL
+    y0 = mla.CYarn(1.0, 40, 4096, 32, 1, 1, 1)
+    assert lib.mla_yarn_tables(ctypes.byref(y0), 64, 192, None, None, None) == mla.MLA_ERR_DIMS
