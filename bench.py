@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of single-token MLA decode (one layer) on one MI355X.
+
+A step is one pass of the whole decode path over one batch: kv_a projection +
+latent RMSNorm + YaRN RoPE + paged append, the q chain + absorb, decode
+attention over the paged latent cache, the W_UV expansion and o_proj.  The
+workload is the full per-layer configuration: batch 32, 16384 cached rows per
+sequence (append at 16383), DeepSeek-V3 shapes (128 heads, latent 512, rope
+64), hidden 7168, q_lora 1536, 4-bit affine (group 64) projections, bf16
+cache.  Inputs are synthetic (seeded) and resident in HBM before timing.
+
+Prints one JSON line.  ``roofline`` describes the attention call (its split
+kernel plus the split-K combine kernel), timed with HIP events on the stream
+it is launched on; ``cpu_baseline`` is the fp64 oracle timed on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode attn: HBM GB/s + MFMA util + tokens/s, 128 heads, L=4096..131072"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+ROW_BYTES = 576 * 2            # one bf16 cache row [c_kv ; k_pe]
+ROW_FLOPS = 2 * 128 * 576 + 2 * 128 * 512   # scores + latent combine per row, 128 heads
+COUNTERS = os.path.join(ROOT, "profiles", "attn_mfma_cfg5_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_11_amd", "csrc", "attn_mfma.hip")
+
+
+def attn_alg(B, rows, H=128, W=576, C=512):
+    """Algorithmic bytes and flops of one attention call: every cache row once,
+    q_abs (bf16) in, v_combine (fp32) out."""
+    byts = rows * ROW_BYTES + B * H * W * 2 + B * H * C * 4
+    return byts, rows * ROW_FLOPS
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """Counter-measured HBM bytes per attention call, if taken on this kernel source.
+
+    The figures live in a JSON block of the counter summary under profiles/."""
+    try:
+        with open(COUNTERS) as f:
+            text = f.read()
+        c = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, ValueError, IndexError):
+        return None
+    if c.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return c.get("hbm_bytes_per_call")
+
+
+def time_attn_only(cfg, torch, D, S, mla, iters=20, warm=5):
+    """Attention call alone on a full-size configuration (q_abs given or absorbed once)."""
+    case = S.make_case(cfg)
+    ns = D.stage(case)
+    ws = D.workspace(ns)
+    if ns.q_abs_given is not None:
+        q_abs = ns.q_abs_given
+    else:
+        mla.absorb_q(ns.dims, ns.q, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
+                     ws=ws)
+        q_abs = ns.q_abs
+    stream = torch.cuda.current_stream()
+
+    def call():
+        mla.decode_attn(ns.dims, q_abs, ns.pool, ns.table, ns.lens, ns.max_len,
+                        ns.softmax_scale, ns.v_combine, ns.lse, 0, ws)
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    rows = int(case.lens.sum())
+    byts, flops = attn_alg(case.batch, rows)
+    t = ms * 1e-3
+    return {
+        "batch": case.batch, "rows": rows, "ms": round(ms, 4),
+        "gbps": round(byts / t / 1e9, 1), "tflops": round(flops / t / 1e12, 1),
+        "f_hbm": round(byts / t / 1e9 / HBM_PEAK_GBS, 3),
+        "f_mfma": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
+        "f_roof": round(max(byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)) / t, 3),
+        "tokens_per_s": round(case.batch / t, 1),
+    }
+
+
+def cpu_baseline(case, seqs, min_seconds=10.0, max_reps=8):
+    """The oracle's whole step on ``seqs`` sequences of the same workload,
+    repeated until about ``min_seconds`` of host work."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    sub = S_sub(case, seqs)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    reps, total = 0, 0.0
+    while reps < max_reps and (reps == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        res = O.decode_step(sub)
+        total += time.perf_counter() - t0
+        reps += 1
+    assert np.isfinite(res["out"]).all()
+    return {"value": round(seqs * reps / total, 4), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{seqs} of 32 sequences (16384 rows each), whole layer step in fp64 numpy, "
+                      f"{reps} repetitions, {total:.1f} s"}
+
+
+def copy_calibration(torch, gib=1):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters to bytes: each copy reads and writes exactly ``gib`` GiB."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+
+
+def S_sub(case, seqs):
+    import copy
+    sub = copy.copy(case)
+    sub.batch = seqs
+    sub.lens = case.lens[:seqs]
+    sub.table = case.table[:seqs]
+    nb = int(((case.lens[:seqs].astype(int) + 63) // 64).sum())
+    used = sorted(set(case.table[:seqs].reshape(-1).tolist()) - {-1})
+    assert len(used) == nb
+    sub.x = case.x[:seqs]
+    return sub
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-configuration attention lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    import mla_latent_kv_11_amd as mla
+    import mla_synth as S
+    from mla_synth import device as D
+    globals()["S"] = S
+
+    mla.load_library()
+    case = S.make_case(5)
+    ns = D.stage(case)
+    ws = D.workspace(ns)
+    stream = torch.cuda.current_stream()
+    B = case.batch
+    rows = int(case.lens.sum())
+
+    def step(ev=None):
+        mla.cache_append(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq, ns.rope_mscale,
+                         ns.positions, ns.pool, ns.table, ns.status, ws)
+        mla.absorb_q(ns.dims, ns.x, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
+                     ns.q_a, ns.q_a_norm, ns.q_b, ws)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.decode_attn(ns.dims, ns.q_abs, ns.pool, ns.table, ns.lens, ns.max_len,
+                        ns.softmax_scale, ns.v_combine, ns.lse, 0, ws)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    assert int(ns.status.cpu()[0]) == 0
+
+    byts, flops = attn_alg(B, rows)
+    t_attn = attn_ms * 1e-3
+    achieved = byts / t_attn / 1e9
+    r_split, n_split = mla.attn_plan(ns.dims, B, ns.max_len, 0)
+    line = {
+        "metric": METRIC,
+        "value": round(B / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "MLA decode layer, batch 32, L=16384 (append at 16383), 128 heads, "
+                        "kv_lora 512 + rope 64, hidden 7168, q_lora 1536, 4-bit g64 projections, "
+                        "bf16 paged cache (64-row blocks)",
+            "global_batch": B, "seq_len": int(ns.max_len), "parallelism": "none (1 GPU)",
+            "split_rows": r_split, "splits_per_seq": n_split,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 3),
+            "traffic": stored_traffic(),
+            "kernel": "mla_decode_attn (attn_mfma_kernel + attn_combine_kernel)",
+            "ms_per_launch": round(attn_ms, 4),
+            "alg_bytes": byts,
+            "mfma_tflops": round(flops / t_attn / 1e12, 1),
+            "mfma_frac": round(flops / t_attn / 1e12 / BF16_PEAK_TFLOPS, 3),
+        },
+    }
+    if not args.no_extra:
+        extra = {}
+        for cfg in (2, 3, 4):
+            extra[f"cfg{cfg}"] = time_attn_only(cfg, torch, D, S, mla)
+        line["attn_only"] = extra
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seqs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
