@@ -51,6 +51,9 @@ constexpr int kLoads = kTileGran / kThreads;  // 9 granules per thread per tile
 constexpr int kBufs = 3;
 constexpr int kTileBytes = kTileGran * 16;    // 36864
 constexpr int kMaxSplitTiles = 4096;          // 131072 rows per split
+constexpr int kPRow = 80;                     // bytes per head row of P in LDS (64 + 16 pad)
+constexpr size_t kSmemBytes =
+    kBufs * kTileBytes + (kMaxSplitTiles + 8) * 4 + kH * 4 + kH * kPRow + kLoads * kThreads * 4;
 constexpr float kRestartLog2 = 32.0f;         // restart when the max grows by > 2^32
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -67,16 +70,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   MLA_LDS char* tiles = (MLA_LDS char*)smem;
   MLA_LDS int* tile_base = (MLA_LDS int*)(smem + kBufs * kTileBytes);
-  MLA_LDS int* votes = tile_base + kMaxSplitTiles;  // [2][4] restart votes, by tile parity
+  MLA_LDS int* votes = tile_base + kMaxSplitTiles;         // [2][4] restart votes, by tile parity
+  MLA_LDS float* l_heads = (MLA_LDS float*)(votes + 8);    // [128] softmax denominators
+  MLA_LDS char* p_lds = (MLA_LDS char*)(l_heads + kH);     // [128 heads][kPRow] bf16 P, slot order
+  MLA_LDS uint32_t* goff_lds = (MLA_LDS uint32_t*)(p_lds + kH * kPRow);  // [kLoads][256]
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int hf = lane >> 5;          // which half of the wave
   const int l32 = lane & 31;
-  const int head = wave * 32 + l32;  // this lane's head in the O^T / S^T layouts
+  const int head = wave * 32 + l32;  // this lane's head in the S^T layout
 
   int len = a.seq_lens[b];
   len = len < a.max_len ? len : a.max_len;
@@ -84,19 +90,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   int row_end = row_begin + a.split_rows;
   row_end = row_end < len ? row_end : len;
 
-  float* out_o;
+  float* out_base;  // [128 heads][512] of this (sequence, split)
   float* out_lse;
   if (a.num_splits == 1) {
-    out_o = a.v_combine + ((size_t)b * kH + head) * kC;
+    out_base = a.v_combine + (size_t)b * kH * kC;
     out_lse = a.lse ? a.lse + (size_t)b * kH + head : nullptr;
   } else {
     const size_t bs = (size_t)b * a.num_splits + split;
-    out_o = a.part_o + (bs * kH + head) * kC;
+    out_base = a.part_o + bs * kH * kC;
     out_lse = a.part_lse + bs * kH + head;
   }
 
   if (row_begin >= row_end) {  // nothing to attend in this partition
     if (a.num_splits == 1) {
+      float* out_o = out_base + (size_t)head * kC;
       for (int c = hf * 4; c < kC; c += 8)
         *reinterpret_cast<f32x4_t*>(out_o + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -111,6 +118,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     const int t0 = row_begin + i * kTile;
     const int blk = trow[t0 / a.block];
     tile_base[i] = (blk >= 0 && blk < a.num_blocks) ? blk * a.block + (t0 % a.block) : -1;
+  }
+  // Byte offset, inside a tile of 32 consecutive rows, of granule copy k of
+  // this thread: LDS slot p = (k*4 + wave)*64 + lane holds granule
+  // (p % 72) ^ swizzle(row) of row p / 72.
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) {
+    const int p = (k * 4 + wave) * 64 + lane;
+    const int r = p / kGran;
+    const int x = p - r * kGran;
+    const int j = (r >> 1) & 7;
+    goff_lds[k * kThreads + tid] = (uint32_t)(r * (kW * 2) + (x ^ (((j & 1) << 2) | (j >> 1))) * 16);
   }
 
   // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
@@ -134,39 +152,49 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
 
   const char* pool = static_cast<const char*>(a.pool);
-  // Row len-1, which stands in for the rows past the end of the last tile.
-  const int last_tile = ntiles - 1;
-  const int last_base = tile_base[last_tile];
-  const int phys_last = last_base < 0 ? -1 : last_base + ((len - 1) - (row_begin + last_tile * kTile));
+  const uint32_t tiles_lds = (uint32_t)(uintptr_t)tiles;
 
-  // Issue the 9 direct-to-LDS loads of tile i.  Granule slot p of the LDS tile
-  // holds granule (p % 72) ^ swizzle(row) of row p / 72.
-  auto issue_tile = [&](int i) {
-    MLA_LDS char* dst = tiles + (i % kBufs) * kTileBytes;
-    const int base = tile_base[i];
+  // Loop-invariant parts of the LDS read addresses (bytes inside a tile); the
+  // others follow by XOR (the swizzle touches granule bits 1..2 only):
+  //   K rows for k-block kb:   qk0 ^ ((kb & 3) << 5), + (kb >> 2) * 128
+  //   V^T for column block cb: ((pv0 ^ 64*(cb & 1)) ^ 32*rr) + 9216*rr, + (cb >> 1) * 128
+  const uint32_t qk0 = (uint32_t)swz(l32, hf) * 16;
+  uint32_t pv0;
+  {
+    const int k16 = lane & 15, g16 = (lane >> 4) & 1;
+    pv0 = (uint32_t)(swz(4 * hf + (k16 >> 2), 2 * g16 + ((k16 & 3) >> 1)) * 16 + 8 * (k16 & 1));
+  }
+  const uint32_t p_row = (uint32_t)(l32 * kPRow + hf * 16);  // + head block * 32 * kPRow
+
+  // Source of tile i: the address of its first row (a bad table entry reads
+  // row 0 and makes the output NaN) and its last valid row; rows past it
+  // re-read that row and get probability 0.
+  auto tile_src = [&](int i, const char** src, int* rlast) {
+    const int base = __builtin_amdgcn_readfirstlane(tile_base[i]);
+    *src = pool + (size_t)(base < 0 ? 0 : base) * (kW * 2);
     const int t0 = row_begin + i * kTile;
-    int ln = threadIdx.x & 63;
-    asm volatile("" : "+v"(ln));  // recompute per tile: keeps registers free
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int slot0 = (k * 4 + wave) * 64;  // first granule slot of this wave-instruction
-      const int p = slot0 + ln;
-      const int r = p / kGran;
-      const int x = p - r * kGran;
-      const int j = (r >> 1) & 7;
-      const int g = x ^ (((j & 1) << 2) | (j >> 1));
-      int phys = (t0 + r < row_end) ? base + r : phys_last;
-      phys = phys < 0 ? 0 : phys;  // a bad table entry reads row 0; the output becomes NaN
-      const char* src = pool + (size_t)phys * (kW * 2) + g * 16;
-      // 16 bytes per lane straight into LDS at M0 + 16 * lane.  Issued from
-      // asm so the compiler does not treat every later LDS read as aliasing
-      // the in-flight copy (the explicit vmcnt waits order them instead).
-      const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + slot0 * 16));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(src), "s"(lds)
-                   : "memory", "m0");
+    *rlast = (t0 + kTile <= row_end) ? kTile - 1 : row_end - 1 - t0;
+  };
+  // Copy granule k of tile i: 16 bytes per lane straight into LDS at
+  // M0 + 16 * lane.  Issued from asm so that the compiler does not treat every
+  // later LDS read as aliasing the copy; the explicit vmcnt waits order them.
+  auto issue_load = [&](int i, int k, uint32_t off, const char* src, int rlast) {
+    if (rlast < kTile - 1) {
+      const int r = (int)(off / (kW * 2));
+      if (r > rlast) off -= (uint32_t)((r - rlast) * (kW * 2));
     }
+    const uint32_t lds = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes + (k * 4 + wave) * 1024);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(src), "s"(lds)
+                 : "memory");
+  };
+  auto issue_tile = [&](int i) {
+    const char* src;
+    int rlast;
+    tile_src(i, &src, &rlast);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) issue_load(i, k, goff_lds[k * kThreads + tid], src, rlast);
   };
 
   f32x16_t o[kC / 32];
@@ -177,6 +205,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // kRestartLog2 (p would leave the safe range), the workgroup restarts the
   // split with the largest maximum seen as the new reference.  The restart
   // never touches O in registers: the next accumulation simply takes C = 0.
+  const float c = a.scale_log2;
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;
   float l_run = 0.f;
@@ -215,108 +244,161 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       continue;
     }
     if (i == ntiles) break;
-    if (i + 2 < ntiles) issue_tile(i + 2);
     bad |= tile_base[i] < 0;
-
-    const MLA_LDS char* tile = tiles + (i % kBufs) * kTileBytes;
-    int qk_off[4], pv_off[2][2];
-    {
-      int ln = threadIdx.x & 63;
-      asm volatile("" : "+v"(ln));  // recompute per tile: keeps registers free
-      const int ll = ln & 31, hh = ln >> 5, k16 = ln & 15, g16 = (ln >> 4) & 1;
+    const bool load_next = i + 2 < ntiles;
+    const char* nsrc = pool;
+    int nrlast = kTile - 1;
+    uint32_t noff[kLoads];
+    if (load_next) {
+      tile_src(i + 2, &nsrc, &nrlast);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) qk_off[m] = swz(ll, 2 * m + hh) * 16;
-#pragma unroll
-      for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-          pv_off[c1][rr] = swz(8 * rr + 4 * hh + (k16 >> 2), 4 * c1 + 2 * g16 + ((k16 & 3) >> 1)) * 16 +
-                           8 * (k16 & 1);
+      for (int k = 0; k < kLoads; ++k) noff[k] = goff_lds[k * kThreads + tid];
     }
 
-    // ---- scores S^T (rows x heads): K fragments read three k-blocks ahead ----
-    f32x16_t s = f32x16_t{};
+    const uint32_t tile = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes);
+    const MLA_LDS char* tilep = tiles + (i % kBufs) * kTileBytes;
+
+    // ---- scores S^T (rows x heads): two accumulators (even / odd k-block),
+    // K fragments read five k-blocks ahead; the next tile's copies are issued
+    // between the MFMAs ----
+    f32x16_t s;
     {
-      bf16x8_t kf[3];
+      uint32_t qa[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) qa[m] = tile + (qk0 ^ (uint32_t)(m << 5));
+      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+      bf16x8_t kf[5];
       auto kaddr = [&](int kb) {
-        return (const MLA_LDS bf16x8_t*)(tile + qk_off[kb & 3] + (kb >> 2) * 128);
+        return (const MLA_LDS bf16x8_t*)(uintptr_t)(qa[kb & 3] + (kb >> 2) * 128);
       };
 #pragma unroll
-      for (int kb = 0; kb < 3; ++kb) kf[kb] = *kaddr(kb);
+      for (int kb = 0; kb < 5; ++kb) kf[kb] = *kaddr(kb);
 #pragma unroll
       for (int kb = 0; kb < kW / 16; ++kb) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 3], qf[kb], s, 0, 0, 0);
-        if (kb + 3 < kW / 16) kf[kb % 3] = *kaddr(kb + 3);
+        if (kb & 1)
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 5], qf[kb], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 5], qf[kb], s0, 0, 0, 0);
+        if (kb + 5 < kW / 16) kf[kb % 5] = *kaddr(kb + 5);
+        if ((kb & 3) == 3 && load_next) issue_load(i + 2, kb >> 2, noff[kb >> 2], nsrc, nrlast);
         __builtin_amdgcn_sched_barrier(0);
       }
+      s = s0 + s1;
     }
 
     // ---- softmax numerators: lane = head, 16 rows per lane (the rest in lane ^ 32) ----
     const int t0 = row_begin + i * kTile;
     const bool tail = t0 + kTile > row_end;
-    float mt = -INFINITY;
+    if (tail) {  // rows past the end do not take part in the maximum
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float v = s[j] * a.scale_log2;
-      if (tail) {
+      for (int j = 0; j < 16; ++j) {
         const int t = t0 + (j >> 2) * 8 + hf * 4 + (j & 3);
-        v = t < row_end ? v : -INFINITY;
+        s[j] = t < row_end ? s[j] : __builtin_nanf("");
       }
-      s[j] = v;
-      mt = fmaxf(mt, v);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    // extreme of the raw scores (max for a positive scale, min for a negative one);
+    // fmax/fmin ignore the NaN of masked rows
+    float e;
+    if (c >= 0.f) {
+      e = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      e = fmaxf(e, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                         fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+      e = fmaxf(e, __shfl_xor(e, 32, 64));
+    } else {
+      e = fminf(fminf(fminf(s[0], s[1]), fminf(s[2], s[3])), fminf(fminf(s[4], s[5]), fminf(s[6], s[7])));
+      e = fminf(e, fminf(fminf(fminf(s[8], s[9]), fminf(s[10], s[11])),
+                         fminf(fminf(s[12], s[13]), fminf(s[14], s[15]))));
+      e = fminf(e, __shfl_xor(e, 32, 64));
+    }
+    const float mt = e * c;
     m_seen = fmaxf(m_seen, mt);
     if (fresh) m_ref = fmaxf(m_ref, mt);
     fresh = false;
     pending = mt > m_ref + kRestartLog2;
-    bf16x8_t pb[2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float p = __builtin_amdgcn_exp2f(s[j] - m_ref);
-      lsum += p;
-      pb[j >> 3][j & 7] = (__bf16)p;
-    }
-    l_run += lsum;
 
-    // ---- O^T += V^T P^T: per 32-column block, 4 transpose reads one block ahead ----
+    // This lane's 16 numerators, bf16, into the shared P in slot order: head
+    // row h holds slot kb*16 + hf*8 + j <-> row 16*kb + 8*(j/4) + 4*hf + j%4,
+    // the order both MFMA operands of P*V use.  The denominator sums the fp32
+    // numerators (so lse stays exact to fp32, independent of the split plan).
     {
-      s16x4_t vf[2][4];
-      auto read_v = [&](int cb, s16x4_t* dst) {
+      float p[16];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const MLA_LDS char* base = tile + kb * (16 * kGran * 16) + (cb >> 1) * 128;
+      for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c, -m_ref));
+      if (tail) {
 #pragma unroll
-          for (int rr = 0; rr < 2; ++rr)
-            dst[2 * kb + rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (MLA_LDS s16x4_t*)(base + pv_off[cb & 1][rr]));
+        for (int j = 0; j < 16; ++j) {
+          const int t = t0 + (j >> 2) * 8 + hf * 4 + (j & 3);
+          p[j] = t < row_end ? p[j] : 0.f;
         }
-      };
-      read_v(0, vf[0]);
-      // the bf16 P operands were just written by VALU: pad before an MFMA reads them
-      asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
-#pragma unroll
-      for (int cb = 0; cb < kC / 32; ++cb) {
-        if (cb + 1 < kC / 32) read_v(cb + 1, vf[(cb + 1) & 1]);
-        const s16x8_t v0 = __builtin_shufflevector(vf[cb & 1][0], vf[cb & 1][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const s16x8_t v1 = __builtin_shufflevector(vf[cb & 1][2], vf[cb & 1][3], 0, 1, 2, 3, 4, 5, 6, 7);
-        // The accumulator is pinned to AGPRs (the score MFMAs use VGPRs).  The
-        // first k-block takes C = 0 right after a restart.
-        asm volatile(
-            "s_cmp_eq_u32 %4, 0\n\t"
-            "s_cbranch_scc1 1f\n\t"
-            "v_mfma_f32_32x32x16_bf16 %0, %1, %3, 0\n\t"
-            "s_branch 2f\n"
-            "1:\n\t"
-            "v_mfma_f32_32x32x16_bf16 %0, %1, %3, %0\n"
-            "2:\n\t"
-            "v_mfma_f32_32x32x16_bf16 %0, %2, %5, %0"
-            : "+a"(o[cb])
-            : "v"(v0), "v"(v1), "v"(pb[0]), "s"(zero_c), "v"(pb[1])
-            : "scc");
-        __builtin_amdgcn_sched_barrier(0);
       }
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)p[j];
+      float q0 = (p[0] + p[1]) + (p[2] + p[3]), q1 = (p[4] + p[5]) + (p[6] + p[7]);
+      float q2 = (p[8] + p[9]) + (p[10] + p[11]), q3 = (p[12] + p[13]) + (p[14] + p[15]);
+      l_run += (q0 + q1) + (q2 + q3);
+      MLA_LDS char* prow = p_lds + p_row + wave * (32 * kPRow);
+      *(MLA_LDS bf16x8_t*)prow = pb[0];
+      *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
+    }
+    __syncthreads();  // every head's P is visible
+
+    // ---- O^T += V^T P^T for this wave's 128 latent columns and all 128 heads:
+    // V is read from LDS once per workgroup ----
+    {
+      // column blocks 4*wave .. +3: (cb >> 1) = 2*wave + (cbl >> 1), cb & 1 = cbl & 1
+      uint32_t va[2][2];
+#pragma unroll
+      for (int c1 = 0; c1 < 2; ++c1)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          va[c1][rr] = tile + (((pv0 ^ (uint32_t)(64 * c1)) ^ (uint32_t)(32 * rr)) + 9216u * rr) +
+                       (uint32_t)(wave * 256);
+      auto vread = [&](int cbl, int kb) {
+        const uint32_t off = kb * (16 * kGran * 16) + (cbl >> 1) * 128;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][0] + off));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][1] + off));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      s16x8_t vf[2][4];
+      bf16x8_t pf[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          vf[kb][x] = vread(x, kb);
+          pf[kb][x] = *(const MLA_LDS bf16x8_t*)(p_lds + p_row + x * (32 * kPRow) + kb * 32);
+        }
+      }
+#pragma unroll
+      for (int cbl = 0; cbl < 4; ++cbl)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          // first k-block; C = 0 right after a restart
+          asm volatile(
+              "s_cmp_eq_u32 %3, 0\n\t"
+              "s_cbranch_scc1 1f\n\t"
+              "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\t"
+              "s_branch 2f\n"
+              "1:\n\t"
+              "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n"
+              "2:"
+              : "+a"(o[cbl * 4 + hb])
+              : "v"(vf[0][cbl]), "v"(pf[0][hb]), "s"(zero_c)
+              : "scc");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+      for (int cbl = 0; cbl < 4; ++cbl)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+a"(o[cbl * 4 + hb])
+                       : "v"(vf[1][cbl]), "v"(pf[1][hb]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
     zero_c = 0;
   }
@@ -329,17 +411,25 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
                : "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]),
                  "+a"(o[14]), "+a"(o[15]));
 
-  // ---- finish: normalise and store this lane's head ----
+  // ---- finish: this wave's 128 columns of every head, normalised by the
+  // head's denominator (owned by the lanes that computed its scores) ----
   const float l = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv_l = bad ? NAN : 1.0f / l;
+  if (hf == 0) l_heads[head] = l;
+  __syncthreads();
 #pragma unroll
-  for (int cb = 0; cb < kC / 32; ++cb) {
+  for (int hb = 0; hb < 4; ++hb) {
+    const float inv_l = bad ? NAN : 1.0f / l_heads[hb * 32 + l32];
+    float* dst = out_base + (size_t)(hb * 32 + l32) * kC + wave * 128;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int c = cb * 32 + q4 * 8 + hf * 4;
-      f32x4_t v{o[cb][4 * q4 + 0] * inv_l, o[cb][4 * q4 + 1] * inv_l,
-                o[cb][4 * q4 + 2] * inv_l, o[cb][4 * q4 + 3] * inv_l};
-      *reinterpret_cast<f32x4_t*>(out_o + c) = v;
+    for (int cbl = 0; cbl < 4; ++cbl) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = cbl * 32 + q4 * 8 + hf * 4;
+        const f32x16_t& ob = o[cbl * 4 + hb];
+        f32x4_t v{ob[4 * q4 + 0] * inv_l, ob[4 * q4 + 1] * inv_l, ob[4 * q4 + 2] * inv_l,
+                  ob[4 * q4 + 3] * inv_l};
+        *reinterpret_cast<f32x4_t*>(dst + col) = v;
+      }
     }
   }
   if (out_lse && hf == 0) *out_lse = bad ? NAN : (m_ref + log2f(l)) * kLn2;
@@ -389,7 +479,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
-  const size_t smem = kBufs * kTileBytes + (kMaxSplitTiles + 8) * sizeof(int);
+  const size_t smem = kSmemBytes;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel,
