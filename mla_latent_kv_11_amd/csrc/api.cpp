@@ -105,13 +105,18 @@ int plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t req, int32_t
   return MLA_OK;
 }
 
+// fp16 staging of a GEMM's activations (4-bit weights on MFMA): [Z, B, K]
+size_t ws_stage(int64_t Z, int32_t B, int64_t K) { return align_up((size_t)Z * B * K * 2); }
+
 size_t ws_append(const mla_dims* d, int32_t B) {
-  return d->hidden > 0 ? align_up((size_t)B * (d->kv_lora + d->qk_rope) * 4) : 0;
+  return d->hidden > 0 ? align_up((size_t)B * (d->kv_lora + d->qk_rope) * 4) + ws_stage(1, B, d->hidden)
+                       : 0;
 }
 size_t ws_absorb(const mla_dims* d, int32_t B) {
   if (d->q_lora <= 0) return 0;
+  const int64_t k = d->hidden > d->q_lora ? d->hidden : d->q_lora;
   return align_up((size_t)B * d->q_lora * 4) +
-         align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4);
+         align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4) + ws_stage(1, B, k);
 }
 size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
   if (splits <= 1) return 0;
@@ -119,7 +124,10 @@ size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
          align_up((size_t)B * splits * d->num_heads * 4);
 }
 size_t ws_out(const mla_dims* d, int32_t B) {
-  return d->hidden > 0 ? align_up((size_t)B * d->num_heads * d->v_head * 4) : 0;
+  const size_t heads = align_up((size_t)B * d->num_heads * d->v_head * 4);
+  const size_t st_uv = ws_stage(d->num_heads, B, d->kv_lora);
+  const size_t st_o = ws_stage(1, B, (int64_t)d->num_heads * d->v_head);
+  return d->hidden > 0 ? heads + (st_uv > st_o ? st_uv : st_o) : st_uv;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -227,7 +235,8 @@ int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_wei
     g.K = d->hidden;
     g.B = B;
     g.Z = 1;
-    if ((st = hip_status(launch_gemm_nt(g, s)))) return st;
+    void* stage = static_cast<char*>(ws) + align_up((size_t)B * W * 4);
+    if ((st = hip_status(launch_gemm_nt(g, stage, s)))) return st;
     kv_pre = static_cast<const float*>(ws);
   }
   AppendArgs a{};
@@ -278,6 +287,7 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
   if (q_a) {
     float* q_lat = static_cast<float*>(ws);
     float* q_full = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * d->q_lora * 4));
+    void* stage = reinterpret_cast<char*>(q_full) + align_up((size_t)B * H * (N + R) * 4);
     GemmArgs g{};
     g.w = view(q_a);
     g.x = q_in;
@@ -288,7 +298,7 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
     g.K = d->hidden;
     g.B = B;
     g.Z = 1;
-    if ((st = hip_status(launch_gemm_nt(g, s)))) return st;
+    if ((st = hip_status(launch_gemm_nt(g, stage, s)))) return st;
     if ((st = hip_status(launch_rmsnorm_rows(q_lat, B, d->q_lora, d->q_lora, view(q_a_norm),
                                              d->rms_eps, s))))
       return st;
@@ -302,7 +312,7 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
     g2.K = d->q_lora;
     g2.B = B;
     g2.Z = 1;
-    if ((st = hip_status(launch_gemm_nt(g2, s)))) return st;
+    if ((st = hip_status(launch_gemm_nt(g2, stage, s)))) return st;
     q = q_full;
   }
   AbsorbArgs a{};
@@ -390,10 +400,13 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
     if (d->hidden < 1) return MLA_ERR_DIMS;
     if ((st = check_weight(o_proj, d->hidden, (int64_t)H * V, true))) return st;
     if (!ws || ws_bytes < ws_out(d, B)) return MLA_ERR_WORKSPACE;
+  } else if (kv_b->dtype == MLA_Q4G64 && (!ws || ws_bytes < ws_out(d, B))) {
+    return MLA_ERR_WORKSPACE;
   }
   if (B == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* heads_out = o_proj ? static_cast<float*>(ws) : out;
+  void* stage = o_proj ? static_cast<char*>(ws) + align_up((size_t)B * H * V * 4) : ws;
   GemmArgs g{};
   g.w = view(kv_b);
   g.w_row0 = N;
@@ -408,7 +421,7 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
   g.K = C;
   g.B = B;
   g.Z = H;
-  if ((st = hip_status(launch_gemm_nt(g, s)))) return st;
+  if ((st = hip_status(launch_gemm_nt(g, stage, s)))) return st;
   if (o_proj) {
     GemmArgs g2{};
     g2.w = view(o_proj);
@@ -420,7 +433,7 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
     g2.K = H * V;
     g2.B = B;
     g2.Z = 1;
-    st = hip_status(launch_gemm_nt(g2, s));
+    st = hip_status(launch_gemm_nt(g2, stage, s));
   }
   return st;
 }

@@ -94,7 +94,11 @@ struct GemmArgs {
   int64_t y_b, y_z;
   int32_t O, K, B, Z;
 };
-hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t s);
+// 4-bit weights with K % 512 == 0 run on MFMA and need a staging buffer of
+// gemm_staging_bytes() for the fp16 copy of x; other weights ignore it.
+bool gemm_uses_mfma(const GemmArgs& a);
+size_t gemm_staging_bytes(const GemmArgs& a);
+hipError_t launch_gemm_nt(const GemmArgs& a, void* staging, hipStream_t s);
 
 // In-place RMSNorm of x[b][0..n) with gamma (1 x n weight of F32/BF16).
 hipError_t launch_rmsnorm_rows(float* x, int32_t B, int32_t n, int64_t stride, WeightView gamma,

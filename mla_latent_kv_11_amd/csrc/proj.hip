@@ -75,6 +75,81 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit affine weights on MFMA: y[z][b][o] = sum_k W[row(z, o)][k] x[z][b][k].
+// One workgroup = 32 outputs x 32 tokens; its 4 waves split K in quarters and
+// reduce through LDS (deterministic).  Per 128-k chunk a lane dequantises one
+// row's 64 consecutive k (8 packed words, one scale/bias group) into fp16 MFMA
+// A operands and multiplies them by 64 fp16 activations of one token:
+// v_mfma_f32_32x32x16_f16, k-slot j of lane-half h at step st <-> k = k0 + 64h
+// + 8st + j (the same map on both operands).  fp32 accumulate.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__global__ void __launch_bounds__(256) to_f16_kernel(const float* x, int64_t x_b, int64_t x_z,
+                                                     _Float16* y, int32_t B, int32_t K, int32_t Z) {
+  const int64_t n = (int64_t)Z * B * K;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t k = i % K, zb = i / K;
+    const int64_t bb = zb % B, z = zb / B;
+    y[i] = (_Float16)x[z * x_z + bb * x_b + k];
+  }
+}
+
+__global__ void __launch_bounds__(256) gemm_q4_mfma_kernel(GemmArgs a, const _Float16* xh) {
+  __shared__ f32x16_t red[3][64];
+  const int z = blockIdx.z;
+  const int o0 = blockIdx.x * 32;
+  const int b0 = blockIdx.y * 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+  const int kq = a.K / 4;
+  const int kbeg = wave * kq;
+
+  int row = o0 + l32;
+  row = row < a.O ? row : a.O - 1;  // rows past the end read a valid row; never stored
+  const int64_t wrow = a.w_row0 + (int64_t)z * a.w_zrows + row;
+  const uint32_t* wp = static_cast<const uint32_t*>(a.w.data) + wrow * (a.w.cols >> 3);
+  const uint16_t* sp = a.w.scales + wrow * (a.w.cols >> 6);
+  const uint16_t* bp = a.w.biases + wrow * (a.w.cols >> 6);
+  const int tok = b0 + l32;
+  const bool tok_ok = tok < a.B;
+  const _Float16* xp = xh + ((int64_t)z * a.B + (tok_ok ? tok : 0)) * a.K;
+
+  f32x16_t acc = f32x16_t{};
+  for (int k0 = kbeg; k0 < kbeg + kq; k0 += 128) {
+    const int kk = k0 + 64 * h;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(wp + (kk >> 3));
+    const uint4 w1 = *reinterpret_cast<const uint4*>(wp + (kk >> 3) + 4);
+    const float sc = bf16_to_f32(sp[kk >> 6]);
+    const float bi = bf16_to_f32(bp[kk >> 6]);
+    f16x8_t xf[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      xf[st] = tok_ok ? *reinterpret_cast<const f16x8_t*>(xp + kk + 8 * st) : f16x8_t{};
+    const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      f16x8_t wf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        wf[j] = (_Float16)fmaf((float)((words[st] >> (4 * j)) & 15u), sc, bi);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, xf[st], acc, 0, 0, 0);
+    }
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || !tok_ok) return;
+  acc += red[0][lane];
+  acc += red[1][lane];
+  acc += red[2][lane];
+  float* y = a.y + (int64_t)z * a.y_z + (int64_t)tok * a.y_b;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int o = o0 + (j >> 2) * 8 + h * 4 + (j & 3);
+    if (o < a.O) y[o] = acc[j];
+  }
+}
+
 // Sum over the 256 threads of a block; every thread gets the total.
 __device__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -145,37 +220,39 @@ __global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
   }
 }
 
-// grid (H, ceil(C/128)); thread = one latent column c of head h; tokens in
-// chunks of 16 with their q_nope rows staged in LDS.
-constexpr int kAbsC = 128, kAbsB = 16;
+// grid (H, ceil(C/128)); thread = one latent column c of head h.  Each W_UK
+// element is read (and dequantised) once per chunk of up to 32 tokens whose
+// q_nope rows are staged in LDS.
+constexpr int kAbsC = 128, kAbsB = 32;
 
 template <typename T>
 __global__ void __launch_bounds__(kAbsC) absorb_kernel(AbsorbArgs a) {
-  extern __shared__ float qn[];  // [kAbsB][N]
+  extern __shared__ float qn[];  // [N][kAbsB]: token-minor so one n is a broadcast row
   const int h = blockIdx.x;
   const int c = blockIdx.y * kAbsC + threadIdx.x;
   const int QW = a.N + a.R;
   const int W = a.C + a.R;
   T* out = static_cast<T*>(a.q_abs);
   const int64_t wrow = (int64_t)h * (a.N + a.V);
+  const int cc = c < a.C ? c : a.C - 1;
   for (int b0 = 0; b0 < a.B; b0 += kAbsB) {
     const int nb = (a.B - b0) < kAbsB ? (a.B - b0) : kAbsB;
-    for (int e = threadIdx.x; e < nb * a.N; e += kAbsC) {
-      const int bb = e / a.N, n = e - bb * a.N;
-      qn[bb * a.N + n] = a.q[((size_t)(b0 + bb) * a.H + h) * QW + n];
+    for (int e = threadIdx.x; e < kAbsB * a.N; e += kAbsC) {
+      const int n = e / kAbsB, bb = e - n * kAbsB;
+      qn[e] = bb < nb ? a.q[((size_t)(b0 + bb) * a.H + h) * QW + n] : 0.f;
     }
     __syncthreads();
-    if (c < a.C) {
-      float acc[kAbsB];
+    float acc[kAbsB];
 #pragma unroll
-      for (int i = 0; i < kAbsB; ++i) acc[i] = 0.f;
-      for (int n = 0; n < a.N; ++n) {
-        const float w = weight_at(a.kv_b, wrow + n, c);
+    for (int i = 0; i < kAbsB; ++i) acc[i] = 0.f;
+    for (int n = 0; n < a.N; ++n) {
+      const float w = weight_at(a.kv_b, wrow + n, cc);
+      const float* qrow = qn + n * kAbsB;
 #pragma unroll
-        for (int i = 0; i < kAbsB; ++i) acc[i] = fmaf(w, qn[i * a.N + n], acc[i]);
-      }
-      for (int i = 0; i < nb; ++i) Elem<T>::store(out, ((size_t)(b0 + i) * a.H + h) * W + c, acc[i]);
+      for (int i = 0; i < kAbsB; ++i) acc[i] = fmaf(w, qrow[i], acc[i]);
     }
+    if (c < a.C)
+      for (int i = 0; i < nb; ++i) Elem<T>::store(out, ((size_t)(b0 + i) * a.H + h) * W + c, acc[i]);
     __syncthreads();
   }
   if (blockIdx.y == 0) {
@@ -194,8 +271,26 @@ __global__ void __launch_bounds__(kAbsC) absorb_kernel(AbsorbArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
+bool gemm_uses_mfma(const GemmArgs& a) {
+  return a.w.dtype == MLA_Q4G64 && (a.K % 512) == 0 && (a.w.cols % 64) == 0 && a.K <= a.w.cols;
+}
+
+size_t gemm_staging_bytes(const GemmArgs& a) {
+  return gemm_uses_mfma(a) ? (size_t)a.Z * a.B * a.K * sizeof(_Float16) : 0;
+}
+
+hipError_t launch_gemm_nt(const GemmArgs& a, void* staging, hipStream_t s) {
   if (a.O <= 0 || a.B <= 0 || a.Z <= 0) return hipSuccess;
+  if (gemm_uses_mfma(a)) {
+    _Float16* xh = static_cast<_Float16*>(staging);
+    const int64_t n = (int64_t)a.Z * a.B * a.K;
+    const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(to_f16_kernel, dim3(blocks), dim3(256), 0, s, a.x, a.x_b, a.x_z, xh, a.B, a.K,
+                       a.Z);
+    dim3 grid((a.O + 31) / 32, (a.B + 31) / 32, a.Z);
+    hipLaunchKernelGGL(gemm_q4_mfma_kernel, grid, dim3(256), 0, s, a, (const _Float16*)xh);
+    return hipGetLastError();
+  }
   dim3 grid((a.O + kTO - 1) / kTO, (a.B + kTB - 1) / kTB, a.Z);
   hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -220,7 +315,7 @@ hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s) {
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   dim3 grid(a.H, (a.C + kAbsC - 1) / kAbsC);
-  const size_t smem = (size_t)kAbsB * a.N * sizeof(float);
+  const size_t smem = (size_t)kAbsB * a.N * sizeof(float);  // [N][32] token-minor
   if (a.cache_dtype == MLA_F32)
     hipLaunchKernelGGL(absorb_kernel<float>, grid, dim3(kAbsC), smem, s, a);
   else

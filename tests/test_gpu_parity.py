@@ -254,7 +254,11 @@ def test_out_proj(cfg, kw):
         close_f32(got, ref, "out")
     else:
         close_bf16(got, ref, "out")
-        assert np.max(np.abs(got - ref)) <= 1e-4 * np.max(np.abs(ref))
+        # 4-bit weights run on fp16 MFMA: each operand rounded to an 11-bit
+        # significand gives ~4e-4 rms relative error per GEMM stage, two stages
+        # here, so the largest error over the outputs stays well under 2e-3 max|ref|.
+        lim = 2e-3 if O.weight_dtype(case.kv_b) == O.Q4G64 else 1e-4
+        assert np.max(np.abs(got - ref)) <= lim * np.max(np.abs(ref))
 
 
 # ----------------------------------------------------------------------------
