@@ -105,18 +105,26 @@ int plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t req, int32_t
   return MLA_OK;
 }
 
-// fp16 staging of a GEMM's activations (4-bit weights on MFMA): [Z, B, K]
-size_t ws_stage(int64_t Z, int32_t B, int64_t K) { return align_up((size_t)Z * B * K * 2); }
-
+// Workspace regions of the projection calls (each 256-byte aligned); "packed"
+// is the fp16 activation layout of the 4-bit MFMA path (packed_index):
+//   append : x packed [B][hidden]; kv_a partial sums [S][B][W] fp32
+//   absorb : x packed [B][hidden]; q_a partial sums [S][B][q_lora] fp32;
+//            normalised q latent packed [B][q_lora]; q [B][H][N+R] fp32
+//   out    : v_combine packed [H][B][C]; per-head W_UV outputs [B][H*V]
+//            (packed fp16 for a 4-bit o_proj, else fp32)
 size_t ws_append(const mla_dims* d, int32_t B) {
-  return d->hidden > 0 ? align_up((size_t)B * (d->kv_lora + d->qk_rope) * 4) + ws_stage(1, B, d->hidden)
-                       : 0;
+  if (d->hidden <= 0) return 0;
+  return align_up(packed_bytes(1, B, d->hidden)) +
+         align_up((size_t)gemm_max_splits(d->hidden) * B * (d->kv_lora + d->qk_rope) * 4);
+}
+size_t ws_q_part(const mla_dims* d, int32_t B) {
+  return align_up((size_t)gemm_max_splits(d->hidden) * B * d->q_lora * 4);
 }
 size_t ws_absorb(const mla_dims* d, int32_t B) {
   if (d->q_lora <= 0) return 0;
-  const int64_t k = d->hidden > d->q_lora ? d->hidden : d->q_lora;
-  return align_up((size_t)B * d->q_lora * 4) +
-         align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4) + ws_stage(1, B, k);
+  return align_up(packed_bytes(1, B, d->hidden)) + ws_q_part(d, B) +
+         align_up(packed_bytes(1, B, d->q_lora)) +
+         align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4);
 }
 size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
   if (splits <= 1) return 0;
@@ -124,10 +132,8 @@ size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
          align_up((size_t)B * splits * d->num_heads * 4);
 }
 size_t ws_out(const mla_dims* d, int32_t B) {
-  const size_t heads = align_up((size_t)B * d->num_heads * d->v_head * 4);
-  const size_t st_uv = ws_stage(d->num_heads, B, d->kv_lora);
-  const size_t st_o = ws_stage(1, B, (int64_t)d->num_heads * d->v_head);
-  return d->hidden > 0 ? heads + (st_uv > st_o ? st_uv : st_o) : st_uv;
+  const size_t vc = align_up(packed_bytes(d->num_heads, B, d->kv_lora));
+  return vc + (d->hidden > 0 ? align_up((size_t)((B + 31) / 32) * 32 * d->num_heads * d->v_head * 4) : 0);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -224,23 +230,33 @@ int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_wei
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const float* kv_pre = x;
+  int kv_splits = 1;
   if (d->hidden > 0) {
+    char* base = static_cast<char*>(ws);
     GemmArgs g{};
     g.w = view(kv_a);
     g.x = x;
     g.x_b = d->hidden;
-    g.y = static_cast<float*>(ws);
+    g.y = reinterpret_cast<float*>(base + align_up(packed_bytes(1, B, d->hidden)));
     g.y_b = W;
+    g.y_s = (int64_t)B * W;
     g.O = W;
     g.K = d->hidden;
     g.B = B;
     g.Z = 1;
-    void* stage = static_cast<char*>(ws) + align_up((size_t)B * W * 4);
-    if ((st = hip_status(launch_gemm_nt(g, stage, s)))) return st;
-    kv_pre = static_cast<const float*>(ws);
+    if (gemm_mfma_ok(g)) {
+      g.xp = reinterpret_cast<_Float16*>(base);
+      if ((st = hip_status(launch_pack_f16(x, d->hidden, 0, 1, B, d->hidden,
+                                           reinterpret_cast<_Float16*>(base), s))))
+        return st;
+    }
+    if ((st = hip_status(launch_gemm_nt(g, gemm_max_splits(d->hidden), &kv_splits, s)))) return st;
+    kv_pre = g.y;
   }
   AppendArgs a{};
   a.kv_pre = kv_pre;
+  a.kv_splits = kv_splits;
+  a.kv_split_stride = (int64_t)B * W;
   a.gamma = view(kv_a_norm);
   a.inv_freq = rope->inv_freq;
   a.rope_mscale = rope->mscale;
@@ -285,26 +301,28 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
 
   const float* q = q_in;
   if (q_a) {
-    float* q_lat = static_cast<float*>(ws);
-    float* q_full = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * d->q_lora * 4));
-    void* stage = reinterpret_cast<char*>(q_full) + align_up((size_t)B * H * (N + R) * 4);
+    char* base = static_cast<char*>(ws);
+    _Float16* x_pk = reinterpret_cast<_Float16*>(base);
+    base += align_up(packed_bytes(1, B, d->hidden));
+    float* q_part = reinterpret_cast<float*>(base);
+    base += ws_q_part(d, B);
+    _Float16* q_lat_pk = reinterpret_cast<_Float16*>(base);
+    base += align_up(packed_bytes(1, B, d->q_lora));
+    float* q_full = reinterpret_cast<float*>(base);
     GemmArgs g{};
     g.w = view(q_a);
     g.x = q_in;
     g.x_b = d->hidden;
-    g.y = q_lat;
+    g.y = q_part;
     g.y_b = d->q_lora;
+    g.y_s = (int64_t)B * d->q_lora;
     g.O = d->q_lora;
     g.K = d->hidden;
     g.B = B;
     g.Z = 1;
-    if ((st = hip_status(launch_gemm_nt(g, stage, s)))) return st;
-    if ((st = hip_status(launch_rmsnorm_rows(q_lat, B, d->q_lora, d->q_lora, view(q_a_norm),
-                                             d->rms_eps, s))))
-      return st;
     GemmArgs g2{};
     g2.w = view(q_b);
-    g2.x = q_lat;
+    g2.x = q_part;  // normalised in place on the fp32 path
     g2.x_b = d->q_lora;
     g2.y = q_full;
     g2.y_b = (int64_t)H * (N + R);
@@ -312,7 +330,20 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
     g2.K = d->q_lora;
     g2.B = B;
     g2.Z = 1;
-    if ((st = hip_status(launch_gemm_nt(g2, stage, s)))) return st;
+    if (gemm_mfma_ok(g2)) g2.xp = q_lat_pk;
+    if (gemm_mfma_ok(g)) {
+      g.xp = x_pk;
+      if ((st = hip_status(launch_pack_f16(q_in, d->hidden, 0, 1, B, d->hidden, x_pk, s))))
+        return st;
+    }
+    int splits = 1;
+    if ((st = hip_status(launch_gemm_nt(g, gemm_max_splits(d->hidden), &splits, s)))) return st;
+    if ((st = hip_status(launch_rmsnorm_rows(q_part, splits, g.y_s, B, d->q_lora, d->q_lora,
+                                             view(q_a_norm), d->rms_eps,
+                                             g2.xp ? nullptr : q_part,
+                                             g2.xp ? q_lat_pk : nullptr, s))))
+      return st;
+    if ((st = hip_status(launch_gemm_nt(g2, 1, &splits, s)))) return st;
     q = q_full;
   }
   AbsorbArgs a{};
@@ -400,13 +431,12 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
     if (d->hidden < 1) return MLA_ERR_DIMS;
     if ((st = check_weight(o_proj, d->hidden, (int64_t)H * V, true))) return st;
     if (!ws || ws_bytes < ws_out(d, B)) return MLA_ERR_WORKSPACE;
-  } else if (kv_b->dtype == MLA_Q4G64 && (!ws || ws_bytes < ws_out(d, B))) {
-    return MLA_ERR_WORKSPACE;
   }
   if (B == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* heads_out = o_proj ? static_cast<float*>(ws) : out;
-  void* stage = o_proj ? static_cast<char*>(ws) + align_up((size_t)B * H * V * 4) : ws;
+  char* base = static_cast<char*>(ws);
+  _Float16* vc_pk = reinterpret_cast<_Float16*>(base);
+  void* heads = base + align_up(packed_bytes(H, B, C));
   GemmArgs g{};
   g.w = view(kv_b);
   g.w_row0 = N;
@@ -414,18 +444,17 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
   g.x = v_combine;
   g.x_b = (int64_t)H * C;
   g.x_z = C;
-  g.y = heads_out;
+  g.y = out;
   g.y_b = (int64_t)H * V;
   g.y_z = V;
   g.O = V;
   g.K = C;
   g.B = B;
   g.Z = H;
-  if ((st = hip_status(launch_gemm_nt(g, stage, s)))) return st;
+  GemmArgs g2{};
   if (o_proj) {
-    GemmArgs g2{};
     g2.w = view(o_proj);
-    g2.x = heads_out;
+    g2.x = static_cast<const float*>(heads);
     g2.x_b = (int64_t)H * V;
     g2.y = out;
     g2.y_b = d->hidden;
@@ -433,8 +462,23 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
     g2.K = H * V;
     g2.B = B;
     g2.Z = 1;
-    st = hip_status(launch_gemm_nt(g2, stage, s));
+    g.y = static_cast<float*>(heads);
+    if (gemm_mfma_ok(g2)) {  // W_UV writes packed fp16 straight for the MFMA path
+      g2.xp = static_cast<const _Float16*>(heads);
+      g.y = nullptr;
+      g.yp = static_cast<_Float16*>(heads);
+      g.yp_K = (int64_t)H * V;
+    }
   }
+  if (gemm_mfma_ok(g)) {
+    if (!ws || ws_bytes < ws_out(d, B)) return MLA_ERR_WORKSPACE;
+    g.xp = vc_pk;
+    if ((st = hip_status(launch_pack_f16(v_combine, (int64_t)H * C, C, H, B, C, vc_pk, s))))
+      return st;
+  }
+  int splits = 1;
+  if ((st = hip_status(launch_gemm_nt(g, 1, &splits, s)))) return st;
+  if (o_proj) st = hip_status(launch_gemm_nt(g2, 1, &splits, s));
   return st;
 }
 

@@ -85,27 +85,64 @@ hipError_t launch_attn_generic_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
 
 // y[z][b][o] = sum_k W[z*w_zrows + w_row0 + o][k] * x[z*x_z + b*x_b + k], o < O, k < K.
+//
+// The 4-bit MFMA path reads its activations packed (xp, fp16, see packed_index);
+// the fp32 path reads x.  The result goes to fp32 y or, for a following GEMM on
+// the MFMA path, packed fp16 yp holding the logical matrix [b][z*y_z + o] with
+// row length yp_K.  With K splits the partial sums of split s land at
+// y + s * y_s and the consumer adds them.
 struct GemmArgs {
   WeightView w;
   int64_t w_row0, w_zrows;
   const float* x;
+  const _Float16* xp;
   int64_t x_b, x_z;
   float* y;
-  int64_t y_b, y_z;
+  _Float16* yp;
+  int64_t y_b, y_z, y_s, yp_K;
   int32_t O, K, B, Z;
 };
-// 4-bit weights with K % 512 == 0 run on MFMA and need a staging buffer of
-// gemm_staging_bytes() for the fp16 copy of x; other weights ignore it.
-bool gemm_uses_mfma(const GemmArgs& a);
-size_t gemm_staging_bytes(const GemmArgs& a);
-hipError_t launch_gemm_nt(const GemmArgs& a, void* staging, hipStream_t s);
 
-// In-place RMSNorm of x[b][0..n) with gamma (1 x n weight of F32/BF16).
-hipError_t launch_rmsnorm_rows(float* x, int32_t B, int32_t n, int64_t stride, WeightView gamma,
-                               float eps, hipStream_t s);
+// Packed fp16 activations of a logical [Z][B][K] matrix (K % 128 == 0), laid
+// out in the order the MFMA lanes read them: tiles of 32 tokens, then units of
+// 128 k, then MFMA step st (8 k), lane half hh (64 k), token in tile, and 8
+// values in pair order k0 k4 k1 k5 k2 k6 k3 k7.  One step of one unit is 1 KB
+// contiguous for the 64 lanes.  Token slots past B are zero.
+__host__ __device__ __forceinline__ int64_t packed_index(int64_t z, int64_t b, int64_t k,
+                                                          int64_t B, int64_t K) {
+  const int64_t tiles = (B + 31) >> 5;
+  const int64_t unit = ((z * tiles + (b >> 5)) * (K >> 7) + (k >> 7));
+  const int64_t lane = ((k >> 6) & 1) * 32 + (b & 31);
+  return ((unit * 8 + ((k >> 3) & 7)) * 64 + lane) * 8 + ((k & 3) << 1) + ((k >> 2) & 1);
+}
+__host__ __device__ __forceinline__ size_t packed_bytes(int64_t Z, int64_t B, int64_t K) {
+  return (size_t)Z * ((B + 31) / 32) * 32 * K * 2;
+}
+
+constexpr int kMaxKSplits = 16;
+
+// True when the weight runs on the 4-bit MFMA path (which reads xp).
+bool gemm_mfma_ok(const GemmArgs& a);
+// Largest number of K splits the MFMA path may use for a depth K (workspace sizing).
+int gemm_max_splits(int64_t K);
+// Launches y = x W^T; *splits receives the number of K splits written (1 unless
+// max_splits > 1 and y is fp32).
+hipError_t launch_gemm_nt(const GemmArgs& a, int max_splits, int* splits, hipStream_t s);
+// Packs fp32 x[z*x_z + b*x_b + k] into packed fp16 (packed_index) for the MFMA path.
+hipError_t launch_pack_f16(const float* x, int64_t x_b, int64_t x_z, int32_t Z, int32_t B,
+                           int32_t K, _Float16* xp, hipStream_t s);
+
+// RMSNorm of rows b < B of the sum of S split partials part[s*split_stride +
+// b*stride + i], i < n, with gamma (1 x n weight of F32/BF16), written to
+// y[b*stride + i] (fp32; may alias part) or packed fp16 yp (n % 128 == 0).
+hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_stride, int32_t B,
+                               int32_t n, int64_t stride, WeightView gamma, float eps, float* y,
+                               _Float16* yp, hipStream_t s);
 
 struct AppendArgs {
-  const float* kv_pre;      // [B, W] fp32, pre-norm row
+  const float* kv_pre;      // [S][B, W] fp32 partial sums of the pre-norm row
+  int32_t kv_splits;        // S >= 1
+  int64_t kv_split_stride;
   WeightView gamma;         // 1 x C
   const float* inv_freq;    // [R/2]
   float rope_mscale;

@@ -12,6 +12,8 @@
 //                     (turbospark deepseek2/attn.rs, encode_mla_absorb_q).
 #include <math.h>
 
+#include <type_traits>
+
 #include "mla_common.h"
 
 namespace {
@@ -65,89 +67,173 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs a) {
     }
     __syncthreads();
   }
-  float* y = a.y + (int64_t)z * a.y_z;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int o = o0 + 4 * to + i, bb = b0 + 2 * tb + j;
-      if (o < a.O && bb < a.B) y[(int64_t)bb * a.y_b + o] = acc[i][j];
+      if (o >= a.O || bb >= a.B) continue;
+      if (a.yp)
+        a.yp[packed_index(0, bb, (int64_t)z * a.y_z + o, a.B, a.yp_K)] = (_Float16)acc[i][j];
+      else
+        a.y[(int64_t)z * a.y_z + (int64_t)bb * a.y_b + o] = acc[i][j];
     }
 }
 
 // ---------------------------------------------------------------------------
-// 4-bit affine weights on MFMA: y[z][b][o] = sum_k W[row(z, o)][k] x[z][b][k].
-// One workgroup = 32 outputs x 32 tokens; its 4 waves split K in quarters and
-// reduce through LDS (deterministic).  Per 128-k chunk a lane dequantises one
-// row's 64 consecutive k (8 packed words, one scale/bias group) into fp16 MFMA
-// A operands and multiplies them by 64 fp16 activations of one token:
-// v_mfma_f32_32x32x16_f16, k-slot j of lane-half h at step st <-> k = k0 + 64h
-// + 8st + j (the same map on both operands).  fp32 accumulate.
+// 4-bit affine weights on MFMA (v_mfma_f32_32x32x16_f16, fp32 accumulate).
+//
+// A workgroup owns 32 weight rows x 32 tokens and nw waves; wave w takes U
+// consecutive units of 128 k (unit u covers k = 128u .. 128u + 127) starting at
+// unit (s*nw + w)*U, where s is the workgroup's K split.  Tokens are the M
+// operand and weight rows the N operand, so the reduced tile is stored as 32
+// consecutive outputs per token.  In a unit, lane-half hh holds k = 128u + 64hh
+// + 8st + (0..7) at MFMA step st; register r of a step pairs k-offsets r and
+// r + 4, which are the two nibbles ((word >> 4r) & 0x000F000F) of packed word
+// st, and the packed activations hold the same pairs.  A nibble becomes fp16
+// 1024 + q through the exponent bits 0x6400, then q * scale + bias in packed
+// fp16 arithmetic.  The next unit's loads are issued before the current unit
+// is multiplied.  The nw partial tiles are added in LDS in a fixed order.
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-__global__ void __launch_bounds__(256) to_f16_kernel(const float* x, int64_t x_b, int64_t x_z,
-                                                     _Float16* y, int32_t B, int32_t K, int32_t Z) {
-  const int64_t n = (int64_t)Z * B * K;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t k = i % K, zb = i / K;
-    const int64_t bb = zb % B, z = zb / B;
-    y[i] = (_Float16)x[z * x_z + bb * x_b + k];
+constexpr int kQ4MaxWaves = 16;
+
+struct Unit {  // one lane's share of a unit: 64 nibbles of its row, 64 activations
+  uint4 w[2];
+  uint16_t sc, bi;
+  uint4 x[8];
+};
+
+__device__ __forceinline__ f16x8_t dequant8(uint32_t word, f16x2_t s2, f16x2_t b2) {
+  const f16x2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    const f16x2_t q = __builtin_bit_cast(f16x2_t, t) - k1024;
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
   }
+  return __builtin_bit_cast(f16x8_t, uint4{r[0], r[1], r[2], r[3]});
 }
 
-__global__ void __launch_bounds__(256) gemm_q4_mfma_kernel(GemmArgs a, const _Float16* xh) {
-  __shared__ f32x16_t red[3][64];
-  const int z = blockIdx.z;
-  const int o0 = blockIdx.x * 32;
-  const int b0 = blockIdx.y * 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
-  const int kq = a.K / 4;
-  const int kbeg = wave * kq;
+template <int U>
+__global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs a, int nw, int S) {
+  extern __shared__ float red[];  // [nw][16][64]
+  const int zz = blockIdx.z / S, s = blockIdx.z - zz * S;
+  const int o0 = blockIdx.x * 32, b0 = blockIdx.y * 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  const int units = a.K >> 7;
+  const int ubeg = (s * nw + wave) * U;
 
   int row = o0 + l32;
   row = row < a.O ? row : a.O - 1;  // rows past the end read a valid row; never stored
-  const int64_t wrow = a.w_row0 + (int64_t)z * a.w_zrows + row;
-  const uint32_t* wp = static_cast<const uint32_t*>(a.w.data) + wrow * (a.w.cols >> 3);
+  const int64_t wrow = a.w_row0 + (int64_t)zz * a.w_zrows + row;
+  const uint4* wp = static_cast<const uint4*>(a.w.data) + wrow * (a.w.cols >> 5);
   const uint16_t* sp = a.w.scales + wrow * (a.w.cols >> 6);
   const uint16_t* bp = a.w.biases + wrow * (a.w.cols >> 6);
-  const int tok = b0 + l32;
-  const bool tok_ok = tok < a.B;
-  const _Float16* xp = xh + ((int64_t)z * a.B + (tok_ok ? tok : 0)) * a.K;
+  const uint4* xq = reinterpret_cast<const uint4*>(a.xp) +
+                    ((int64_t)zz * gridDim.y + blockIdx.y) * units * 512 + lane;
 
+  Unit ub[2];
+  auto issue = [&](int slot, int ku) {
+    const int kq = ku * 2 + hh;  // 64-k quarter = scale group
+    ub[slot].w[0] = wp[2 * kq];
+    ub[slot].w[1] = wp[2 * kq + 1];
+    ub[slot].sc = sp[kq];
+    ub[slot].bi = bp[kq];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) ub[slot].x[st] = xq[(int64_t)ku * 512 + st * 64];
+  };
+
+  // Loads are issued unconditionally (units past the end re-read the last one)
+  // so the number of loads in flight is the same on every path and the wait
+  // before a unit's MFMAs leaves the next unit's loads outstanding.
+  const int ulast = units - 1;
   f32x16_t acc = f32x16_t{};
-  for (int k0 = kbeg; k0 < kbeg + kq; k0 += 128) {
-    const int kk = k0 + 64 * h;
-    const uint4 w0 = *reinterpret_cast<const uint4*>(wp + (kk >> 3));
-    const uint4 w1 = *reinterpret_cast<const uint4*>(wp + (kk >> 3) + 4);
-    const float sc = bf16_to_f32(sp[kk >> 6]);
-    const float bi = bf16_to_f32(bp[kk >> 6]);
-    f16x8_t xf[8];
+  issue(0, ubeg < ulast ? ubeg : ulast);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int ku = ubeg + u;
+    if (u + 1 < U) issue((u + 1) & 1, ku + 1 < ulast ? ku + 1 : ulast);
+    if (ku >= units) continue;
+    const Unit& c = ub[u & 1];
+    const _Float16 sh = (_Float16)bf16_to_f32(c.sc), bh = (_Float16)bf16_to_f32(c.bi);
+    const f16x2_t s2 = {sh, sh}, b2 = {bh, bh};
+    const uint32_t words[8] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w,
+                               c.w[1].x, c.w[1].y, c.w[1].z, c.w[1].w};
 #pragma unroll
     for (int st = 0; st < 8; ++st)
-      xf[st] = tok_ok ? *reinterpret_cast<const f16x8_t*>(xp + kk + 8 * st) : f16x8_t{};
-    const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      f16x8_t wf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        wf[j] = (_Float16)fmaf((float)((words[st] >> (4 * j)) & 15u), sc, bi);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, xf[st], acc, 0, 0, 0);
-    }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c.x[st]),
+                                                   dequant8(words[st], s2, b2), acc, 0, 0, 0);
   }
-  if (wave > 0) red[wave - 1][lane] = acc;
+
+#pragma unroll
+  for (int j = 0; j < 16; ++j) red[(wave * 16 + j) * 64 + lane] = acc[j];
   __syncthreads();
-  if (wave != 0 || !tok_ok) return;
-  acc += red[0][lane];
-  acc += red[1][lane];
-  acc += red[2][lane];
-  float* y = a.y + (int64_t)z * a.y_z + (int64_t)tok * a.y_b;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int o = o0 + (j >> 2) * 8 + h * 4 + (j & 3);
-    if (o < a.O) y[o] = acc[j];
+  const int nthr = nw * 64;
+  for (int e = threadIdx.x; e < 1024; e += nthr) {
+    const int ln = e & 63, j = e >> 6;
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += red[(w * 16 + j) * 64 + ln];
+    const int o = o0 + (ln & 31);
+    const int t = b0 + (j >> 2) * 8 + (ln >> 5) * 4 + (j & 3);
+    if (o >= a.O || t >= a.B) continue;
+    if (a.yp)
+      a.yp[packed_index(0, t, (int64_t)zz * a.y_z + o, a.B, a.yp_K)] = (_Float16)v;
+    else
+      a.y[(int64_t)s * a.y_s + (int64_t)zz * a.y_z + (int64_t)t * a.y_b + o] = v;
   }
+}
+
+// fp32 x[z*x_z + b*x_b + k] -> packed fp16; one thread writes one 16-byte chunk
+// (8 values of one token), so the stores are contiguous.
+__global__ void __launch_bounds__(256) pack_f16_kernel(const float* x, int64_t x_b, int64_t x_z,
+                                                       int32_t B, int32_t K, int64_t chunks,
+                                                       bool vec, _Float16* xp) {
+  const int64_t units = K >> 7, tiles = (B + 31) >> 5;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(c & 63);
+    const int64_t us = c >> 6;            // (unit_global * 8 + st)
+    const int st = (int)(us & 7);
+    const int64_t ug = us >> 3;           // (z * tiles + tile) * units + u
+    const int64_t u = ug % units, zt = ug / units;
+    const int64_t tile = zt % tiles, z = zt / tiles;
+    const int64_t b = tile * 32 + (lane & 31);
+    const int64_t k = u * 128 + (lane >> 5) * 64 + st * 8;
+    uint4 o = uint4{0u, 0u, 0u, 0u};
+    if (b < B) {
+      const float* src = x + z * x_z + b * x_b + k;
+      float v[8];
+      if (vec) {
+        const float4 v0 = reinterpret_cast<const float4*>(src)[0];
+        const float4 v1 = reinterpret_cast<const float4*>(src)[1];
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = src[i];
+      }
+      const f16x8_t h = {(_Float16)v[0], (_Float16)v[4], (_Float16)v[1], (_Float16)v[5],
+                         (_Float16)v[2], (_Float16)v[6], (_Float16)v[3], (_Float16)v[7]};
+      o = __builtin_bit_cast(uint4, h);
+    }
+    reinterpret_cast<uint4*>(xp)[c] = o;
+  }
+}
+
+// Sum of S <= kMaxKSplits partials p[s * stride]; every load is issued
+// unconditionally (clamped to split 0) so they overlap.
+__device__ __forceinline__ float sum_splits(const float* p, int S, int64_t stride) {
+  float v = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < kMaxKSplits; ++sp) {
+    const float t = p[(sp < S ? sp : 0) * stride];
+    v += sp < S ? t : 0.f;
+  }
+  return v;
 }
 
 // Sum over the 256 threads of a block; every thread gets the total.
@@ -167,15 +253,40 @@ __device__ __forceinline__ float gamma_at(const WeightView& g, int i) {
                             : bf16_to_f32(static_cast<const uint16_t*>(g.data)[i]);
 }
 
-__global__ void __launch_bounds__(256) rmsnorm_rows_kernel(float* x, int32_t n, int64_t stride,
-                                                           WeightView gamma, float eps) {
+__global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* part, int32_t S,
+                                                           int64_t split_stride, int32_t B,
+                                                           int32_t n, int64_t stride,
+                                                           WeightView gamma, float eps, float* y,
+                                                           _Float16* yp) {
   __shared__ float red[4];
-  float* row = x + (int64_t)blockIdx.x * stride;
+  const int64_t b = blockIdx.x;
+  constexpr int kPer = 8;  // values per thread kept in registers (n <= 2048)
+  float v[kPer];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) ss = fmaf(row[i], row[i], ss);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    v[r] = i < n ? sum_splits(part + b * stride + i, S, split_stride) : 0.f;
+    ss = fmaf(v[r], v[r], ss);
+  }
+  for (int i = threadIdx.x + 256 * kPer; i < n; i += 256) {
+    const float t = sum_splits(part + b * stride + i, S, split_stride);
+    ss = fmaf(t, t, ss);
+  }
   const float tot = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(tot / (float)n + eps);
-  for (int i = threadIdx.x; i < n; i += 256) row[i] = row[i] * inv * gamma_at(gamma, i);
+  auto put = [&](int i, float t) {
+    const float o = t * inv * gamma_at(gamma, i);
+    if (yp) yp[packed_index(0, b, i, B, n)] = (_Float16)o;
+    else y[b * stride + i] = o;
+  };
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    if (i < n) put(i, v[r]);
+  }
+  for (int i = threadIdx.x + 256 * kPer; i < n; i += 256)
+    put(i, sum_splits(part + b * stride + i, S, split_stride));
 }
 
 // (x, y) -> mscale * (x cos a - y sin a, x sin a + y cos a), a = pos * inv_freq,
@@ -205,16 +316,20 @@ __global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
     return;
   }
   const float* src = a.kv_pre + (size_t)b * W;
+  auto kv = [&](int i) { return sum_splits(src + i, a.kv_splits, a.kv_split_stride); };
   T* dst = static_cast<T*>(a.pool) + ((size_t)blk * a.block + pos % a.block) * W;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < a.C; i += 256) ss = fmaf(src[i], src[i], ss);
+  for (int i = threadIdx.x; i < a.C; i += 256) {
+    const float v = kv(i);
+    ss = fmaf(v, v, ss);
+  }
   const float tot = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(tot / (float)a.C + a.eps);
   for (int i = threadIdx.x; i < a.C; i += 256)
-    Elem<T>::store(dst, i, src[i] * inv * gamma_at(a.gamma, i));
+    Elem<T>::store(dst, i, kv(i) * inv * gamma_at(a.gamma, i));
   for (int i = threadIdx.x; i < a.R / 2; i += 256) {
     float ox, oy;
-    rope_pair(src[a.C + 2 * i], src[a.C + 2 * i + 1], pos, a.inv_freq[i], a.rope_mscale, &ox, &oy);
+    rope_pair(kv(a.C + 2 * i), kv(a.C + 2 * i + 1), pos, a.inv_freq[i], a.rope_mscale, &ox, &oy);
     Elem<T>::store(dst, a.C + 2 * i, ox);
     Elem<T>::store(dst, a.C + 2 * i + 1, oy);
   }
@@ -269,37 +384,181 @@ __global__ void __launch_bounds__(kAbsC) absorb_kernel(AbsorbArgs a) {
   }
 }
 
+// 4-bit W_UK on MFMA: q'[b][h][c] = sum_n W_UK[h][n][c] q_nope[b][h][n].
+// grid (H, ceil(C/128), ceil(B/32)), 256 threads.  The workgroup first loads
+// its W_UK slice (128 n x 128 c, 16 bytes per row per thread, coalesced) and
+// dequantises it into LDS as fp16 transposed to [c][n], so one MFMA operand
+// (8 consecutive n of one c) is one 16-byte LDS read.  Wave w then owns
+// columns c0..c0+31 (c0 = 128 blockIdx.y + 32 w) for 32 tokens: the token is
+// the MFMA M dimension and k-slot j of lane-half hh at step st is n = n0 +
+// 64hh + 8st + j on both operands.  Workgroups with blockIdx.y == 0 also
+// rotate q_pe of their tokens.
+constexpr int kAbsN = 128, kAbsCols = 128, kAbsPitch = kAbsN + 8;  // LDS row pitch in halfs
+
+template <typename T>
+__global__ void __launch_bounds__(256) absorb_q4_mfma_kernel(AbsorbArgs a) {
+  __shared__ _Float16 wt[kAbsCols * kAbsPitch];  // [c][n]
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.z * 32;
+  const int cw0 = blockIdx.y * kAbsCols;
+  const int QW = a.N + a.R;
+  const int W = a.C + a.R;
+  T* out = static_cast<T*>(a.q_abs);
+  if (blockIdx.y == 0) {
+    const int half = a.R / 2;
+    const int nb = (a.B - b0) < 32 ? (a.B - b0) : 32;
+    for (int e = threadIdx.x; e < nb * half; e += 256) {
+      const int bb = b0 + e / half, i = e % half;
+      const float* qp = a.q + ((size_t)bb * a.H + h) * QW + a.N;
+      float ox, oy;
+      rope_pair(qp[2 * i], qp[2 * i + 1], a.positions[bb], a.inv_freq[i], a.rope_mscale, &ox, &oy);
+      const size_t o = ((size_t)bb * a.H + h) * W + a.C + 2 * i;
+      Elem<T>::store(out, o, ox);
+      Elem<T>::store(out, o + 1, oy);
+    }
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  const int c0 = wave * 32;  // within the workgroup's columns
+  const bool wave_on = cw0 + c0 < a.C;
+  const int tok = b0 + l32;
+  const bool tok_ok = tok < a.B;
+  const float* qp = a.q + ((size_t)(tok_ok ? tok : 0) * a.H + h) * QW;
+  const int64_t row0 = (int64_t)h * (a.N + a.V);
+  const int64_t cols8 = a.kv_b.cols >> 3, cols64 = a.kv_b.cols >> 6;
+  // staging role: rows 2np, 2np+1 (np = thread % 64), columns 32 cq .. 32 cq + 31
+  const int np = threadIdx.x & 63, cq = threadIdx.x >> 6;
+  const int cst = cw0 + 32 * cq;
+  const bool st_on = cst < a.C;
+  f32x16_t acc = f32x16_t{};
+  for (int n0 = 0; n0 < a.N; n0 += kAbsN) {
+    if (st_on) {
+      uint4 wv[2];
+      float sc[2], bi[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int64_t row = row0 + n0 + 2 * np + r;
+        wv[r] = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(a.kv_b.data) +
+                                                row * cols8 + (cst >> 3));
+        sc[r] = bf16_to_f32(a.kv_b.scales[row * cols64 + (cst >> 6)]);
+        bi[r] = bf16_to_f32(a.kv_b.biases[row * cols64 + (cst >> 6)]);
+      }
+      const uint32_t w0[4] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w};
+      const uint32_t w1[4] = {wv[1].x, wv[1].y, wv[1].z, wv[1].w};
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const float v0 = fmaf((float)((w0[c >> 3] >> (4 * (c & 7))) & 15u), sc[0], bi[0]);
+        const float v1 = fmaf((float)((w1[c >> 3] >> (4 * (c & 7))) & 15u), sc[1], bi[1]);
+        const _Float16 pr[2] = {(_Float16)v0, (_Float16)v1};
+        *reinterpret_cast<uint32_t*>(&wt[(32 * cq + c) * kAbsPitch + 2 * np]) =
+            __builtin_bit_cast(uint32_t, pr);
+      }
+    }
+    __syncthreads();
+    if (wave_on) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int nb = 64 * hh + 8 * st;
+        f16x8_t qa = f16x8_t{};
+        if (tok_ok) {
+          const float4 x0 = *reinterpret_cast<const float4*>(qp + n0 + nb);
+          const float4 x1 = *reinterpret_cast<const float4*>(qp + n0 + nb + 4);
+          qa = f16x8_t{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                       (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+        }
+        const f16x8_t wb = *reinterpret_cast<const f16x8_t*>(&wt[(c0 + l32) * kAbsPitch + nb]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, wb, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  if (!wave_on) return;
+  const int c = cw0 + c0 + l32;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int t = b0 + (j >> 2) * 8 + hh * 4 + (j & 3);
+    if (t < a.B) Elem<T>::store(out, ((size_t)t * a.H + h) * W + c, acc[j]);
+  }
+}
+
 }  // namespace
 
-bool gemm_uses_mfma(const GemmArgs& a) {
-  return a.w.dtype == MLA_Q4G64 && (a.K % 512) == 0 && (a.w.cols % 64) == 0 && a.K <= a.w.cols;
-}
+namespace {
+constexpr int kMaxU = 16;
 
-size_t gemm_staging_bytes(const GemmArgs& a) {
-  return gemm_uses_mfma(a) ? (size_t)a.Z * a.B * a.K * sizeof(_Float16) : 0;
-}
-
-hipError_t launch_gemm_nt(const GemmArgs& a, void* staging, hipStream_t s) {
-  if (a.O <= 0 || a.B <= 0 || a.Z <= 0) return hipSuccess;
-  if (gemm_uses_mfma(a)) {
-    _Float16* xh = static_cast<_Float16*>(staging);
-    const int64_t n = (int64_t)a.Z * a.B * a.K;
-    const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-    hipLaunchKernelGGL(to_f16_kernel, dim3(blocks), dim3(256), 0, s, a.x, a.x_b, a.x_z, xh, a.B, a.K,
-                       a.Z);
-    dim3 grid((a.O + 31) / 32, (a.B + 31) / 32, a.Z);
-    hipLaunchKernelGGL(gemm_q4_mfma_kernel, grid, dim3(256), 0, s, a, (const _Float16*)xh);
-    return hipGetLastError();
+hipError_t launch_q4(const GemmArgs& a, int U, int nw, int S, hipStream_t s) {
+  dim3 grid((a.O + 31) / 32, (a.B + 31) / 32, a.Z * S);
+  const size_t lds = (size_t)nw * 16 * 64 * sizeof(float);
+  switch (U) {
+    case 1: hipLaunchKernelGGL(gemm_q4_mfma_kernel<1>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+    case 2: hipLaunchKernelGGL(gemm_q4_mfma_kernel<2>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+    case 4: hipLaunchKernelGGL(gemm_q4_mfma_kernel<4>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+    case 8: hipLaunchKernelGGL(gemm_q4_mfma_kernel<8>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+    default: hipLaunchKernelGGL(gemm_q4_mfma_kernel<16>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
   }
+  return hipGetLastError();
+}
+}  // namespace
+
+bool gemm_mfma_ok(const GemmArgs& a) {
+  return a.w.dtype == MLA_Q4G64 && a.K > 0 && (a.K % 128) == 0 && (a.w.cols % 64) == 0 &&
+         a.K <= a.w.cols && (a.K / 128) <= kQ4MaxWaves * kMaxU;
+}
+
+int gemm_max_splits(int64_t K) {
+  const int64_t units = (K + 127) / 128;
+  const int64_t s = (units + 7) / 8;
+  return (int)(s < 1 ? 1 : (s > kMaxKSplits ? kMaxKSplits : s));
+}
+
+hipError_t launch_gemm_nt(const GemmArgs& a, int max_splits, int* splits, hipStream_t s) {
+  *splits = 1;
+  if (a.O <= 0 || a.B <= 0 || a.Z <= 0) return hipSuccess;
+  if (a.yp && (a.yp_K % 128) != 0) return hipErrorInvalidValue;
+  if (gemm_mfma_ok(a)) {
+    if (!a.xp) return hipErrorInvalidValue;
+    const int units = a.K / 128;
+    const int64_t tiles = (int64_t)((a.O + 31) / 32) * a.Z * ((a.B + 31) / 32);
+    int U = 1, nw, S = 1;
+    if (max_splits > kMaxKSplits) max_splits = kMaxKSplits;
+    if (tiles >= 128 || max_splits <= 1 || a.yp) {
+      while ((units + U - 1) / U > kQ4MaxWaves) U *= 2;
+      nw = (units + U - 1) / U;
+    } else {  // few row tiles: spread K over workgroups, the consumer adds the splits
+      nw = units < 8 ? units : 8;
+      S = (units + nw - 1) / nw;
+      while (S > max_splits) {
+        U *= 2;
+        S = (units + nw * U - 1) / (nw * U);
+      }
+    }
+    *splits = S;
+    return launch_q4(a, U, nw, S, s);
+  }
+  if (!a.x) return hipErrorInvalidValue;  // the fp32 path reads x
   dim3 grid((a.O + kTO - 1) / kTO, (a.B + kTB - 1) / kTB, a.Z);
   hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_rows(float* x, int32_t B, int32_t n, int64_t stride, WeightView gamma,
-                               float eps, hipStream_t s) {
+hipError_t launch_pack_f16(const float* x, int64_t x_b, int64_t x_z, int32_t Z, int32_t B,
+                           int32_t K, _Float16* xp, hipStream_t s) {
+  if (Z <= 0 || B <= 0 || K <= 0) return hipSuccess;
+  if (K % 128 != 0) return hipErrorInvalidValue;
+  const bool vec = x_b % 4 == 0 && x_z % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  const int64_t chunks = (int64_t)packed_bytes(Z, B, K) / 16;
+  const int64_t blocks = (chunks + 255) / 256 < 8192 ? (chunks + 255) / 256 : 8192;
+  hipLaunchKernelGGL(pack_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, x_b, x_z, B, K,
+                     chunks, vec, xp);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_stride, int32_t B,
+                               int32_t n, int64_t stride, WeightView gamma, float eps, float* y,
+                               _Float16* yp, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, x, n, stride, gamma, eps);
+  if (S < 1 || S > kMaxKSplits || (yp && n % 128 != 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, part, S, split_stride, B, n,
+                     stride, gamma, eps, y, yp);
   return hipGetLastError();
 }
 
@@ -314,6 +573,14 @@ hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
+  if (a.kv_b.dtype == MLA_Q4G64 && a.N % kAbsN == 0 && a.C % 32 == 0) {
+    dim3 grid(a.H, (a.C + 127) / 128, (a.B + 31) / 32);
+    if (a.cache_dtype == MLA_F32)
+      hipLaunchKernelGGL(absorb_q4_mfma_kernel<float>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(absorb_q4_mfma_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid(a.H, (a.C + kAbsC - 1) / kAbsC);
   const size_t smem = (size_t)kAbsB * a.N * sizeof(float);  // [N][32] token-minor
   if (a.cache_dtype == MLA_F32)

@@ -162,7 +162,8 @@ def oracle_for(case):
     return O.decode_step(case)
 
 
-@pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(lens=[200, 64, 1], batch=3, paged=True))])
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(lens=[200, 64, 1], batch=3, paged=True)),
+                                    (5, dict(lens=[64] * 40, batch=40))])
 def test_cache_append(cfg, kw):
     case = S.make_case(cfg, **kw)
     ns = D.stage(case)
@@ -182,8 +183,15 @@ def test_cache_append(cfg, kw):
         ref = res["appended_rows"][b]
         if d.cache_dtype == O.F32:
             assert np.max(np.abs(g - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref)))
-        else:  # within one bf16 step of the unrounded row
+        elif case.kv_a is None or O.weight_dtype(case.kv_a) != O.Q4G64:
+            # within one bf16 step of the unrounded row
             assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+        else:
+            # 4-bit kv_a on fp16 MFMA: operand rounding leaves ~4e-4 rms(row) on
+            # top of the bf16 step; 2e-3 rms(row) is about five of those sigmas
+            rms = np.sqrt(np.mean(ref ** 2))
+            assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + 2e-3 * rms)
+            close_bf16(g, ref, "appended row")
     # every other row bit-identical (NaN fill included)
     assert np.array_equal(got[~written].view(np.uint8), case.pool[~written].view(np.uint8))
 
@@ -212,7 +220,9 @@ def test_cache_append_bad_positions_flagged():
 
 
 @pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(lens=[300, 1000], batch=2)),
-                                    (5, dict(lens=[70, 200], batch=2))])
+                                    (5, dict(lens=[70, 200], batch=2)),
+                                    (5, dict(lens=[64] * 40, batch=40)),
+                                    (5, dict(lens=[64] * 96, batch=96))])
 def test_absorb_q(cfg, kw):
     case = S.make_case(cfg, **kw)
     ns = D.stage(case)
@@ -233,7 +243,8 @@ def test_absorb_q(cfg, kw):
 
 
 @pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(lens=[50, 10], batch=2)),
-                                    (5, dict(lens=[70, 200], batch=2))])
+                                    (5, dict(lens=[70, 200], batch=2)),
+                                    (5, dict(lens=[64] * 40, batch=40))])
 def test_out_proj(cfg, kw):
     case = S.make_case(cfg, **kw)
     ns = D.stage(case)
