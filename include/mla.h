@@ -95,7 +95,9 @@ typedef struct mla_dims {
  *   MLA_BF16: data = uint16 [rows, cols]
  *   MLA_Q4G64: data = uint32 [rows, cols/8]; element k of a row sits in word
  *     k/8 at bits 4*(k%8)..+3 (low nibble first); scales, biases = bf16
- *     [rows, cols/64]; w = scale * nibble + bias.
+ *     [rows, cols/64]; w = scale * nibble + bias.  Products with a Q4G64
+ *     weight whose depth is a multiple of 128 run on fp16 MFMA: w and the
+ *     activations are rounded to fp16 (11-bit significands), sums are fp32.
  * A norm weight (gamma) is passed as a 1 x n matrix of MLA_F32 or MLA_BF16.
  * All pointers are device pointers. */
 typedef struct mla_weight {
@@ -212,7 +214,10 @@ int mla_absorb_q(const mla_dims* dims, int32_t batch, const float* q_in,
  *   lse          device float [batch, H] or NULL: natural-log sum of exp of
  *                the scaled scores
  * bf16 caches run on the MFMA kernel (H = 128, C = 512, R = 64, block_size a
- * multiple of 32); f32 caches on a VALU kernel of any shape.
+ * multiple of 32); f32 caches on a VALU kernel of any shape.  With more than
+ * one split the bf16 kernel keeps each split's normalised partial in fp16
+ * times a power-of-two scale per head (2^-11 relative rounding before the
+ * fp32 merge); the f32 kernel keeps fp32 partials.
  * Errors: NULL, DIMS (max_seq_len < 0, split_rows), UNSUPPORTED, CAPACITY
  * (max_seq_len > max_blocks_per_seq * block_size), WORKSPACE. */
 int mla_decode_attn(const mla_dims* dims, int32_t batch, const void* q_abs,

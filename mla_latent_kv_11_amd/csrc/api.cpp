@@ -126,10 +126,16 @@ size_t ws_absorb(const mla_dims* d, int32_t B) {
          align_up(packed_bytes(1, B, d->q_lora)) +
          align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4);
 }
+// Split partials: fp16 values plus a power-of-two exponent per (sequence,
+// split, head) for a bf16 cache, fp32 values for an fp32 cache; and the lse.
+size_t ws_attn_o(const mla_dims* d, int32_t B, int32_t splits) {
+  const size_t elem = d->cache_dtype == MLA_BF16 ? 2 : 4;
+  return align_up((size_t)B * splits * d->num_heads * d->kv_lora * elem);
+}
 size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
   if (splits <= 1) return 0;
-  return align_up((size_t)B * splits * d->num_heads * d->kv_lora * 4) +
-         align_up((size_t)B * splits * d->num_heads * 4);
+  const size_t lse = align_up((size_t)B * splits * d->num_heads * 4);
+  return ws_attn_o(d, B, splits) + lse * (d->cache_dtype == MLA_BF16 ? 2 : 1);
 }
 size_t ws_out(const mla_dims* d, int32_t B) {
   const size_t vc = align_up(packed_bytes(d->num_heads, B, d->kv_lora));
@@ -397,11 +403,14 @@ int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_c
   a.seq_lens = seq_lens;
   a.v_combine = v_combine;
   a.lse = lse;
-  a.part_o = static_cast<float*>(ws);
-  a.part_lse = splits > 1
-                   ? reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                              align_up((size_t)B * splits * d->num_heads * d->kv_lora * 4))
-                   : nullptr;
+  if (splits > 1) {
+    char* base = static_cast<char*>(ws);
+    if (bf16) a.part_oh = reinterpret_cast<_Float16*>(base);
+    else a.part_o = reinterpret_cast<float*>(base);
+    base += ws_attn_o(d, B, splits);
+    a.part_lse = reinterpret_cast<float*>(base);
+    if (bf16) a.part_exp = reinterpret_cast<float*>(base + align_up((size_t)B * splits * d->num_heads * 4));
+  }
   a.B = B;
   a.H = d->num_heads;
   a.C = d->kv_lora;

@@ -28,7 +28,8 @@
 //
 // Split-K (flash decoding): grid = (splits, batch). A split with a single
 // partition writes v_combine/lse directly; otherwise it writes the normalised
-// partial O and its lse, merged by attn_combine_kernel.
+// partial O (fp16 with a power-of-two exponent per head) and its lse, merged
+// by attn_combine_kernel.
 #include <math.h>
 
 #include <type_traits>
@@ -90,22 +91,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   int row_end = row_begin + a.split_rows;
   row_end = row_end < len ? row_end : len;
 
-  float* out_base;  // [128 heads][512] of this (sequence, split)
-  float* out_lse;
-  if (a.num_splits == 1) {
-    out_base = a.v_combine + (size_t)b * kH * kC;
-    out_lse = a.lse ? a.lse + (size_t)b * kH + head : nullptr;
-  } else {
-    const size_t bs = (size_t)b * a.num_splits + split;
-    out_base = a.part_o + bs * kH * kC;
-    out_lse = a.part_lse + bs * kH + head;
-  }
+  // Outputs of this (sequence, split): with one partition v_combine and lse
+  // directly, otherwise the fp16 partial [128 heads][512], its exponent and lse.
+  const size_t bs = (size_t)b * a.num_splits + split;
+  float* out_lse = a.num_splits == 1 ? (a.lse ? a.lse + (size_t)b * kH + head : nullptr)
+                                     : a.part_lse + bs * kH + head;
 
   if (row_begin >= row_end) {  // nothing to attend in this partition
     if (a.num_splits == 1) {
-      float* out_o = out_base + (size_t)head * kC;
+      float* out_o = a.v_combine + (size_t)b * kH * kC + (size_t)head * kC;
       for (int c = hf * 4; c < kC; c += 8)
         *reinterpret_cast<f32x4_t*>(out_o + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else if (hf == 0) {
+      a.part_exp[bs * kH + head] = 0.f;
     }
     if (out_lse && hf == 0) *out_lse = -INFINITY;
     return;
@@ -416,29 +414,75 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   const float l = l_run + __shfl_xor(l_run, 32, 64);
   if (hf == 0) l_heads[head] = l;
   __syncthreads();
+  if (a.num_splits == 1) {
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const float inv_l = bad ? NAN : 1.0f / l_heads[hb * 32 + l32];
-    float* dst = out_base + (size_t)(hb * 32 + l32) * kC + wave * 128;
+    for (int hb = 0; hb < 4; ++hb) {
+      const float inv_l = bad ? NAN : 1.0f / l_heads[hb * 32 + l32];
+      float* dst = a.v_combine + (size_t)b * kH * kC + (size_t)(hb * 32 + l32) * kC + wave * 128;
 #pragma unroll
-    for (int cbl = 0; cbl < 4; ++cbl) {
+      for (int cbl = 0; cbl < 4; ++cbl) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int col = cbl * 32 + q4 * 8 + hf * 4;
-        const f32x16_t& ob = o[cbl * 4 + hb];
-        f32x4_t v{ob[4 * q4 + 0] * inv_l, ob[4 * q4 + 1] * inv_l, ob[4 * q4 + 2] * inv_l,
-                  ob[4 * q4 + 3] * inv_l};
-        *reinterpret_cast<f32x4_t*>(dst + col) = v;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int col = cbl * 32 + q4 * 8 + hf * 4;
+          const f32x16_t& ob = o[cbl * 4 + hb];
+          f32x4_t v{ob[4 * q4 + 0] * inv_l, ob[4 * q4 + 1] * inv_l, ob[4 * q4 + 2] * inv_l,
+                    ob[4 * q4 + 3] * inv_l};
+          *reinterpret_cast<f32x4_t*>(dst + col) = v;
+        }
       }
+    }
+  } else {
+    // fp16 partial: O / l * 2^-e with e >= 0 the smallest exponent that keeps
+    // the head's largest magnitude under 2^15 (0 unless |V| is huge); the
+    // largest |O| / l of each head over the four waves meets in LDS (the P
+    // area, free after the barrier above).
+    MLA_LDS float* amax_lds = (MLA_LDS float*)p_lds;  // [4 waves][128 heads]
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      float mx = 0.f;
+#pragma unroll
+      for (int cbl = 0; cbl < 4; ++cbl)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(o[cbl * 4 + hb][j]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (hf == 0) amax_lds[wave * kH + hb * 32 + l32] = mx / l_heads[hb * 32 + l32];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int h = hb * 32 + l32;
+      const float amax = fmaxf(fmaxf(amax_lds[h], amax_lds[kH + h]),
+                               fmaxf(amax_lds[2 * kH + h], amax_lds[3 * kH + h]));
+      // floor(log2 amax) from the exponent bits; e keeps amax * 2^-e below 2^15
+      const int lg = (int)((__float_as_uint(amax) >> 23) & 255u) - 127;
+      const int e = (amax >= 32768.f && amax <= 3.0e38f) ? lg - 14 : 0;
+      const float scale = __uint_as_float((uint32_t)(127 - e) << 23);
+      const float inv_l = bad ? NAN : scale / l_heads[h];
+      _Float16* dst = a.part_oh + (bs * kH + h) * kC + wave * 128;
+#pragma unroll
+      for (int cbl = 0; cbl < 4; ++cbl) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int col = cbl * 32 + q4 * 8 + hf * 4;
+          const f32x16_t& ob = o[cbl * 4 + hb];
+          typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+          const f16x4_t v{(_Float16)(ob[4 * q4 + 0] * inv_l), (_Float16)(ob[4 * q4 + 1] * inv_l),
+                          (_Float16)(ob[4 * q4 + 2] * inv_l), (_Float16)(ob[4 * q4 + 3] * inv_l)};
+          *reinterpret_cast<f16x4_t*>(dst + col) = v;
+        }
+      }
+      if (wave == 0 && hf == 0) a.part_exp[bs * kH + h] = (float)e;
     }
   }
   if (out_lse && hf == 0) *out_lse = bad ? NAN : (m_ref + log2f(l)) * kLn2;
 }
 
 // Merge the normalised partials of every split: lse = log sum_s exp(lse_s),
-// v = sum_s exp(lse_s - lse) O_s.  One workgroup per (sequence, 2 heads), 128
+// v = sum_s exp(lse_s - lse) O_s, with O_s = 2^e_s * (stored fp16 value) for
+// the MFMA kernel's partials.  One workgroup per (sequence, 2 heads), 128
 // threads per head, 4 consecutive latent columns per thread and step; the max
 // and the weight sum over splits are wavefront reductions.  C % 4 == 0.
+template <bool kF16>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int b = blockIdx.y;
   const int h = blockIdx.x * 2 + (threadIdx.x >> 7);
@@ -466,9 +510,17 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     for (int s = 0; s < S; ++s) {
       const float ls = lse_s[(size_t)s * a.H];
       if (ls == -INFINITY) continue;
-      const float w = expf(ls - m);
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(
-          a.part_o + (((size_t)b * S + s) * a.H + h) * a.C + c);
+      const size_t off = (((size_t)b * S + s) * a.H + h) * a.C + c;
+      f32x4_t v;
+      float w = expf(ls - m);
+      if constexpr (kF16) {
+        typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+        const f16x4_t hv = *reinterpret_cast<const f16x4_t*>(a.part_oh + off);
+        v = f32x4_t{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
+        w = ldexpf(w, (int)a.part_exp[((size_t)b * S + s) * a.H + h]);
+      } else {
+        v = *reinterpret_cast<const f32x4_t*>(a.part_o + off);
+      }
       acc += w * v;
     }
     *reinterpret_cast<f32x4_t*>(dst + c) = acc * inv;
@@ -492,7 +544,10 @@ hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
+  if (a.part_oh)
+    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<false>, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

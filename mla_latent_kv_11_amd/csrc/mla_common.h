@@ -73,7 +73,9 @@ struct AttnArgs {
   const int32_t* seq_lens;  // [B]
   float* v_combine;         // [B, H, C]
   float* lse;               // [B, H] or null
-  float* part_o;            // [B, S, H, C] (S > 1)
+  float* part_o;            // [B, S, H, C] fp32 partials (fp32 kernel, S > 1)
+  _Float16* part_oh;        // [B, S, H, C] fp16 partials * 2^-part_exp (MFMA kernel, S > 1)
+  float* part_exp;          // [B, S, H]    the exponent e of each fp16 partial
   float* part_lse;          // [B, S, H]   (S > 1)
   int32_t B, H, C, R, block, max_blocks, num_blocks;
   int32_t max_len, split_rows, num_splits;

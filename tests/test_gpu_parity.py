@@ -140,6 +140,27 @@ def test_attn_growing_scores_restart_path():
         close_bf16(lse, rlse, f"lse split={split}")
 
 
+def test_attn_split_partials_beyond_fp16_range():
+    # Latent values scaled by 2^17 (exact in bf16) and the latent part of q by
+    # 2^-17: the scores are unchanged and v_combine scales by 2^17, past the
+    # fp16 range the split partials are stored in, so the per-head exponent
+    # must carry the scale through the combine.
+    case = S.make_case(4, lens=[300, 200], seed=16)
+    pool = S.bf16_bits_to_f32(case.pool)
+    pool[..., :512] *= 2.0 ** 17
+    case.pool = S.to_bf16_bits(pool)
+    q = S.bf16_bits_to_f32(case.q_abs)
+    q[..., :512] *= 2.0 ** -17
+    case.q_abs = S.to_bf16_bits(q)
+    ns = D.stage(case)
+    rvc, rlse = oracle_attn(case)
+    for split in (0, 64):
+        vc, lse = attn_only(case, ns, split)
+        assert np.isfinite(vc).all()
+        close_bf16(vc * 2.0 ** -17, rvc * 2.0 ** -17, f"v_combine / 2^17 split={split}")
+        close_bf16(lse, rlse, f"lse split={split}")
+
+
 def test_attn_f32_kernel_config1_shapes():
     case = S.make_case(1, sharp=True)
     rng = np.random.default_rng(15)
