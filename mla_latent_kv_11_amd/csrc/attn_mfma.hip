@@ -176,11 +176,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // Copy granule k of tile i: 16 bytes per lane straight into LDS at
   // M0 + 16 * lane.  Issued from asm so that the compiler does not treat every
   // later LDS read as aliasing the copy; the explicit vmcnt waits order them.
-  auto issue_load = [&](int i, int k, uint32_t off, const char* src, int rlast) {
-    if (rlast < kTile - 1) {
-      const int r = (int)(off / (kW * 2));
-      if (r > rlast) off -= (uint32_t)((r - rlast) * (kW * 2));
-    }
+  auto clamp_rows = [&](uint32_t off, int rlast) {  // rows past rlast re-read row rlast
+    const int r = (int)(off / (kW * 2));
+    return r > rlast ? off - (uint32_t)((r - rlast) * (kW * 2)) : off;
+  };
+  auto issue_load = [&](int i, int k, uint32_t off, const char* src) {
     const uint32_t lds = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes + (k * 4 + wave) * 1024);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
@@ -192,7 +192,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     int rlast;
     tile_src(i, &src, &rlast);
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) issue_load(i, k, goff_lds[k * kThreads + tid], src, rlast);
+    for (int k = 0; k < kLoads; ++k) {
+      uint32_t off = goff_lds[k * kThreads + tid];
+      if (rlast < kTile - 1) off = clamp_rows(off, rlast);
+      issue_load(i, k, off, src);
+    }
   };
 
   f32x16_t o[kC / 32];
@@ -243,14 +247,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     }
     if (i == ntiles) break;
     bad |= tile_base[i] < 0;
-    const bool load_next = i + 2 < ntiles;
+    // Copies of tile i + 2 go out between the score MFMAs.  Past the split's
+    // end they still go out (no branch in the MFMA sequence): they re-read the
+    // pool's first 32 rows into the idle third buffer, and the vmcnt(0) at
+    // the top of the last passes drains them.
     const char* nsrc = pool;
     int nrlast = kTile - 1;
     uint32_t noff[kLoads];
-    if (load_next) {
-      tile_src(i + 2, &nsrc, &nrlast);
 #pragma unroll
-      for (int k = 0; k < kLoads; ++k) noff[k] = goff_lds[k * kThreads + tid];
+    for (int k = 0; k < kLoads; ++k) noff[k] = goff_lds[k * kThreads + tid];
+    if (i + 2 < ntiles) {
+      tile_src(i + 2, &nsrc, &nrlast);
+      if (nrlast < kTile - 1) {  // the split's last tile: once per split
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) noff[k] = clamp_rows(noff[k], nrlast);
+      }
     }
 
     const uint32_t tile = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes);
@@ -264,11 +275,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       uint32_t qa[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) qa[m] = tile + (qk0 ^ (uint32_t)(m << 5));
-      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-      bf16x8_t kf[5];
       auto kaddr = [&](int kb) {
         return (const MLA_LDS bf16x8_t*)(uintptr_t)(qa[kb & 3] + (kb >> 2) * 128);
       };
+      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+      bf16x8_t kf[5];
 #pragma unroll
       for (int kb = 0; kb < 5; ++kb) kf[kb] = *kaddr(kb);
 #pragma unroll
@@ -278,7 +289,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         else
           s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 5], qf[kb], s0, 0, 0, 0);
         if (kb + 5 < kW / 16) kf[kb % 5] = *kaddr(kb + 5);
-        if ((kb & 3) == 3 && load_next) issue_load(i + 2, kb >> 2, noff[kb >> 2], nsrc, nrlast);
+        if ((kb & 3) == 3) issue_load(i + 2, kb >> 2, noff[kb >> 2], nsrc);
         __builtin_amdgcn_sched_barrier(0);
       }
       s = s0 + s1;
@@ -360,15 +371,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
             (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][1] + off));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
+      // Issued in the order the MFMAs below consume them (P of the k-block
+      // first, then V^T by column block), so the first MFMAs start early.
       s16x8_t vf[2][4];
       bf16x8_t pf[2][4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          vf[kb][x] = vread(x, kb);
+        for (int x = 0; x < 4; ++x)
           pf[kb][x] = *(const MLA_LDS bf16x8_t*)(p_lds + p_row + x * (32 * kPRow) + kb * 32);
-        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) vf[kb][x] = vread(x, kb);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int cbl = 0; cbl < 4; ++cbl)

@@ -75,6 +75,17 @@ def test_attn_bf16_ragged_paged(split_rows):
     close_bf16(lse, rlse, f"lse split={split_rows}")
 
 
+def test_attn_more_splits_than_one_weight_chunk():
+    # 71 splits of 64 rows for the long sequence: the combine walks its split
+    # weights in chunks of 64; the short sequence leaves 69 splits empty.
+    case = S.make_case(4, lens=[4500, 130], paged=True, seed=17)
+    ns = D.stage(case)
+    vc, lse = attn_only(case, ns, 64)
+    rvc, rlse = oracle_attn(case)
+    close_bf16(vc, rvc, "v_combine")
+    close_bf16(lse, rlse, "lse")
+
+
 def test_attn_bf16_invariances():
     case = S.make_case(4, lens=[700, 5, 129], paged=True, seed=12)
     ns = D.stage(case)
