@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROW_BYTES = 576 * 2            # one bf16 cache row [c_kv ; k_pe]
 ROW_FLOPS = 2 * 128 * 576 + 2 * 128 * 512   # scores + latent combine per row, 128 heads
-COUNTERS = os.path.join(ROOT, "profiles", "attn_mfma_cfg5_counters.md")
+COUNTERS = os.path.join(ROOT, "profiles", "attn_mfma_b32_L16384_counters.md")
 KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_11_amd", "csrc", "attn_mfma.hip")
 
 
