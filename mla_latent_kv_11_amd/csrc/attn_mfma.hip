@@ -295,6 +295,33 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       s = s0 + s1;
     }
 
+    // ---- V^T fragments for this wave's 128 latent columns (column blocks
+    // 4*wave .. +3: (cb >> 1) = 2*wave + (cbl >> 1), cb & 1 = cbl & 1).  They do
+    // not depend on P, so they are read now and land while the softmax runs. ----
+    s16x8_t vf[2][4];
+    {
+      uint32_t va[2][2];
+#pragma unroll
+      for (int c1 = 0; c1 < 2; ++c1)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          va[c1][rr] = tile + (((pv0 ^ (uint32_t)(64 * c1)) ^ (uint32_t)(32 * rr)) + 9216u * rr) +
+                       (uint32_t)(wave * 256);
+      auto vread = [&](int cbl, int kb) {
+        const uint32_t off = kb * (16 * kGran * 16) + (cbl >> 1) * 128;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][0] + off));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][1] + off));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) vf[kb][x] = vread(x, kb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     // ---- softmax numerators: lane = head, 16 rows per lane (the rest in lane ^ 32) ----
     const int t0 = row_begin + i * kTile;
     const bool tail = t0 + kTile > row_end;
@@ -312,12 +339,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       e = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
       e = fmaxf(e, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
                          fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-      e = fmaxf(e, __shfl_xor(e, 32, 64));
+      float lo, hi;
+      wave_halves(e, &lo, &hi);
+      e = fmaxf(lo, hi);
     } else {
       e = fminf(fminf(fminf(s[0], s[1]), fminf(s[2], s[3])), fminf(fminf(s[4], s[5]), fminf(s[6], s[7])));
       e = fminf(e, fminf(fminf(fminf(s[8], s[9]), fminf(s[10], s[11])),
                          fminf(fminf(s[12], s[13]), fminf(s[14], s[15]))));
-      e = fminf(e, __shfl_xor(e, 32, 64));
+      float lo, hi;
+      wave_halves(e, &lo, &hi);
+      e = fminf(lo, hi);
     }
     const float mt = e * c;
     m_seen = fmaxf(m_seen, mt);
@@ -355,35 +386,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     // ---- O^T += V^T P^T for this wave's 128 latent columns and all 128 heads:
     // V is read from LDS once per workgroup ----
     {
-      // column blocks 4*wave .. +3: (cb >> 1) = 2*wave + (cbl >> 1), cb & 1 = cbl & 1
-      uint32_t va[2][2];
-#pragma unroll
-      for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-          va[c1][rr] = tile + (((pv0 ^ (uint32_t)(64 * c1)) ^ (uint32_t)(32 * rr)) + 9216u * rr) +
-                       (uint32_t)(wave * 256);
-      auto vread = [&](int cbl, int kb) {
-        const uint32_t off = kb * (16 * kGran * 16) + (cbl >> 1) * 128;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][0] + off));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][1] + off));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      // Issued in the order the MFMAs below consume them (P of the k-block
-      // first, then V^T by column block), so the first MFMAs start early.
-      s16x8_t vf[2][4];
       bf16x8_t pf[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           pf[kb][x] = *(const MLA_LDS bf16x8_t*)(p_lds + p_row + x * (32 * kPRow) + kb * 32);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) vf[kb][x] = vread(x, kb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
 #pragma unroll
       for (int cbl = 0; cbl < 4; ++cbl)
 #pragma unroll
@@ -425,7 +433,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 
   // ---- finish: this wave's 128 columns of every head, normalised by the
   // head's denominator (owned by the lanes that computed its scores) ----
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  float l_lo, l_hi;
+  wave_halves(l_run, &l_lo, &l_hi);
+  const float l = l_lo + l_hi;
   if (hf == 0) l_heads[head] = l;
   __syncthreads();
   if (a.num_splits == 1) {
@@ -458,7 +468,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       for (int cbl = 0; cbl < 4; ++cbl)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(o[cbl * 4 + hb][j]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float m_lo, m_hi;
+      wave_halves(mx, &m_lo, &m_hi);
+      mx = fmaxf(m_lo, m_hi);
       if (hf == 0) amax_lds[wave * kH + hb * 32 + l32] = mx / l_heads[hb * 32 + l32];
     }
     __syncthreads();

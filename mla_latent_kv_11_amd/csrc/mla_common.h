@@ -56,6 +56,15 @@ __device__ __forceinline__ float weight_at(const WeightView& w, int64_t r, int64
   return fmaf(bf16_to_f32(w.scales[g]), q, bf16_to_f32(w.biases[g]));
 }
 
+// The two halves of a wave side by side: lo = x[lane % 32], hi = x[lane % 32 + 32]
+// in every lane, by v_permlane32_swap (a VALU op; no LDS traffic, so it does
+// not wait behind outstanding LDS reads the way a bpermute shuffle does).
+__device__ __forceinline__ void wave_halves(float x, float* lo, float* hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  *lo = __uint_as_float(r[0]);
+  *hi = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
