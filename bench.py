@@ -4,6 +4,10 @@
 A step is one pass of the whole decode path over one batch: kv_a projection +
 latent RMSNorm + YaRN RoPE + paged append, the q chain + absorb, decode
 attention over the paged latent cache, the W_UV expansion and o_proj.  The
+append and the absorb are independent and run on two streams, and the whole
+step is replayed as one HIP graph (``--eager``: every call launched on one
+stream).  The attention call is then timed alone with HIP events around
+back-to-back launches on the same inputs.  The
 workload is the full per-layer configuration: batch 32, 16384 cached rows per
 sequence (append at 16383), DeepSeek-V3 shapes (128 heads, latent 512, rope
 64), hidden 7168, q_lora 1536, 4-bit affine (group 64) projections, bf16
@@ -62,7 +66,7 @@ def stored_traffic():
     return c.get("hbm_bytes_per_call")
 
 
-def time_attn_only(cfg, torch, D, S, mla, iters=20, warm=5):
+def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50):
     """Attention call alone on a full-size configuration (q_abs given or absorbed once)."""
     case = S.make_case(cfg)
     ns = D.stage(case)
@@ -153,11 +157,15 @@ def S_sub(case, seqs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU needs some tens of ms of sustained load to reach steady clocks;
+    # 200 steps are about 60 ms
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extra", action="store_true", help="skip the per-configuration attention lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call eagerly on one stream (no graphs, no second stream)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -178,38 +186,42 @@ def main():
     mla.load_library()
     case = S.make_case(5)
     ns = D.stage(case)
-    ws = D.workspace(ns)
-    stream = torch.cuda.current_stream()
     B = case.batch
     rows = int(case.lens.sum())
-
-    def step(ev=None):
-        mla.cache_append(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq, ns.rope_mscale,
-                         ns.positions, ns.pool, ns.table, ns.status, ws)
-        mla.absorb_q(ns.dims, ns.x, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
-                     ns.q_a, ns.q_a_norm, ns.q_b, ws)
-        if ev is not None:
-            ev[0].record(stream)
-        mla.decode_attn(ns.dims, ns.q_abs, ns.pool, ns.table, ns.lens, ns.max_len,
-                        ns.softmax_scale, ns.v_combine, ns.lse, 0, ws)
-        if ev is not None:
-            ev[1].record(stream)
-        mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws)
-
+    # One step = cache_append and absorb_q (two streams: independent), then
+    # decode_attn, then out_proj, replayed as one HIP graph (--eager: the calls
+    # launched one by one on one stream).
+    step = D.GraphStep(case, ns, two_streams=not args.eager)
     for _ in range(args.warmup):
-        step()
+        step.run(eager=True)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    if not args.eager:
+        step.capture()
+        for _ in range(args.warmup):
+            step.run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step.run(eager=args.eager)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms_step = wall * 1e3 / args.steps
     assert int(ns.status.cpu()[0]) == 0
+
+    # The attention call on its stream: back-to-back launches of the same call
+    # on the step's inputs between two HIP events (events cannot time a node
+    # inside a replayed graph).
+    stream = torch.cuda.current_stream()
+    n_attn = max(args.steps, 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step.attn()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n_attn):
+        step.attn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = e0.elapsed_time(e1) / n_attn
 
     byts, flops = attn_alg(B, rows)
     t_attn = attn_ms * 1e-3
@@ -232,6 +244,8 @@ def main():
             "workload": "MLA decode layer, batch 32, L=16384 (append at 16383), 128 heads, "
                         "kv_lora 512 + rope 64, hidden 7168, q_lora 1536, 4-bit g64 projections, "
                         "bf16 paged cache (64-row blocks)",
+            "launch": "eager, one stream" if args.eager else
+                      "one HIP graph per step; append | absorb on two streams",
             "global_batch": B, "seq_len": int(ns.max_len), "parallelism": "none (1 GPU)",
             "split_rows": r_split, "splits_per_seq": n_split,
         },
@@ -244,6 +258,7 @@ def main():
             "traffic": stored_traffic(),
             "kernel": "mla_decode_attn (attn_mfma_kernel + attn_combine_kernel)",
             "ms_per_launch": round(attn_ms, 4),
+            "timing": f"{n_attn} back-to-back decode_attn calls between two HIP events",
             "alg_bytes": byts,
             "mfma_tflops": round(flops / t_attn / 1e12, 1),
             "mfma_frac": round(flops / t_attn / 1e12 / BF16_PEAK_TFLOPS, 3),

@@ -79,7 +79,9 @@ int max_split_rows(const mla_dims* d) {
 }
 
 // Rows per split and splits per sequence.  Automatic: about one workgroup per
-// compute unit over batch * max_seq_len rows, at least 256 rows per split.
+// compute unit over batch * max_seq_len rows, at least 256 rows per split: each
+// split also reads the sequence's 147 KB query and writes a 128 KB partial, so
+// shorter splits cost more in overhead than they gain in parallelism.
 int plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t req, int32_t* rows,
          int32_t* splits) {
   if (max_len < 0 || batch < 0) return MLA_ERR_DIMS;

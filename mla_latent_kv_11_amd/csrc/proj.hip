@@ -129,22 +129,28 @@ __global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs
 
   int row = o0 + l32;
   row = row < a.O ? row : a.O - 1;  // rows past the end read a valid row; never stored
-  const int64_t wrow = a.w_row0 + (int64_t)zz * a.w_zrows + row;
-  const uint4* wp = static_cast<const uint4*>(a.w.data) + wrow * (a.w.cols >> 5);
-  const uint16_t* sp = a.w.scales + wrow * (a.w.cols >> 6);
-  const uint16_t* bp = a.w.biases + wrow * (a.w.cols >> 6);
-  const uint4* xq = reinterpret_cast<const uint4*>(a.xp) +
-                    ((int64_t)zz * gridDim.y + blockIdx.y) * units * 512 + lane;
+  const uint32_t wrow = (uint32_t)(a.w_row0 + (int64_t)zz * a.w_zrows + row);
+  // Per-lane 32-bit byte offsets from uniform bases (the matrices are under
+  // 2 GiB), so each load takes one address register instead of a 64-bit pointer.
+  const char* wbase = static_cast<const char*>(a.w.data);
+  const char* sbase = reinterpret_cast<const char*>(a.w.scales);
+  const char* bbase = reinterpret_cast<const char*>(a.w.biases);
+  const char* xbase = reinterpret_cast<const char*>(a.xp);
+  const uint32_t woff = wrow * (uint32_t)(a.w.cols >> 1) + 32u * hh;  // + 64 per unit
+  const uint32_t soff = wrow * (uint32_t)(a.w.cols >> 6) * 2u + 2u * hh;  // + 4 per unit
+  const uint32_t xoff =
+      (uint32_t)((zz * gridDim.y + blockIdx.y) * units) * 8192u + 16u * lane;  // + 8192 per unit
 
   Unit ub[2];
   auto issue = [&](int slot, int ku) {
-    const int kq = ku * 2 + hh;  // 64-k quarter = scale group
-    ub[slot].w[0] = wp[2 * kq];
-    ub[slot].w[1] = wp[2 * kq + 1];
-    ub[slot].sc = sp[kq];
-    ub[slot].bi = bp[kq];
+    const uint32_t wo = woff + 64u * ku, so = soff + 4u * ku, xo = xoff + 8192u * ku;
+    ub[slot].w[0] = *reinterpret_cast<const uint4*>(wbase + wo);
+    ub[slot].w[1] = *reinterpret_cast<const uint4*>(wbase + wo + 16u);
+    ub[slot].sc = *reinterpret_cast<const uint16_t*>(sbase + so);
+    ub[slot].bi = *reinterpret_cast<const uint16_t*>(bbase + so);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) ub[slot].x[st] = xq[(int64_t)ku * 512 + st * 64];
+    for (int st = 0; st < 8; ++st)
+      ub[slot].x[st] = *reinterpret_cast<const uint4*>(xbase + xo + 1024u * st);
   };
 
   // Loads are issued unconditionally (units past the end re-read the last one)
@@ -500,8 +506,12 @@ hipError_t launch_q4(const GemmArgs& a, int U, int nw, int S, hipStream_t s) {
 }  // namespace
 
 bool gemm_mfma_ok(const GemmArgs& a) {
+  // 32-bit byte offsets inside the kernel: weights and packed activations under 2 GiB
+  const int64_t wbytes = (int64_t)a.w.rows * a.w.cols / 2;
+  const int64_t xbytes = (int64_t)packed_bytes(a.Z, a.B, a.K);
   return a.w.dtype == MLA_Q4G64 && a.K > 0 && (a.K % 128) == 0 && (a.w.cols % 64) == 0 &&
-         a.K <= a.w.cols && (a.K / 128) <= kQ4MaxWaves * kMaxU;
+         a.K <= a.w.cols && (a.K / 128) <= kQ4MaxWaves * kMaxU && wbytes < (1ll << 31) &&
+         xbytes < (1ll << 31);
 }
 
 int gemm_max_splits(int64_t K) {

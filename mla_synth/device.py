@@ -99,3 +99,72 @@ def run_step(case: Case, ns, split_rows: int = 0, ws=None, stream=None) -> None:
                     ns.v_combine, ns.lse, split_rows, ws, stream)
     if ns.kv_b is not None:
         mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws, stream)
+
+
+class GraphStep:
+    """One decode step as the library calls it, replayable as one HIP graph:
+
+      pre   cache_append on the calling stream and, at the same time, absorb_q
+            on a side stream (independent: both only read x; each has its own
+            workspace) -- or both on the calling stream (two_streams=False)
+      attn  decode_attn
+      post  out_proj
+
+    ``run(eager=True)`` launches the calls; ``capture()`` records the whole
+    step into one graph and ``run()`` replays it on the current stream.
+    Library calls only; the graph allocates nothing.
+    """
+
+    def __init__(self, case: Case, ns, split_rows: int = 0, two_streams: bool = True):
+        self.case, self.ns, self.split_rows = case, ns, split_rows
+        self.two_streams = two_streams
+        self.ws_a = workspace(ns, split_rows)
+        self.ws_b = workspace(ns, split_rows)
+        self.side = torch.cuda.Stream()
+        self.q_abs = ns.q_abs_given if ns.q_abs_given is not None else ns.q_abs
+        self.graph = None
+
+    def pre(self):
+        ns, case = self.ns, self.case
+        cur = torch.cuda.current_stream()
+        side = self.two_streams and ns.q_abs_given is None
+        if ns.q_abs_given is None:
+            if side:
+                self.side.wait_stream(cur)
+            with torch.cuda.stream(self.side if side else cur):
+                q_in = ns.q if ns.q is not None else ns.x
+                mla.absorb_q(ns.dims, q_in, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions,
+                             ns.q_abs, ns.q_a, ns.q_a_norm, ns.q_b, self.ws_b)
+        if case.appended:
+            mla.cache_append(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq, ns.rope_mscale,
+                             ns.positions, ns.pool, ns.table, ns.status, self.ws_a)
+        if side:
+            cur.wait_stream(self.side)
+
+    def attn(self):
+        ns = self.ns
+        mla.decode_attn(ns.dims, self.q_abs, ns.pool, ns.table, ns.lens, ns.max_len,
+                        ns.softmax_scale, ns.v_combine, ns.lse, self.split_rows, self.ws_a)
+
+    def post(self):
+        ns = self.ns
+        if ns.kv_b is not None:
+            mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, self.ws_a)
+
+    def capture(self):
+        """Record the whole step (run it eagerly at least once before)."""
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.pre()
+            self.attn()
+            self.post()
+        torch.cuda.synchronize()
+
+    def run(self, eager=False):
+        if eager:
+            self.pre()
+            self.attn()
+            self.post()
+        else:
+            self.graph.replay()

@@ -80,8 +80,8 @@ def test_attn_validation_before_launch(lib):
 def test_plan_and_workspace(lib):
     r, s = mla.attn_plan(DS, 4, 131072, 2048)
     assert (r, s) == (2048, 64)
-    r, s = mla.attn_plan(DS, 1, 100, 0)
-    assert s == 1 and r >= 100
+    r, s = mla.attn_plan(DS, 1, 100, 0)   # automatic: splits of >= 256 rows covering the context
+    assert r % 64 == 0 and r >= 256 and r * s >= 100 and r * (s - 1) < 100
     need = mla.workspace_bytes(DS, 4, 131072, 2048)
     # bf16 cache: fp16 split partials, plus an lse and an exponent per (seq, split, head)
     assert need >= 4 * 64 * 128 * 512 * 2 + 2 * (4 * 64 * 128 * 4)
