@@ -7,7 +7,8 @@ attention over the paged latent cache, the W_UV expansion and o_proj.  The
 append and the absorb are independent and run on two streams, and the whole
 step is replayed as one HIP graph (``--eager``: every call launched on one
 stream).  The attention call is then timed alone with HIP events around
-back-to-back launches on the same inputs.  The
+back-to-back calls on the same inputs, launched the same way (a replayed graph
+of 20 calls; ``--eager``: one by one).  The
 workload is the full per-layer configuration: batch 32, 16384 cached rows per
 sequence (append at 16383), DeepSeek-V3 shapes (128 heads, latent 512, rope
 64), hidden 7168, q_lora 1536, 4-bit affine (group 64) projections, bf16
@@ -208,17 +209,28 @@ def main():
     ms_step = wall * 1e3 / args.steps
     assert int(ns.status.cpu()[0]) == 0
 
-    # The attention call on its stream: back-to-back launches of the same call
-    # on the step's inputs between two HIP events (events cannot time a node
-    # inside a replayed graph).
+    # The attention call on its stream, launched the way the step launches it:
+    # a graph of back-to-back calls on the step's inputs, replayed between two
+    # HIP events (events cannot be read from nodes inside a replayed graph).
+    # --eager: the calls launched one by one between the events.
     stream = torch.cuda.current_stream()
-    n_attn = max(args.steps, 20)
+    per_graph, reps = 20, max(args.steps // 20, 5)
+    n_attn = per_graph * reps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    step.attn()
+    if args.eager:
+        attn_run = lambda: [step.attn() for _ in range(per_graph)]
+    else:
+        g_attn = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g_attn):
+            for _ in range(per_graph):
+                step.attn()
+        attn_run = g_attn.replay
+    attn_run()
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(n_attn):
-        step.attn()
+    for _ in range(reps):
+        attn_run()
     e1.record(stream)
     torch.cuda.synchronize()
     attn_ms = e0.elapsed_time(e1) / n_attn
@@ -258,7 +270,9 @@ def main():
             "traffic": stored_traffic(),
             "kernel": "mla_decode_attn (attn_mfma_kernel + attn_combine_kernel)",
             "ms_per_launch": round(attn_ms, 4),
-            "timing": f"{n_attn} back-to-back decode_attn calls between two HIP events",
+            "timing": f"{n_attn} back-to-back decode_attn calls ("
+                      + ("eager" if args.eager else f"graphs of {per_graph}, replayed")
+                      + ") between two HIP events",
             "alg_bytes": byts,
             "mfma_tflops": round(flops / t_attn / 1e12, 1),
             "mfma_frac": round(flops / t_attn / 1e12 / BF16_PEAK_TFLOPS, 3),
