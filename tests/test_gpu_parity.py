@@ -6,6 +6,7 @@ sides.  Tolerances (stated by the target, applied elementwise):
   * bf16 caches: |gpu - ref| <= 2e-2 + 1e-2 |ref|
   * integer work (slots, untouched pool rows, paged == contiguous): bit-exact
 """
+import copy
 import math
 
 import numpy as np
@@ -81,6 +82,56 @@ def test_attn_more_splits_than_one_weight_chunk():
     case = S.make_case(4, lens=[4500, 130], paged=True, seed=17)
     ns = D.stage(case)
     vc, lse = attn_only(case, ns, 64)
+    rvc, rlse = oracle_attn(case)
+    close_bf16(vc, rvc, "v_combine")
+    close_bf16(lse, rlse, "lse")
+
+
+def repage(case, block, seed):
+    """The same logical rows in a pool of ``block``-row blocks, randomly permuted."""
+    import dataclasses
+    d = case.dims
+    rng = np.random.default_rng(seed)
+    rows = [O.gather_rows(case.pool, case.table, b, int(case.lens[b]), d.block_size)
+            for b in range(case.batch)]
+    nb = [(len(r) + block - 1) // block for r in rows]
+    order = rng.permutation(sum(nb)).astype(np.int32)
+    pool = np.full((sum(nb), block, d.width), S.BF16_NAN, dtype=np.uint16)
+    table = np.full((case.batch, max(nb)), -1, dtype=np.int32)
+    k = 0
+    for b, r in enumerate(rows):
+        ids = order[k:k + nb[b]]
+        k += nb[b]
+        table[b, :nb[b]] = ids
+        flat = np.full((nb[b] * block, d.width), S.BF16_NAN, dtype=np.uint16)
+        flat[:len(r)] = r
+        pool[ids] = flat.reshape(nb[b], block, d.width)
+    out = copy.copy(case)
+    out.dims = dataclasses.replace(d, block_size=block)
+    out.pool, out.table = pool, table
+    return out
+
+
+@pytest.mark.parametrize("block", [32, 128])
+def test_attn_block_sizes(block):
+    # tiles are 32 consecutive logical rows whatever the block size, so the
+    # result must not change by a single bit when the same rows are re-paged
+    case = S.make_case(4, lens=[700, 33, 129, 64], paged=True, seed=18)
+    ns = D.stage(case)
+    a64, l64 = attn_only(case, ns, 128)
+    other = repage(case, block, seed=19)
+    ns2 = D.stage(other)
+    a, l = attn_only(other, ns2, 128)
+    assert np.array_equal(a, a64) and np.array_equal(l, l64), f"block {block} != block 64"
+    rvc, rlse = oracle_attn(other)
+    close_bf16(a, rvc, f"v_combine block={block}")
+
+
+def test_attn_longest_single_split():
+    # 131072 rows in one split: the split's tile table (4096 entries) is full
+    case = S.make_case(4, batch=1, lens=[131072], seed=20)
+    ns = D.stage(case)
+    vc, lse = attn_only(case, ns, 131072)
     rvc, rlse = oracle_attn(case)
     close_bf16(vc, rvc, "v_combine")
     close_bf16(lse, rlse, "lse")
