@@ -295,15 +295,91 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* part, in
     put(i, sum_splits(part + b * stride + i, S, split_stride));
 }
 
-// (x, y) -> mscale * (x cos a - y sin a, x sin a + y cos a), a = pos * inv_freq,
-// angle and rotation in fp64 (exact enough for positions in the millions).
+// v[0..7] = sum over S <= kMaxKSplits of the 16-byte aligned 8-vectors
+// p[s * stride .. +7]; the loads of eight splits are issued together (indices
+// clamped to valid splits, the extra ones masked).
+__device__ __forceinline__ void sum_splits8(const float* p, int S, int64_t stride, float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 lo[8], hi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sp = s0 + j < S ? s0 + j : S - 1;
+      lo[j] = reinterpret_cast<const float4*>(p + sp * stride)[0];
+      hi[j] = reinterpret_cast<const float4*>(p + sp * stride)[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float m = s0 + j < S ? 1.f : 0.f;
+      v[0] = fmaf(m, lo[j].x, v[0]); v[1] = fmaf(m, lo[j].y, v[1]);
+      v[2] = fmaf(m, lo[j].z, v[2]); v[3] = fmaf(m, lo[j].w, v[3]);
+      v[4] = fmaf(m, hi[j].x, v[4]); v[5] = fmaf(m, hi[j].y, v[5]);
+      v[6] = fmaf(m, hi[j].z, v[6]); v[7] = fmaf(m, hi[j].w, v[7]);
+    }
+  }
+}
+
+__device__ __forceinline__ void gamma8(const WeightView& g, int k0, float gm[8]) {
+  if (g.dtype == MLA_F32) {
+    const float4 a = reinterpret_cast<const float4*>(static_cast<const float*>(g.data) + k0)[0];
+    const float4 b = reinterpret_cast<const float4*>(static_cast<const float*>(g.data) + k0)[1];
+    gm[0] = a.x; gm[1] = a.y; gm[2] = a.z; gm[3] = a.w;
+    gm[4] = b.x; gm[5] = b.y; gm[6] = b.z; gm[7] = b.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.data) + k0);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gm[2 * i] = __uint_as_float(u[i] << 16);
+      gm[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+}
+
+// RMSNorm of the summed split partials of one token per block, straight into
+// the packed fp16 layout: thread t owns k = 8t .. 8t + 7, one 16-byte packed
+// chunk.  Block = n/8 threads rounded up to whole waves; n % 8 == 0.
+__global__ void __launch_bounds__(1024) rmsnorm_pack_kernel(const float* part, int32_t S,
+                                                            int64_t split_stride, int32_t B,
+                                                            int32_t n, int64_t stride,
+                                                            WeightView gamma, float eps,
+                                                            _Float16* yp) {
+  __shared__ float red[16];
+  const int64_t b = blockIdx.x;
+  const int k0 = 8 * threadIdx.x;
+  const bool on = k0 < n;
+  float v[8];
+  if (on) sum_splits8(part + b * stride + k0, S, split_stride, v);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = on ? fmaf(v[i], v[i], ss) : ss;
+  const float tot = block_sum(ss, red);
+  if (!on) return;
+  const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+  float gm[8];
+  gamma8(gamma, k0, gm);
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = v[i] * inv * gm[i];
+  const f16x8_t h = {(_Float16)o[0], (_Float16)o[4], (_Float16)o[1], (_Float16)o[5],
+                     (_Float16)o[2], (_Float16)o[6], (_Float16)o[3], (_Float16)o[7]};
+  *reinterpret_cast<uint4*>(yp + packed_index(0, b, k0, B, n)) = __builtin_bit_cast(uint4, h);
+}
+
+// (x, y) -> mscale * (x cos a - y sin a, x sin a + y cos a), a = pos * inv_freq.
+// The angle is formed and reduced to [-pi, pi] in fp64 (pos * inv_freq in
+// fp32 would lose up to 1e-3 rad at 16k), then sin/cos and the rotation run in
+// fp32 (accurate library sincosf, about 1e-7 relative).
 __device__ __forceinline__ void rope_pair(float x, float y, int pos, float inv_freq, float mscale,
                                           float* ox, float* oy) {
+  const double two_pi = 6.283185307179586476925286766559;
   const double ang = (double)pos * (double)inv_freq;
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  *ox = (float)((double)mscale * ((double)x * cs - (double)y * sn));
-  *oy = (float)((double)mscale * ((double)x * sn + (double)y * cs));
+  const float r = (float)(ang - two_pi * rint(ang / two_pi));
+  float sn, cs;
+  sincosf(r, &sn, &cs);
+  *ox = mscale * (x * cs - y * sn);
+  *oy = mscale * (x * sn + y * cs);
 }
 
 template <typename T>
@@ -338,6 +414,59 @@ __global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
     rope_pair(kv(a.C + 2 * i), kv(a.C + 2 * i + 1), pos, a.inv_freq[i], a.rope_mscale, &ox, &oy);
     Elem<T>::store(dst, a.C + 2 * i, ox);
     Elem<T>::store(dst, a.C + 2 * i + 1, oy);
+  }
+}
+
+// One appended row per block, 8 values per thread: threads t < C/8 own latent
+// values 8t .. 8t + 7 (RMSNorm), the next R/8 own k_pe values (4 RoPE pairs
+// each); every thread stores 8 cache elements at once.  C % 8 == R % 8 == 0.
+template <typename T>
+__global__ void __launch_bounds__(256) append_rows_vec_kernel(AppendArgs a) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int W = a.C + a.R;
+  const int pos = a.positions[b];
+  if (pos < 0 || (int64_t)pos >= (int64_t)a.max_blocks * a.block) {
+    if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_POS_RANGE);
+    return;
+  }
+  const int blk = a.table[(size_t)b * a.max_blocks + pos / a.block];
+  if (blk < 0 || blk >= a.num_blocks) {
+    if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_BAD_BLOCK);
+    return;
+  }
+  const int k0 = 8 * threadIdx.x;
+  const bool latent = k0 < a.C, on = k0 < W;
+  float v[8];
+  if (on) sum_splits8(a.kv_pre + (size_t)b * W + k0, a.kv_splits, a.kv_split_stride, v);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = latent ? fmaf(v[i], v[i], ss) : ss;
+  const float tot = block_sum(ss, red);
+  if (!on) return;
+  T* dst = static_cast<T*>(a.pool) + ((size_t)blk * a.block + pos % a.block) * W + k0;
+  float o[8];
+  if (latent) {
+    const float inv = 1.0f / sqrtf(tot / (float)a.C + a.eps);
+    float gm[8];
+    gamma8(a.gamma, k0, gm);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = v[i] * inv * gm[i];
+  } else {
+    const int i0 = (k0 - a.C) / 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rope_pair(v[2 * i], v[2 * i + 1], pos, a.inv_freq[i0 + i], a.rope_mscale, &o[2 * i], &o[2 * i + 1]);
+  }
+  if constexpr (std::is_same<T, float>::value) {
+    reinterpret_cast<float4*>(dst)[0] = float4{o[0], o[1], o[2], o[3]};
+    reinterpret_cast<float4*>(dst)[1] = float4{o[4], o[5], o[6], o[7]};
+  } else {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = (uint32_t)f32_to_bf16(o[2 * i]) | ((uint32_t)f32_to_bf16(o[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(dst) = uint4{u[0], u[1], u[2], u[3]};
   }
 }
 
@@ -567,6 +696,14 @@ hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_strid
                                _Float16* yp, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (S < 1 || S > kMaxKSplits || (yp && n % 128 != 0)) return hipErrorInvalidValue;
+  const bool aligned = (reinterpret_cast<uintptr_t>(part) & 15) == 0 && stride % 4 == 0 &&
+                       split_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(gamma.data) & 15) == 0;
+  if (yp && aligned && n <= 8192) {
+    const int threads = ((n / 8) + 63) / 64 * 64;
+    hipLaunchKernelGGL(rmsnorm_pack_kernel, dim3(B), dim3(threads), 0, s, part, S, split_stride,
+                       B, n, stride, gamma, eps, yp);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, part, S, split_stride, B, n,
                      stride, gamma, eps, y, yp);
   return hipGetLastError();
@@ -574,6 +711,20 @@ hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_strid
 
 hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
+  const int W = a.C + a.R;
+  const size_t elem = a.cache_dtype == MLA_F32 ? 4 : 2;
+  const bool vec = a.C % 8 == 0 && a.R % 8 == 0 && W <= 2048 &&
+                   (reinterpret_cast<uintptr_t>(a.kv_pre) & 15) == 0 &&
+                   a.kv_split_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(a.pool) & 15) == 0 &&
+                   ((size_t)W * elem) % 16 == 0 && (reinterpret_cast<uintptr_t>(a.gamma.data) & 15) == 0;
+  if (vec) {
+    const int threads = ((W / 8) + 63) / 64 * 64;
+    if (a.cache_dtype == MLA_F32)
+      hipLaunchKernelGGL(append_rows_vec_kernel<float>, dim3(a.B), dim3(threads), 0, s, a);
+    else
+      hipLaunchKernelGGL(append_rows_vec_kernel<uint16_t>, dim3(a.B), dim3(threads), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.cache_dtype == MLA_F32)
     hipLaunchKernelGGL(append_rows_kernel<float>, dim3(a.B), dim3(256), 0, s, a);
   else
