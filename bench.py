@@ -16,8 +16,13 @@ cache.  Inputs are synthetic (seeded) and resident in HBM before timing.
 
 Prints one JSON line.  ``roofline`` describes the attention call (its split
 kernel plus the split-K combine kernel), timed with HIP events on the stream
-it is launched on; ``cpu_baseline`` is the fp64 oracle timed on a bounded
-sample of the same workload on the host cores.
+it is launched on, hot (back-to-back calls) and cold (``ms_per_launch_cold``:
+a 1 GiB write evicts the last-level cache before each call); ``cpu_baseline``
+is the fp64 oracle timed on a bounded sample of the same workload on the host
+cores.  ``attn_only`` repeats the attention measurement on the other
+full-size workloads (one 4096-row sequence; 64 ragged paged sequences of
+1024-8192 rows; 4 sequences of 131072 rows), each with the oracle's attention
+timed on the same inputs.
 """
 from __future__ import annotations
 
@@ -25,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -67,8 +73,38 @@ def stored_traffic():
     return c.get("hbm_bytes_per_call")
 
 
-def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50):
-    """Attention call alone on a full-size configuration (q_abs given or absorbed once)."""
+def cold_call_ms(torch, call, stream, runs=20, scratch_bytes=1 << 30):
+    """Median time of single calls, each after a 1 GiB write (not timed) that
+    evicts the 256 MB last-level cache, so that every input comes from HBM."""
+    scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device="cuda")
+    ev = []
+    for r in range(runs):
+        scratch.fill_(r & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    del scratch
+    return statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
+
+
+def oracle_attn_seconds(case):
+    """The oracle's latent attention (fp64 numpy) on the same inputs, one pass;
+    its query is the oracle's own absorbed query, computed outside the timing."""
+    from oracle import mla_oracle as O
+    q64 = O.attention_query(case)
+    sc = float(O.tables_for(case)[2])
+    t0 = time.perf_counter()
+    O.attention_latent(case.dims, q64, case.pool, case.table, case.lens, sc)
+    return time.perf_counter() - t0
+
+
+def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50, oracle=True):
+    """Attention call alone on a full-size configuration (q_abs given or absorbed
+    once): hot (back-to-back calls) and cold (cache evicted before each call),
+    and the oracle's attention on the same inputs."""
     case = S.make_case(cfg)
     ns = D.stage(case)
     ws = D.workspace(ns)
@@ -93,17 +129,36 @@ def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
+    ms_cold = cold_call_ms(torch, call, stream)
     rows = int(case.lens.sum())
     byts, flops = attn_alg(case.batch, rows)
     t = ms * 1e-3
-    return {
-        "batch": case.batch, "rows": rows, "ms": round(ms, 4),
+    out = {
+        "batch": case.batch, "rows": rows, "ms": round(ms, 4), "ms_cold": round(ms_cold, 4),
         "gbps": round(byts / t / 1e9, 1), "tflops": round(flops / t / 1e12, 1),
         "f_hbm": round(byts / t / 1e9 / HBM_PEAK_GBS, 3),
         "f_mfma": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
         "f_roof": round(max(byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)) / t, 3),
         "tokens_per_s": round(case.batch / t, 1),
+        "f_roof_cold": round(max(byts / (HBM_PEAK_GBS * 1e9),
+                                 flops / (BF16_PEAK_TFLOPS * 1e12)) / (ms_cold * 1e-3), 3),
     }
+    del ns, ws
+    if oracle:
+        sec = oracle_attn_seconds(case)
+        out["oracle"] = {"seconds": round(sec, 3), "rows_per_s": round(rows / sec, 1),
+                         "gbps_equiv": round(byts / sec / 1e9, 3),
+                         "tokens_per_s": round(case.batch / sec, 3),
+                         "gpu_speedup": round(sec / t, 1), "cores": oracle_threads()}
+    return out
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] + [1]))
+    except Exception:
+        return os.cpu_count() or 1
 
 
 def cpu_baseline(case, seqs, min_seconds=10.0, max_reps=8):
@@ -112,11 +167,7 @@ def cpu_baseline(case, seqs, min_seconds=10.0, max_reps=8):
     import numpy as np
     from oracle import mla_oracle as O
     sub = S_sub(case, seqs)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = oracle_threads()
     reps, total = 0, 0.0
     while reps < max_reps and (reps == 0 or total < min_seconds):
         t0 = time.perf_counter()
@@ -278,10 +329,12 @@ def main():
             "mfma_frac": round(flops / t_attn / 1e12 / BF16_PEAK_TFLOPS, 3),
         },
     }
+    # the same call on this workload with the last-level cache evicted before each call
+    line["roofline"]["ms_per_launch_cold"] = round(cold_call_ms(torch, step.attn, stream), 4)
     if not args.no_extra:
         extra = {}
-        for cfg in (2, 3, 4):
-            extra[f"cfg{cfg}"] = time_attn_only(cfg, torch, D, S, mla)
+        for cfg, name in ((2, "b1_L4096"), (3, "b64_L1024-8192_paged"), (4, "b4_L131072")):
+            extra[name] = time_attn_only(cfg, torch, D, S, mla, oracle=not args.no_cpu)
         line["attn_only"] = extra
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seqs)

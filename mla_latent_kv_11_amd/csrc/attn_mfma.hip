@@ -20,7 +20,10 @@
 // lane (one head per lane); the resident Q (144 VGPRs), scores and fragments
 // share the 256 VGPRs.  O is only ever touched by MFMAs inside the loop.
 //
-// Tiles stream HBM -> LDS with 16-byte direct-to-LDS loads, three buffers deep.
+// Tiles stream HBM -> LDS with 16-byte direct-to-LDS loads, three buffers deep;
+// a wave waits for its copies of tile i + 1 just before the barrier that
+// publishes tile i's P, so the next tile's first K fragments are read during
+// tile i's P*V.
 // The LDS tile is 32 rows x 72 sixteen-byte granules with an XOR swizzle of the
 // granule index inside each aligned group of 8, chosen so that both the
 // row-wise K reads (16 rows, one granule each) and the transpose V reads (4
@@ -29,10 +32,8 @@
 // Split-K (flash decoding): grid = (splits, batch). A split with a single
 // partition writes v_combine/lse directly; otherwise it writes the normalised
 // partial O (fp16 with a power-of-two exponent per head) and its lse, merged
-// by attn_combine_kernel.
+// by attn_combine_f16_kernel.
 #include <math.h>
-
-#include <type_traits>
 
 #include "mla_common.h"
 
@@ -218,12 +219,27 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 
   issue_tile(0);
   if (ntiles > 1) issue_tile(1);
+  // K fragment of k-block kb: base qa[kb & 3] of the tile, + (kb >> 2) * 128.
+  // The bases are made opaque so that the constant offsets fold into the
+  // reads instead of becoming 36 hoisted addresses.
+  auto kbases = [&](uint32_t t, uint32_t* qa) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      qa[m] = t + (qk0 ^ (uint32_t)(m << 5));
+      asm volatile("" : "+v"(qa[m]));
+    }
+  };
+  auto kaddr = [&](const uint32_t* qa, int kb) {
+    return (const MLA_LDS bf16x8_t*)(uintptr_t)(qa[kb & 3] + (kb >> 2) * 128);
+  };
+  bf16x8_t kf[5];  // K fragments of the next five k-blocks
   // Iteration ntiles only collects the last tile's restart vote.
   for (int i = 0; i <= ntiles; ++i) {
-    if (i + 1 < ntiles) {
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    } else {
+    // Tile i > 0 was waited for before the previous tile's P barrier.
+    if (i + 1 >= ntiles) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if (i == 0) {
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 (tile 1's copies are newer)
     }
     if (lane == 0) votes[(i & 1) * 4 + wave] = __ballot(pending) != 0;
     __syncthreads();
@@ -265,30 +281,26 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     }
 
     const uint32_t tile = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes);
-    const MLA_LDS char* tilep = tiles + (i % kBufs) * kTileBytes;
 
     // ---- scores S^T (rows x heads): two accumulators (even / odd k-block),
     // K fragments read five k-blocks ahead; the next tile's copies are issued
     // between the MFMAs ----
     f32x16_t s;
     {
-      uint32_t qa[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) qa[m] = tile + (qk0 ^ (uint32_t)(m << 5));
-      auto kaddr = [&](int kb) {
-        return (const MLA_LDS bf16x8_t*)(uintptr_t)(qa[kb & 3] + (kb >> 2) * 128);
-      };
       f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-      bf16x8_t kf[5];
+      uint32_t qa[4];
+      kbases(tile, qa);
+      if (i == 0) {  // otherwise read during the previous tile's P*V
 #pragma unroll
-      for (int kb = 0; kb < 5; ++kb) kf[kb] = *kaddr(kb);
+        for (int kb = 0; kb < 5; ++kb) kf[kb] = *kaddr(qa, kb);
+      }
 #pragma unroll
       for (int kb = 0; kb < kW / 16; ++kb) {
         if (kb & 1)
           s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 5], qf[kb], s1, 0, 0, 0);
         else
           s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 5], qf[kb], s0, 0, 0, 0);
-        if (kb + 5 < kW / 16) kf[kb % 5] = *kaddr(kb + 5);
+        if (kb + 5 < kW / 16) kf[kb % 5] = *kaddr(qa, kb + 5);
         if ((kb & 3) == 3) issue_load(i + 2, kb >> 2, noff[kb >> 2], nsrc);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -381,35 +393,72 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       *(MLA_LDS bf16x8_t*)prow = pb[0];
       *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
     }
-    __syncthreads();  // every head's P is visible
+    // this wave's copies of tile i + 1 (all but the newest kLoads) have landed
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    __syncthreads();  // every head's P is visible, and so is tile i + 1
 
     // ---- O^T += V^T P^T for this wave's 128 latent columns and all 128 heads:
     // V is read from LDS once per workgroup ----
     {
       bf16x8_t pf[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {  // the first half's fragments first
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           pf[kb][x] = *(const MLA_LDS bf16x8_t*)(p_lds + p_row + x * (32 * kPRow) + kb * 32);
-#pragma unroll
-      for (int cbl = 0; cbl < 4; ++cbl)
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          // first k-block; C = 0 right after a restart
-          asm volatile(
-              "s_cmp_eq_u32 %3, 0\n\t"
-              "s_cbranch_scc1 1f\n\t"
-              "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\t"
-              "s_branch 2f\n"
-              "1:\n\t"
-              "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n"
-              "2:"
-              : "+a"(o[cbl * 4 + hb])
-              : "v"(vf[0][cbl]), "v"(pf[0][hb]), "s"(zero_c)
-              : "scc");
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // first k-block, 16 MFMAs in one block; C = 0 right after a restart
+      // (one uniform branch per tile)
+      asm volatile(
+          "s_cmp_eq_u32 %24, 0\n\t"
+          "s_cbranch_scc1 1f\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %16, %20, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %1, %16, %21, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %2, %16, %22, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %3, %16, %23, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %4, %17, %20, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %5, %17, %21, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %6, %17, %22, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %7, %17, %23, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %8, %18, %20, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %9, %18, %21, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %10, %18, %22, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %11, %18, %23, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %12, %19, %20, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %13, %19, %21, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %14, %19, %22, 0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %15, %19, %23, 0\n\t"
+          "s_branch 2f\n"
+          "1:\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %16, %20, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %1, %16, %21, %1\n\t"
+          "v_mfma_f32_32x32x16_bf16 %2, %16, %22, %2\n\t"
+          "v_mfma_f32_32x32x16_bf16 %3, %16, %23, %3\n\t"
+          "v_mfma_f32_32x32x16_bf16 %4, %17, %20, %4\n\t"
+          "v_mfma_f32_32x32x16_bf16 %5, %17, %21, %5\n\t"
+          "v_mfma_f32_32x32x16_bf16 %6, %17, %22, %6\n\t"
+          "v_mfma_f32_32x32x16_bf16 %7, %17, %23, %7\n\t"
+          "v_mfma_f32_32x32x16_bf16 %8, %18, %20, %8\n\t"
+          "v_mfma_f32_32x32x16_bf16 %9, %18, %21, %9\n\t"
+          "v_mfma_f32_32x32x16_bf16 %10, %18, %22, %10\n\t"
+          "v_mfma_f32_32x32x16_bf16 %11, %18, %23, %11\n\t"
+          "v_mfma_f32_32x32x16_bf16 %12, %19, %20, %12\n\t"
+          "v_mfma_f32_32x32x16_bf16 %13, %19, %21, %13\n\t"
+          "v_mfma_f32_32x32x16_bf16 %14, %19, %22, %14\n\t"
+          "v_mfma_f32_32x32x16_bf16 %15, %19, %23, %15\n\t"
+          "2:"
+          : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+            "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+            "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
+          : "v"(vf[0][0]), "v"(vf[0][1]), "v"(vf[0][2]), "v"(vf[0][3]), "v"(pf[0][0]),
+            "v"(pf[0][1]), "v"(pf[0][2]), "v"(pf[0][3]), "s"(zero_c)
+          : "scc");
+      __builtin_amdgcn_sched_barrier(0);
+      // the first K fragments of tile i + 1 go out between the second half's
+      // MFMAs, where the first half's fragments are dead
+      uint32_t nqa[4];
+      kbases(tiles_lds + (uint32_t)(((i + 1) % kBufs) * kTileBytes), nqa);
 #pragma unroll
       for (int cbl = 0; cbl < 4; ++cbl)
 #pragma unroll
@@ -417,6 +466,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                        : "+a"(o[cbl * 4 + hb])
                        : "v"(vf[1][cbl]), "v"(pf[1][hb]));
+          const int n = cbl * 4 + hb;
+          if (n % 3 == 0 && n / 3 < 5) kf[n / 3] = *kaddr(nqa, n / 3);
           __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -504,11 +555,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 }
 
 // Merge the normalised partials of every split: lse = log sum_s exp(lse_s),
-// v = sum_s exp(lse_s - lse) O_s, with O_s = 2^e_s * (stored fp16 value) for
-// the MFMA kernel's partials.  One workgroup per (sequence, 2 heads), 128
-// threads per head, 4 consecutive latent columns per thread and step; the max
-// and the weight sum over splits are wavefront reductions.  C % 4 == 0.
-template <bool kF16>
+// v = sum_s exp(lse_s - lse) O_s.  This one takes the generic kernel's fp32
+// partials (any H and C): one workgroup per (sequence, 2 heads), 128 threads
+// per head, 4 consecutive latent columns per thread and step; the max and the
+// weight sum over splits are wavefront reductions.  C % 4 == 0.
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int b = blockIdx.y;
   const int h = blockIdx.x * 2 + (threadIdx.x >> 7);
@@ -537,21 +587,57 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
       const float ls = lse_s[(size_t)s * a.H];
       if (ls == -INFINITY) continue;
       const size_t off = (((size_t)b * S + s) * a.H + h) * a.C + c;
-      f32x4_t v;
-      float w = expf(ls - m);
-      if constexpr (kF16) {
-        typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-        const f16x4_t hv = *reinterpret_cast<const f16x4_t*>(a.part_oh + off);
-        v = f32x4_t{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
-        w = ldexpf(w, (int)a.part_exp[((size_t)b * S + s) * a.H + h]);
-      } else {
-        v = *reinterpret_cast<const f32x4_t*>(a.part_o + off);
-      }
-      acc += w * v;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + off);
+      acc += expf(ls - m) * v;
     }
     *reinterpret_cast<f32x4_t*>(dst + c) = acc * inv;
   }
   if (a.lse && (threadIdx.x & 127) == 0) a.lse[(size_t)b * a.H + h] = m + logf(wsum);
+}
+
+// The same merge for the MFMA kernel's partials (H = 128, C = 512), stored as
+// fp16 times 2^-e_s: O_s = 2^e_s * (stored value), and 2^e_s folds into the
+// split's weight.  One wave per (sequence, head), 8 consecutive latent columns
+// per lane, so every split's partial row is one 1 KB coalesced read per wave;
+// four heads per workgroup.
+__global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
+  const int b = blockIdx.y;
+  const int h = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int S = a.num_splits;
+  const float* lse_s = a.part_lse + (size_t)b * S * kH + h;  // stride kH over s
+  const float* exp_s = a.part_exp + (size_t)b * S * kH + h;
+
+  float m = -INFINITY;
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, lse_s[(size_t)s * kH]);
+  m = wave_max(m);
+  float* dst = a.v_combine + ((size_t)b * kH + h) * kC + lane * 8;
+  if (m == -INFINITY) {  // empty sequence
+    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = -INFINITY;
+    return;
+  }
+  float wsum = 0.f;
+  for (int s = lane; s < S; s += 64) wsum += expf(lse_s[(size_t)s * kH] - m);
+  wsum = wave_sum(wsum);
+  const float inv = 1.0f / wsum;
+
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  const _Float16* src = a.part_oh + ((size_t)b * S * kH + h) * kC + lane * 8;
+  const size_t sstride = (size_t)kH * kC;
+  f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float ls = lse_s[(size_t)s * kH];
+    if (ls == -INFINITY) continue;  // an empty split leaves its partial unwritten
+    const float w = ldexpf(expf(ls - m), (int)exp_s[(size_t)s * kH]);
+    const f16x8_t v = *reinterpret_cast<const f16x8_t*>(src + (size_t)s * sstride);
+    lo += w * f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    hi += w * f32x4_t{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+  }
+  *reinterpret_cast<f32x4_t*>(dst) = lo * inv;
+  *reinterpret_cast<f32x4_t*>(dst + 4) = hi * inv;
+  if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = m + logf(wsum);
 }
 
 }  // namespace
@@ -571,9 +657,9 @@ hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
   if (a.part_oh)
-    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_f16_kernel, dim3(kH / 4, a.B), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<false>, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

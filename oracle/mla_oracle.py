@@ -392,6 +392,31 @@ def tables_for(case):
     return inv32, float(np.float32(rm)), float(np.float32(sc))
 
 
+def attention_query(case, res=None, model_q_abs_storage=True) -> np.ndarray:
+    """The absorbed query the latent attention of ``decode_step`` consumes:
+    q_abs as given, or q (given, else the q chain) absorbed through W_UK with
+    its rope part rotated.  Intermediates go into ``res`` when one is passed."""
+    d = case.dims
+    res = {} if res is None else res
+    if case.q_abs is not None:
+        res["q_abs_stored"] = case.q_abs
+        return widen(case.q_abs, d.cache_dtype)
+    inv, rm, _ = tables_for(case)
+    kvb_dt = weight_dtype(case.kv_b)
+    kv_b64 = weight_f64(case.kv_b, kvb_dt, d.num_heads * (d.qk_nope + d.v_head), d.kv_lora)
+    res["kv_b64"] = kv_b64
+    if case.q is not None:
+        q = widen(case.q, F32)
+    else:
+        q = q_chain(d, case.x, case.q_a, case.q_a_norm, case.q_b)
+    res["q"] = q
+    q_abs64 = absorb_q(d, q, kv_b64, inv, rm, case.positions)
+    res["q_abs64"] = q_abs64
+    stored = round_to(q_abs64, d.cache_dtype)
+    res["q_abs_stored"] = stored
+    return widen(stored, d.cache_dtype) if model_q_abs_storage else q_abs64
+
+
 def decode_step(case, *, model_q_abs_storage=True):
     """Run append -> absorb (q chain) -> latent attention -> out_proj on a case.
 
@@ -410,24 +435,7 @@ def decode_step(case, *, model_q_abs_storage=True):
                                   case.positions, case.pool, case.table)
         res["appended_rows"] = rows
     res["pool"] = pool
-    if case.q_abs is not None:
-        q_abs64 = widen(case.q_abs, d.cache_dtype)
-        res["q_abs_stored"] = case.q_abs
-    else:
-        kvb_dt = weight_dtype(case.kv_b)
-        kv_b64 = weight_f64(case.kv_b, kvb_dt, d.num_heads * (d.qk_nope + d.v_head), d.kv_lora)
-        res["kv_b64"] = kv_b64
-        if case.q is not None:
-            q = widen(case.q, F32)
-        else:
-            q = q_chain(d, case.x, case.q_a, case.q_a_norm, case.q_b)
-        res["q"] = q
-        q_abs64 = absorb_q(d, q, kv_b64, inv, rm, case.positions)
-        res["q_abs64"] = q_abs64
-        stored = round_to(q_abs64, d.cache_dtype)
-        res["q_abs_stored"] = stored
-        if model_q_abs_storage:
-            q_abs64 = widen(stored, d.cache_dtype)
+    q_abs64 = attention_query(case, res, model_q_abs_storage)
     vc, lse, ps = attention_latent(d, q_abs64, pool, case.table, case.lens, sc)
     res.update(v_combine=vc, lse=lse, p=ps)
     if case.kv_b is not None:
