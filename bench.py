@@ -319,7 +319,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 3),
             "traffic": stored_traffic(),
-            "kernel": "mla_decode_attn (attn_mfma_kernel + attn_combine_kernel)",
+            "kernel": "mla_decode_attn (attn_mfma_kernel + attn_combine_f16_kernel)",
             "ms_per_launch": round(attn_ms, 4),
             "timing": f"{n_attn} back-to-back decode_attn calls ("
                       + ("eager" if args.eager else f"graphs of {per_graph}, replayed")

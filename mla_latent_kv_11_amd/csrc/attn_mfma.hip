@@ -35,6 +35,8 @@
 // by attn_combine_f16_kernel.
 #include <math.h>
 
+#include <mutex>
+
 #include "mla_common.h"
 
 // The tile copies set M0 inside inline asm.  No compiler-generated code in this
@@ -644,12 +646,22 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
 
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
   const size_t smem = kSmemBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  // The dynamic LDS limit is raised once per device (the launch may come from
+  // any host thread and any current device).
+  static std::mutex mu;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (!attr_set[dev]) {
+      e = hipFuncSetAttribute((const void*)attn_mfma_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e != hipSuccess) return e;
+      attr_set[dev] = true;
+    }
   }
   hipLaunchKernelGGL(attn_mfma_kernel, dim3(a.num_splits, a.B), dim3(kThreads), smem, s, a);
   return hipGetLastError();
