@@ -6,9 +6,9 @@ latent RMSNorm + YaRN RoPE + paged append, the q chain + absorb, decode
 attention over the paged latent cache, the W_UV expansion and o_proj.  The
 append and the absorb are independent and run on two streams, and the whole
 step is replayed as one HIP graph (``--eager``: every call launched on one
-stream).  The attention call is then timed alone with HIP events around
-back-to-back calls on the same inputs, launched the same way (a replayed graph
-of 20 calls; ``--eager``: one by one).  The
+stream).  The attention call is then timed where the step runs it (HIP events
+around decode_attn inside eager steps, between append/absorb and out_proj), and
+also back to back (a replayed graph of 20 calls; ``--eager``: one by one).  The
 workload is the full per-layer configuration: batch 32, 16384 cached rows per
 sequence (append at 16383), DeepSeek-V3 shapes (128 heads, latent 512, rope
 64), hidden 7168, q_lora 1536, 4-bit affine (group 64) projections, bf16
@@ -260,11 +260,26 @@ def main():
     ms_step = wall * 1e3 / args.steps
     assert int(ns.status.cpu()[0]) == 0
 
-    # The attention call on its stream, launched the way the step launches it:
-    # a graph of back-to-back calls on the step's inputs, replayed between two
-    # HIP events (events cannot be read from nodes inside a replayed graph).
-    # --eager: the calls launched one by one between the events.
+    # The attention call timed where the step runs it: eager steps (the same
+    # kernels the graph replays), HIP events on its stream right before and
+    # after decode_attn, between the step's append/absorb and its out_proj.
     stream = torch.cuda.current_stream()
+    n_in = max(args.steps, 50)
+    in_step = []
+    for _ in range(n_in):
+        step.pre()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step.attn()
+        e1.record(stream)
+        step.post()
+        in_step.append((e0, e1))
+    torch.cuda.synchronize()
+    attn_ms = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in in_step)
+
+    # The same call back to back: a graph of 20 calls on the step's inputs,
+    # replayed between two HIP events (events cannot be read from nodes inside
+    # a replayed graph); --eager: the calls launched one by one.
     per_graph, reps = 20, max(args.steps // 20, 5)
     n_attn = per_graph * reps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -284,7 +299,7 @@ def main():
         attn_run()
     e1.record(stream)
     torch.cuda.synchronize()
-    attn_ms = e0.elapsed_time(e1) / n_attn
+    attn_b2b_ms = e0.elapsed_time(e1) / n_attn
 
     byts, flops = attn_alg(B, rows)
     t_attn = attn_ms * 1e-3
@@ -321,7 +336,10 @@ def main():
             "traffic": stored_traffic(),
             "kernel": "mla_decode_attn (attn_mfma_kernel + attn_combine_f16_kernel)",
             "ms_per_launch": round(attn_ms, 4),
-            "timing": f"{n_attn} back-to-back decode_attn calls ("
+            "timing": f"mean of {n_in} decode_attn calls inside eager steps, HIP events on "
+                      "their stream around each call",
+            "ms_per_launch_back_to_back": round(attn_b2b_ms, 4),
+            "timing_back_to_back": f"{n_attn} back-to-back decode_attn calls ("
                       + ("eager" if args.eager else f"graphs of {per_graph}, replayed")
                       + ") between two HIP events",
             "alg_bytes": byts,
