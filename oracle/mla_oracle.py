@@ -47,6 +47,11 @@ Readings of points the pages leave open (each also listed in the design doc):
     pages, a storage convention.
   * Paging: logical row t of sequence b lives at pool[table[b][t // block],
     t % block].
+  * Q8_0 kv_b ([ts/deepseek2] ``validate_q8_0_matrix`` and its unit test: the
+    row width must tile whole blocks, and a 64-wide row holds two, so a block
+    is 32 values): the pages name the format without its byte layout; it is
+    read as GGUF's Q8_0, each block a little-endian binary16 scale d followed
+    by 32 signed 8-bit q, element = d * q (34 bytes per block).
 """
 from __future__ import annotations
 
@@ -54,7 +59,8 @@ import math
 
 import numpy as np
 
-F32, BF16, Q4G64 = 0, 1, 2
+F32, BF16, Q4G64, Q8_0 = 0, 1, 2, 3
+Q8_0_BLOCK, Q8_0_BLOCK_BYTES = 32, 34
 
 
 # ----------------------------------------------------------------------------
@@ -115,10 +121,26 @@ def dequant_q4(packed, scales, biases, rows: int, cols: int, group: int = 64) ->
     return q.astype(np.float64) * np.repeat(s, group, axis=1) + np.repeat(b, group, axis=1)
 
 
+def dequant_q8_0(blocks, rows: int, cols: int) -> np.ndarray:
+    """Q8_0 weight (uint8 bytes, [rows][cols/32] blocks of 34) -> float64 [rows, cols].
+
+    Element k of a row is d * q[k % 32] of block k // 32, with d the block's
+    little-endian binary16 scale and q its signed bytes ([ts/deepseek2]
+    ``validate_q8_0_matrix``; the byte layout is GGUF's Q8_0).
+    """
+    raw = np.asarray(blocks, dtype=np.uint8).reshape(rows, cols // Q8_0_BLOCK, Q8_0_BLOCK_BYTES)
+    d = raw[:, :, :2].copy().view("<f2")[..., 0].astype(np.float64)
+    q = raw[:, :, 2:].view(np.int8).astype(np.float64)
+    return (d[:, :, None] * q).reshape(rows, cols)
+
+
 def weight_f64(w, dtype: int, rows: int, cols: int) -> np.ndarray:
-    """Any stored weight (fp32, bf16 bits, or an object with packed/scales/biases) -> float64."""
+    """Any stored weight (fp32, bf16 bits, Q8_0 bytes, or an object with
+    packed/scales/biases) -> float64."""
     if dtype == Q4G64:
         return dequant_q4(w.packed, w.scales, w.biases, rows, cols)
+    if dtype == Q8_0:
+        return dequant_q8_0(w, rows, cols)
     return widen(w, dtype).reshape(rows, cols)
 
 
@@ -378,7 +400,10 @@ def out_proj(dims, v_combine64, kv_b64, o_proj64=None) -> np.ndarray:
 def weight_dtype(w) -> int:
     if hasattr(w, "packed"):
         return Q4G64
-    return BF16 if np.asarray(w).dtype == np.uint16 else F32
+    dt = np.asarray(w).dtype
+    if dt == np.uint8:
+        return Q8_0
+    return BF16 if dt == np.uint16 else F32
 
 
 def tables_for(case):

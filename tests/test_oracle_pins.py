@@ -83,6 +83,55 @@ def test_q4_quantise_dequantise_error_bound():
     assert np.all(np.abs(w - vals) <= tol)
 
 
+def _q8_0_block(scale_half_bits: int, q) -> bytes:
+    """One Q8_0 block spelled out byte by byte: little-endian binary16 scale, 32 signed bytes."""
+    assert len(q) == 32
+    return struct.pack("<H", scale_half_bits) + struct.pack("<32b", *q)
+
+
+def test_q8_0_dequant_single_block_closed_form():
+    # d = 0.5 (binary16 0x3800); q spans the whole int8 range, so a byte read as
+    # unsigned, a swapped scale byte order or a dropped scale all fail.
+    q = [0, 1, -1, 2, -2, 127, -128, 64, -64, 3, -3, 100, -100, 5, -5, 7,
+         -7, 9, -9, 11, -11, 13, -13, 15, -15, 17, -17, 19, -19, 21, -21, 126]
+    raw = np.frombuffer(_q8_0_block(0x3800, q), dtype=np.uint8)
+    w = O.dequant_q8_0(raw, 1, 32)
+    assert w.shape == (1, 32)
+    assert w[0].tolist() == [0.5 * v for v in q]
+    assert O.weight_f64(raw, O.Q8_0, 1, 32).tolist() == w.tolist()
+    assert O.weight_dtype(raw) == O.Q8_0
+
+
+def test_q8_0_block_order_and_scales():
+    # 2 rows x 64 columns = 4 blocks, row-major, each with its own scale:
+    # 1.0 (0x3c00), -2.0 (0xc000), 2^-14 (0x0400, smallest normal) and the
+    # subnormal 2^-24 (0x0001); q = k + 1 - 16 * (block index) within a block.
+    scales = [(0x3C00, 1.0), (0xC000, -2.0), (0x0400, 2.0 ** -14), (0x0001, 2.0 ** -24)]
+    raw = b""
+    expect = np.zeros((2, 64))
+    for blk, (bits, d) in enumerate(scales):
+        q = [(k + 1 - 16 * blk) for k in range(32)]
+        raw += _q8_0_block(bits, q)
+        r, c0 = divmod(blk, 2)
+        expect[r, 32 * c0:32 * c0 + 32] = [d * v for v in q]
+    w = O.dequant_q8_0(np.frombuffer(raw, dtype=np.uint8), 2, 64)
+    assert np.array_equal(w, expect)
+
+
+def test_q8_0_round_trip_of_grid_values():
+    # values on a block's grid d * q (|q| <= 127) come back exactly
+    rng = np.random.default_rng(11)
+    rows, cols = 3, 96
+    d = np.float16(rng.uniform(0.01, 0.1, size=(rows, cols // 32)))
+    q = rng.integers(-127, 128, size=(rows, cols))
+    raw = bytearray()
+    for r in range(rows):
+        for b in range(cols // 32):
+            raw += _q8_0_block(int(d[r, b].view(np.uint16)), q[r, 32 * b:32 * b + 32].tolist())
+    w = O.dequant_q8_0(np.frombuffer(bytes(raw), dtype=np.uint8), rows, cols)
+    assert np.array_equal(w, np.repeat(d.astype(np.float64), 32, axis=1) * q)
+
+
 # ----------------------------------------------------------------------------
 # RoPE
 # ----------------------------------------------------------------------------
