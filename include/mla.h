@@ -67,7 +67,8 @@ enum {
 enum {
   MLA_F32 = 0,   /* IEEE float32 */
   MLA_BF16 = 1,  /* bfloat16 bit patterns (uint16) */
-  MLA_Q4G64 = 2  /* 4-bit affine, group 64 along the input dim (weights only) */
+  MLA_Q4G64 = 2, /* 4-bit affine, group 64 along the input dim (weights only) */
+  MLA_Q8_0 = 3   /* 8-bit blocks of 32 with a binary16 scale (kv_b only) */
 };
 
 /* ---- device status flags OR-ed by mla_cache_append (dev_status) ---- */
@@ -98,6 +99,12 @@ typedef struct mla_dims {
  *     [rows, cols/64]; w = scale * nibble + bias.  Products with a Q4G64
  *     weight whose depth is a multiple of 128 run on fp16 MFMA: w and the
  *     activations are rounded to fp16 (11-bit significands), sums are fp32.
+ *   MLA_Q8_0: data = bytes, [rows][cols/32] blocks of 34: a little-endian
+ *     binary16 scale d, then 32 signed bytes q; element = d * q (turbospark
+ *     deepseek2/attn.rs, validate_q8_0_matrix: kv_b read in place; the byte
+ *     layout is GGUF's Q8_0).  cols must be a multiple of 32; scales and
+ *     biases are unused.  Accepted for kv_b only; products with it run on
+ *     the VALU kernels in fp32.
  * A norm weight (gamma) is passed as a 1 x n matrix of MLA_F32 or MLA_BF16.
  * All pointers are device pointers. */
 typedef struct mla_weight {
@@ -187,7 +194,7 @@ int mla_cache_append(const mla_dims* dims, int32_t batch, const float* x,
  *   q_a_norm   1 x q_lora gamma (required with q_a)
  *   q_b        [H*(N+R), q_lora] up projection (required with q_a)
  *   kv_b       [H*(N+V), C]: head h owns rows h*(N+V)..+N-1 (W_UK) then V
- *              rows (W_UV)
+ *              rows (W_UV); F32, BF16, Q4G64 or Q8_0
  *   positions  device int32 [batch]: rotation position of each query
  *   q_abs      device [batch, H, W] of cache_dtype, written:
  *              q_abs[b,h,:C] = sum_n W_UK[h,n,:] q_nope[b,h,n] (fp32
@@ -239,6 +246,16 @@ int mla_decode_attn(const mla_dims* dims, int32_t batch, const void* q_abs,
 int mla_out_proj(const mla_dims* dims, int32_t batch, const float* v_combine,
                  const mla_weight* kv_b, const mla_weight* o_proj, float* out,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* mla_validate_q8_0_kv_b -- host-side check of a Q8_0 kv_b tensor before it
+ * is wrapped as an mla_weight (turbospark deepseek2/attn.rs,
+ * validate_q8_0_matrix and its unit test): the dtype must be MLA_Q8_0, the
+ * shape (rows, cols) must equal (heads * (nope + v_head), kv_lora), kv_lora
+ * must be a positive multiple of 32, and size_bytes must equal
+ * rows * (kv_lora / 32) * 34.  Host values only; touches no device.
+ * Errors: DTYPE (wrong dtype), DIMS (shape, width, size or an overflow). */
+int mla_validate_q8_0_kv_b(int32_t dtype, int64_t rows, int64_t cols, int64_t size_bytes,
+                           int32_t heads, int32_t nope, int32_t kv_lora, int32_t v_head);
 
 /* Bytes of workspace that covers every call above for this geometry, batch,
  * max_seq_len and split_rows (0 = automatic).  Returns 0 for invalid dims. */

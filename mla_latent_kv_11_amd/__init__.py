@@ -24,11 +24,12 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK = 0
 MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE, MLA_ERR_UNSUPPORTED = -1, -2, -3, -4
 MLA_ERR_CAPACITY, MLA_ERR_WORKSPACE, MLA_ERR_HIP = -5, -6, -7
-MLA_F32, MLA_BF16, MLA_Q4G64 = 0, 1, 2
+MLA_F32, MLA_BF16, MLA_Q4G64, MLA_Q8_0 = 0, 1, 2, 3
 MLA_DEV_POS_RANGE, MLA_DEV_BAD_BLOCK = 1, 2
 
 EXPORTED = ("mla_yarn_tables", "mla_cache_append", "mla_absorb_q", "mla_decode_attn",
-            "mla_out_proj", "mla_workspace_bytes", "mla_attn_plan", "mla_status_str")
+            "mla_out_proj", "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan",
+            "mla_status_str")
 
 
 class MLAError(RuntimeError):
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_decode_attn": ([PD, I32, P, PC, P, I32, ctypes.c_float, I32, P, P, P, SZ, P],
                             ctypes.c_int),
         "mla_out_proj": ([PD, I32, P, PW, PW, P, P, SZ, P], ctypes.c_int),
+        "mla_validate_q8_0_kv_b": ([I32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, I32, I32,
+                                    I32, I32], ctypes.c_int),
         "mla_workspace_bytes": ([PD, I32, I32, I32], SZ),
         "mla_attn_plan": ([PD, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
                           ctypes.c_int),
@@ -193,6 +196,13 @@ def yarn_tables(rope_dim: int, qk_head_dim: int, theta=10000.0, factor=40.0,
 def workspace_bytes(dims: Dims, batch: int, max_seq_len: int, split_rows: int = 0) -> int:
     return int(load_library().mla_workspace_bytes(ctypes.byref(dims.c()), batch, max_seq_len,
                                                   split_rows))
+
+
+def validate_q8_0_kv_b(dtype: int, rows: int, cols: int, size_bytes: int, heads: int, nope: int,
+                       kv_lora: int, v_head: int) -> int:
+    """Status of the host-side Q8_0 kv_b check (MLA_OK when the tensor is usable)."""
+    return int(load_library().mla_validate_q8_0_kv_b(dtype, rows, cols, size_bytes, heads, nope,
+                                                     kv_lora, v_head))
 
 
 def attn_plan(dims: Dims, batch: int, max_seq_len: int, split_rows: int = 0):

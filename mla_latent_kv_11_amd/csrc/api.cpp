@@ -43,15 +43,19 @@ int dims_status(const mla_dims* d) {
 }
 
 // A weight must be non-null, of an accepted dtype, and exactly [rows, cols].
-int check_weight(const mla_weight* w, int64_t rows, int64_t cols, bool allow_q4) {
+// allow_q4: the 4-bit affine format; allow_q8: Q8_0 (kv_b only).
+int check_weight(const mla_weight* w, int64_t rows, int64_t cols, bool allow_q4,
+                 bool allow_q8 = false) {
   if (!w || !w->data) return MLA_ERR_NULL;
-  if (w->dtype != MLA_F32 && w->dtype != MLA_BF16 && !(allow_q4 && w->dtype == MLA_Q4G64))
+  if (w->dtype != MLA_F32 && w->dtype != MLA_BF16 && !(allow_q4 && w->dtype == MLA_Q4G64) &&
+      !(allow_q8 && w->dtype == MLA_Q8_0))
     return MLA_ERR_DTYPE;
   if (w->rows != rows || w->cols != cols) return MLA_ERR_DIMS;
   if (w->dtype == MLA_Q4G64) {
     if (cols % 64 != 0) return MLA_ERR_DIMS;
     if (!w->scales || !w->biases) return MLA_ERR_NULL;
   }
+  if (w->dtype == MLA_Q8_0 && (cols % 32 != 0 || cols <= 0)) return MLA_ERR_DIMS;
   return MLA_OK;
 }
 
@@ -151,6 +155,19 @@ double yarn_get(double s, double m) { return s <= 1.0 ? 1.0 : 0.1 * m * log(s) +
 }  // namespace
 
 extern "C" {
+
+int mla_validate_q8_0_kv_b(int32_t dtype, int64_t rows, int64_t cols, int64_t size_bytes,
+                           int32_t heads, int32_t nope, int32_t kv_lora, int32_t v_head) {
+  if (dtype != MLA_Q8_0) return MLA_ERR_DTYPE;
+  if (heads < 1 || nope < 0 || v_head < 0 || kv_lora < 1) return MLA_ERR_DIMS;
+  const int64_t expect_rows = (int64_t)heads * ((int64_t)nope + v_head);  // no overflow in int64
+  if (rows != expect_rows || cols != kv_lora) return MLA_ERR_DIMS;
+  if (kv_lora % 32 != 0) return MLA_ERR_DIMS;
+  const int64_t row_bytes = (int64_t)(kv_lora / 32) * 34;
+  if (rows > INT64_MAX / row_bytes) return MLA_ERR_DIMS;
+  if (size_bytes != rows * row_bytes) return MLA_ERR_DIMS;
+  return MLA_OK;
+}
 
 const char* mla_status_str(int st) {
   switch (st) {
@@ -293,7 +310,7 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
   const int H = d->num_heads, N = d->qk_nope, R = d->qk_rope, V = d->v_head, C = d->kv_lora;
   if (N < 1 || N > 4096) return MLA_ERR_DIMS;
   if (!q_in || !rope || !rope->inv_freq || !positions || !q_abs) return MLA_ERR_NULL;
-  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true))) return st;
+  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true, true))) return st;
   if (q_a) {
     if (d->q_lora < 1 || d->hidden < 1) return MLA_ERR_DIMS;
     if ((st = check_weight(q_a, d->q_lora, d->hidden, true))) return st;
@@ -437,7 +454,7 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
   if (B < 0) return MLA_ERR_DIMS;
   const int H = d->num_heads, N = d->qk_nope, V = d->v_head, C = d->kv_lora;
   if (!v_combine || !out) return MLA_ERR_NULL;
-  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true))) return st;
+  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true, true))) return st;
   if (o_proj) {
     if (d->hidden < 1) return MLA_ERR_DIMS;
     if ((st = check_weight(o_proj, d->hidden, (int64_t)H * V, true))) return st;

@@ -50,6 +50,11 @@ struct WeightView {
 __device__ __forceinline__ float weight_at(const WeightView& w, int64_t r, int64_t k) {
   if (w.dtype == MLA_F32) return static_cast<const float*>(w.data)[r * w.cols + k];
   if (w.dtype == MLA_BF16) return bf16_to_f32(static_cast<const uint16_t*>(w.data)[r * w.cols + k]);
+  if (w.dtype == MLA_Q8_0) {  // 34-byte blocks: binary16 scale, 32 signed bytes
+    const uint8_t* blk = static_cast<const uint8_t*>(w.data) + (r * (w.cols >> 5) + (k >> 5)) * 34;
+    const uint16_t dbits = (uint16_t)(blk[0] | (blk[1] << 8));
+    return (float)__builtin_bit_cast(_Float16, dbits) * (float)(int8_t)blk[2 + (k & 31)];
+  }
   const uint32_t word = static_cast<const uint32_t*>(w.data)[r * (w.cols >> 3) + (k >> 3)];
   const float q = static_cast<float>((word >> (4 * (k & 7))) & 15u);
   const int64_t g = r * (w.cols >> 6) + (k >> 6);

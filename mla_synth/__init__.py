@@ -193,6 +193,43 @@ def build_pool(rng, dims: Dims, lens, *, std=1.0, paged=False, appended=True):
     return pool, table
 
 
+def to_q8_0(w) -> np.ndarray:
+    """float [rows, cols] -> Q8_0 bytes, rows x cols/32 blocks of 34 (input generation).
+
+    Per block of 32: scale d = max|w| / 127 stored as binary16 (little
+    endian), then q = round(w / d) clipped to [-127, 127] as signed bytes.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    rows, cols = w.shape
+    blk = w.reshape(rows, cols // 32, 32)
+    d16 = (np.abs(blk).max(axis=2) / 127.0).astype("<f2")
+    d = d16.astype(np.float64)
+    safe = np.where(d > 0, d, 1.0)
+    q = np.clip(np.rint(blk / safe[..., None]), -127, 127)
+    q = np.where(d[..., None] > 0, q, 0).astype(np.int8)
+    out = np.empty((rows, cols // 32, 34), dtype=np.uint8)
+    out[:, :, :2] = d16.view(np.uint8).reshape(rows, cols // 32, 2)
+    out[:, :, 2:] = q.view(np.uint8)
+    return out.reshape(-1)
+
+
+def with_q8_0_kv_b(case: "Case", seed: int = 808) -> "Case":
+    """The same case with kv_b stored as Q8_0: quantised from its current values
+    (fp32 or bf16), or, for a 4-bit kv_b, from a fresh draw of N(0, 0.02^2)."""
+    import copy
+    d = case.dims
+    rows, cols = d.num_heads * (d.qk_nope + d.v_head), d.kv_lora
+    if isinstance(case.kv_b, Q4Weight):
+        vals = np.random.default_rng(seed).normal(0.0, 0.02, size=(rows, cols))
+    else:
+        kv = np.asarray(case.kv_b)
+        vals = bf16_bits_to_f32(kv) if kv.dtype == np.uint16 else kv.astype(np.float32)
+    out = copy.copy(case)
+    out.kv_b = to_q8_0(vals.reshape(rows, cols))
+    out.name = case.name + "_q8_0kvb"
+    return out
+
+
 def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optional[int] = None,
               paged: Optional[bool] = None, sharp: bool = False) -> Case:
     """Build configuration ``cfg`` (1..5) with optional size overrides.

@@ -28,6 +28,8 @@ def weight(w, rows: int, cols: int, device="cuda") -> mla.Weight:
         return mla.Weight(mla.MLA_Q4G64, rows, cols, t(w.packed, device), t(w.scales, device),
                           t(w.biases, device))
     a = np.asarray(w)
+    if a.dtype == np.uint8:  # Q8_0 blocks
+        return mla.Weight(mla.MLA_Q8_0, rows, cols, t(a.reshape(-1), device))
     dt = mla.MLA_BF16 if a.dtype == np.uint16 else mla.MLA_F32
     return mla.Weight(dt, rows, cols, t(a.reshape(rows, cols), device))
 

@@ -143,6 +143,61 @@ def test_absorb_and_out_proj_validation(lib):
                             None) == mla.MLA_ERR_NULL
 
 
+def test_q8_0_kv_b_validation(lib):
+    # the pages' kv_b check: dtype, shape (H*(N+V), C), C tiling 32-value blocks,
+    # packed size rows * C/32 * 34 -- heads 4, nope 2, kv_lora 64, v 1 as in
+    # the pages' unit test
+    ok = dict(dtype=mla.MLA_Q8_0, rows=12, cols=64, size_bytes=12 * 2 * 34, heads=4, nope=2,
+              kv_lora=64, v_head=1)
+    assert mla.validate_q8_0_kv_b(**ok) == mla.MLA_OK
+    assert mla.validate_q8_0_kv_b(**{**ok, "dtype": 12}) == mla.MLA_ERR_DTYPE
+    assert mla.validate_q8_0_kv_b(**{**ok, "dtype": mla.MLA_BF16}) == mla.MLA_ERR_DTYPE
+    assert mla.validate_q8_0_kv_b(**{**ok, "rows": 11}) == mla.MLA_ERR_DIMS
+    assert mla.validate_q8_0_kv_b(**{**ok, "cols": 32}) == mla.MLA_ERR_DIMS
+    assert mla.validate_q8_0_kv_b(**{**ok, "size_bytes": 12 * 2 * 34 - 1}) == mla.MLA_ERR_DIMS
+    assert mla.validate_q8_0_kv_b(**{**ok, "size_bytes": 12 * 2 * 34 + 1}) == mla.MLA_ERR_DIMS
+    # a width that does not tile whole blocks
+    assert mla.validate_q8_0_kv_b(**{**ok, "cols": 48, "kv_lora": 48,
+                                     "size_bytes": 12 * 34}) == mla.MLA_ERR_DIMS
+    assert mla.validate_q8_0_kv_b(**{**ok, "kv_lora": 0, "cols": 0,
+                                     "size_bytes": 0}) == mla.MLA_ERR_DIMS
+    # DeepSeek-V3 kv_b: 128 heads x (128 + 128) rows x 512
+    assert mla.validate_q8_0_kv_b(mla.MLA_Q8_0, 32768, 512, 32768 * 16 * 34, 128, 128, 512,
+                                  128) == mla.MLA_OK
+
+
+def test_q8_0_accepted_for_kv_b_only(lib):
+    d = mla.Dims(16, 32, 16, 32, 64, hidden=256, q_lora=0, cache_dtype=mla.MLA_F32)
+    rope = mla.CRope(0x100, 1.0)
+    kvb8 = _w(mla.MLA_Q8_0, 16 * 64, 64)
+    # kv_b as Q8_0 passes the weight checks and stops at the missing workspace
+    wo = _w(mla.MLA_F32, 256, 16 * 32)
+    assert lib.mla_out_proj(ctypes.byref(d.c()), 1, 0x10, ctypes.byref(kvb8), ctypes.byref(wo),
+                            0x20, None, 0, None) == mla.MLA_ERR_WORKSPACE
+    # ... but not where its width does not tile 32-value blocks
+    d48 = mla.Dims(16, 32, 16, 32, 48, hidden=256, q_lora=0, cache_dtype=mla.MLA_F32)
+    assert lib.mla_out_proj(ctypes.byref(d48.c()), 1, 0x10,
+                            ctypes.byref(_w(mla.MLA_Q8_0, 16 * 64, 48)), ctypes.byref(wo), 0x20,
+                            None, 0, None) == mla.MLA_ERR_DIMS
+    # o_proj, q_a, q_b and kv_a do not take Q8_0
+    wo8 = _w(mla.MLA_Q8_0, 256, 16 * 32)
+    kvb = _w(mla.MLA_F32, 16 * 64, 64)
+    assert lib.mla_out_proj(ctypes.byref(d.c()), 1, 0x10, ctypes.byref(kvb), ctypes.byref(wo8),
+                            0x20, None, 0, None) == mla.MLA_ERR_DTYPE
+    dq = mla.Dims(16, 32, 16, 32, 64, hidden=256, q_lora=32, cache_dtype=mla.MLA_F32)
+    qa8, qan = _w(mla.MLA_Q8_0, 32, 256), _w(mla.MLA_F32, 1, 32)
+    qb = _w(mla.MLA_F32, 16 * 48, 32)
+    assert lib.mla_absorb_q(ctypes.byref(dq.c()), 1, 0x10, ctypes.byref(qa8), ctypes.byref(qan),
+                            ctypes.byref(qb), ctypes.byref(kvb), ctypes.byref(rope), 0x20, 0x30,
+                            None, 0, None) == mla.MLA_ERR_DTYPE
+    norm = _w(mla.MLA_F32, 1, 64)
+    cache = mla.CCache(0x200, 0x300, 2, 2)
+    assert lib.mla_cache_append(ctypes.byref(d.c()), 1, 0x400,
+                                ctypes.byref(_w(mla.MLA_Q8_0, 80, 256)), ctypes.byref(norm),
+                                ctypes.byref(rope), 0x500, ctypes.byref(cache), None, 0x900,
+                                1 << 20, None) == mla.MLA_ERR_DTYPE
+
+
 @pytest.mark.parametrize("R,head", [(64, 192), (16, 48)])
 def test_library_yarn_table_matches_oracle(lib, R, head):
     inv, rm, sc = mla.yarn_tables(R, head)

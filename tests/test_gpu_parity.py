@@ -356,6 +356,69 @@ def test_out_proj(cfg, kw):
 
 
 # ----------------------------------------------------------------------------
+# Q8_0 kv_b (absorb and expansion read the blocks in place)
+# ----------------------------------------------------------------------------
+Q8_CASES = [(1, {}), (2, dict(lens=[300, 1000], batch=2)), (5, dict(lens=[70, 200], batch=2))]
+
+
+@pytest.mark.parametrize("cfg,kw", Q8_CASES)
+def test_absorb_q_q8_0_kv_b(cfg, kw):
+    case = S.with_q8_0_kv_b(S.make_case(cfg, **kw))
+    ns = D.stage(case)
+    assert ns.kv_b.dtype == mla.MLA_Q8_0
+    ws = D.workspace(ns)
+    q_in = ns.q if ns.q is not None else ns.x
+    mla.absorb_q(ns.dims, q_in, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
+                 ns.q_a, ns.q_a_norm, ns.q_b, ws)
+    sync()
+    res = oracle_for(case)
+    got = O.widen(host(ns.q_abs), case.dims.cache_dtype)
+    if case.dims.cache_dtype == O.F32:
+        close_f32(got, res["q_abs64"], "q_abs")
+    else:
+        close_bf16(got, res["q_abs64"], "q_abs")
+
+
+@pytest.mark.parametrize("cfg,kw", Q8_CASES)
+def test_out_proj_q8_0_kv_b(cfg, kw):
+    case = S.with_q8_0_kv_b(S.make_case(cfg, **kw))
+    ns = D.stage(case)
+    rng = np.random.default_rng(17)
+    vc = rng.standard_normal((case.batch, case.dims.num_heads, case.dims.kv_lora)).astype(np.float32)
+    ns.v_combine = D.t(vc)
+    ws = D.workspace(ns)
+    mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws)
+    sync()
+    d = case.dims
+    kvb = O.weight_f64(case.kv_b, O.Q8_0, d.num_heads * (d.qk_nope + d.v_head), d.kv_lora)
+    o64 = (O.weight_f64(case.o_proj, O.weight_dtype(case.o_proj), d.hidden,
+                        d.num_heads * d.v_head) if case.o_proj is not None else None)
+    ref = O.out_proj(d, vc.astype(np.float64), kvb, o64).reshape(case.batch, -1)
+    got = host(ns.out)
+    if d.cache_dtype == O.F32:
+        close_f32(got, ref, "out")
+    else:
+        close_bf16(got, ref, "out")
+        # Q8_0 decodes exactly in fp32 (binary16 scale x int8) and W_UV sums in
+        # fp32; a 4-bit o_proj adds its fp16-operand error (~4e-4 rms)
+        lim = 2e-3 if case.o_proj is not None and O.weight_dtype(case.o_proj) == O.Q4G64 else 1e-4
+        assert np.max(np.abs(got - ref)) <= lim * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("cfg,kw", [(2, dict(lens=[1000, 37], batch=2)),
+                                    (3, dict(batch=3, lens=[1024, 1500, 2049])),
+                                    (5, dict(batch=2, lens=[300, 1100]))])
+def test_chain_q8_0_kv_b(cfg, kw):
+    case = S.with_q8_0_kv_b(S.make_case(cfg, **kw))
+    ns = D.stage(case)
+    D.run_step(case, ns)
+    sync()
+    res = O.decode_step(case)
+    close_bf16(host(ns.v_combine), res["v_combine"], "v_combine")
+    close_bf16(host(ns.out), res["out"].reshape(case.batch, -1), "out")
+
+
+# ----------------------------------------------------------------------------
 # the whole step, reduced sizes
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg,kw", [
