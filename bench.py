@@ -161,6 +161,43 @@ def oracle_threads():
         return os.cpu_count() or 1
 
 
+def time_kv_b_formats(case, torch, D, S, mla, iters=20):
+    """absorb_q and out_proj of the same layer with kv_b as 4-bit affine (MFMA
+    kernels) and as Q8_0 (read in place by the VALU kernels); HIP events around
+    ``iters`` back-to-back calls of each."""
+    import numpy as np
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, c in (("q4g64", case), ("q8_0", S.with_q8_0_kv_b(case))):
+        ns = D.stage(c)
+        ws = D.workspace(ns)
+
+        def absorb():
+            mla.absorb_q(ns.dims, ns.q if ns.q is not None else ns.x, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions,
+                         ns.q_abs, ns.q_a, ns.q_a_norm, ns.q_b, ws)
+
+        def expand():
+            mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws)
+        r = {}
+        for fname, f in (("absorb_q_ms", absorb), ("out_proj_ms", expand)):
+            for _ in range(5):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            r[fname] = round(e0.elapsed_time(e1) / iters, 4)
+        kv = c.kv_b
+        r["kv_b_bytes"] = int(kv.packed.nbytes + kv.scales.nbytes + kv.biases.nbytes
+                              if hasattr(kv, "packed") else np.asarray(kv).nbytes)
+        out[name] = r
+        del ns, ws
+    return out
+
+
 def cpu_baseline(case, seqs, min_seconds=10.0, max_reps=8):
     """The oracle's whole step on ``seqs`` sequences of the same workload,
     repeated until about ``min_seconds`` of host work."""
@@ -354,6 +391,7 @@ def main():
         for cfg, name in ((2, "b1_L4096"), (3, "b64_L1024-8192_paged"), (4, "b4_L131072")):
             extra[name] = time_attn_only(cfg, torch, D, S, mla, oracle=not args.no_cpu)
         line["attn_only"] = extra
+        line["kv_b_formats"] = time_kv_b_formats(case, torch, D, S, mla)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seqs)
     print(json.dumps(line), flush=True)

@@ -118,9 +118,39 @@ __device__ __forceinline__ f16x8_t dequant8(uint32_t word, f16x2_t s2, f16x2_t b
   return __builtin_bit_cast(f16x8_t, uint4{r[0], r[1], r[2], r[3]});
 }
 
-template <int U>
-__global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs a, int nw, int S) {
-  extern __shared__ float red[];  // [nw][16][64]
+// Q8_0: a lane's share of a unit is two 34-byte blocks of its row (64 of the
+// unit's 128 k).  The q bytes of a block start 2 bytes into it, so they are
+// read as 8 aligned dwords from the 4-byte boundary at or below their start,
+// plus the 16-bit word after those (used when the start is 2 mod 4, and
+// otherwise read from inside the block so no load passes its end).
+struct UnitQ8 {
+  uint32_t q[2][8];
+  uint16_t qx[2];
+  uint16_t d[2];
+  uint4 x[8];
+};
+
+// 8 signed bytes (k0..k3 in lo, k4..k7 in hi) times a binary16 scale, as fp16
+// in the pair order k0 k4 k1 k5 k2 k6 k3 k7 of the packed activations: byte
+// pairs become fp16 1024 + (q + 128) by their bit patterns (the sign bit of
+// each byte flipped, 0x64 above it), then 1152 is subtracted (exact) and the
+// products d * q are rounded once to fp16.
+__device__ __forceinline__ f16x8_t dequant8_q8(uint32_t lo, uint32_t hi, f16x2_t d2) {
+  const f16x2_t k1152 = {(_Float16)1152.f, (_Float16)1152.f};
+  uint32_t r[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // result bytes: lo.b, 0, hi.b, 0
+    const uint32_t sel = (uint32_t)b | (0x0cu << 8) | ((uint32_t)(4 + b) << 16) | (0x0cu << 24);
+    const uint32_t t = __builtin_amdgcn_perm(hi, lo, sel) ^ 0x64806480u;
+    const f16x2_t q = __builtin_bit_cast(f16x2_t, t) - k1152;
+    r[b] = __builtin_bit_cast(uint32_t, q * d2);
+  }
+  return __builtin_bit_cast(f16x8_t, uint4{r[0], r[1], r[2], r[3]});
+}
+
+template <int U, bool kQ8>
+__device__ __forceinline__ void gemm_mfma_body(const GemmArgs& a, int nw, int S, float* red) {
   const int zz = blockIdx.z / S, s = blockIdx.z - zz * S;
   const int o0 = blockIdx.x * 32, b0 = blockIdx.y * 32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
@@ -140,14 +170,32 @@ __global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs
   const uint32_t soff = wrow * (uint32_t)(a.w.cols >> 6) * 2u + 2u * hh;  // + 4 per unit
   const uint32_t xoff =
       (uint32_t)((zz * gridDim.y + blockIdx.y) * units) * 8192u + 16u * lane;  // + 8192 per unit
+  // Q8_0: byte offset of the lane's first block (+ 136 per unit), and the
+  // shift that realigns each block's q bytes (unit strides keep it fixed)
+  const uint32_t q8off = wrow * (uint32_t)((a.w.cols >> 5) * 34) + 68u * hh;
+  const uint32_t q8sh[2] = {((q8off + 2u) & 2u) * 8u, ((q8off + 36u) & 2u) * 8u};
 
-  Unit ub[2];
+  using UnitT = typename std::conditional<kQ8, UnitQ8, Unit>::type;
+  UnitT ub[2];
   auto issue = [&](int slot, int ku) {
-    const uint32_t wo = woff + 64u * ku, so = soff + 4u * ku, xo = xoff + 8192u * ku;
-    ub[slot].w[0] = *reinterpret_cast<const uint4*>(wbase + wo);
-    ub[slot].w[1] = *reinterpret_cast<const uint4*>(wbase + wo + 16u);
-    ub[slot].sc = *reinterpret_cast<const uint16_t*>(sbase + so);
-    ub[slot].bi = *reinterpret_cast<const uint16_t*>(bbase + so);
+    const uint32_t xo = xoff + 8192u * ku;
+    if constexpr (kQ8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t blk = q8off + 136u * ku + 34u * j, qs = blk + 2u, al = qs & ~3u;
+        ub[slot].d[j] = *reinterpret_cast<const uint16_t*>(wbase + blk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          ub[slot].q[j][i] = *reinterpret_cast<const uint32_t*>(wbase + al + 4u * i);
+        ub[slot].qx[j] = *reinterpret_cast<const uint16_t*>(wbase + ((qs & 2u) ? al + 32u : al + 30u));
+      }
+    } else {
+      const uint32_t wo = woff + 64u * ku, so = soff + 4u * ku;
+      ub[slot].w[0] = *reinterpret_cast<const uint4*>(wbase + wo);
+      ub[slot].w[1] = *reinterpret_cast<const uint4*>(wbase + wo + 16u);
+      ub[slot].sc = *reinterpret_cast<const uint16_t*>(sbase + so);
+      ub[slot].bi = *reinterpret_cast<const uint16_t*>(bbase + so);
+    }
 #pragma unroll
     for (int st = 0; st < 8; ++st)
       ub[slot].x[st] = *reinterpret_cast<const uint4*>(xbase + xo + 1024u * st);
@@ -164,15 +212,33 @@ __global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs
     const int ku = ubeg + u;
     if (u + 1 < U) issue((u + 1) & 1, ku + 1 < ulast ? ku + 1 : ulast);
     if (ku >= units) continue;
-    const Unit& c = ub[u & 1];
-    const _Float16 sh = (_Float16)bf16_to_f32(c.sc), bh = (_Float16)bf16_to_f32(c.bi);
-    const f16x2_t s2 = {sh, sh}, b2 = {bh, bh};
-    const uint32_t words[8] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w,
-                               c.w[1].x, c.w[1].y, c.w[1].z, c.w[1].w};
+    const UnitT& c = ub[u & 1];
+    if constexpr (kQ8) {
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c.x[st]),
-                                                   dequant8(words[st], s2, b2), acc, 0, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const _Float16 dh = __builtin_bit_cast(_Float16, c.d[j]);
+        const f16x2_t d2 = {dh, dh};
+        uint32_t qd[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          qd[i] = __builtin_amdgcn_alignbit(i < 7 ? c.q[j][i + 1] : (uint32_t)c.qx[j], c.q[j][i],
+                                            q8sh[j]);
+#pragma unroll
+        for (int st4 = 0; st4 < 4; ++st4)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8_t, c.x[4 * j + st4]),
+              dequant8_q8(qd[2 * st4], qd[2 * st4 + 1], d2), acc, 0, 0, 0);
+      }
+    } else {
+      const _Float16 sh = (_Float16)bf16_to_f32(c.sc), bh = (_Float16)bf16_to_f32(c.bi);
+      const f16x2_t s2 = {sh, sh}, b2 = {bh, bh};
+      const uint32_t words[8] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w,
+                                 c.w[1].x, c.w[1].y, c.w[1].z, c.w[1].w};
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c.x[st]),
+                                                     dequant8(words[st], s2, b2), acc, 0, 0, 0);
+    }
   }
 
 #pragma unroll
@@ -191,6 +257,18 @@ __global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs
     else
       a.y[(int64_t)s * a.y_s + (int64_t)zz * a.y_z + (int64_t)t * a.y_b + o] = v;
   }
+}
+
+template <int U>
+__global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs a, int nw, int S) {
+  extern __shared__ float red[];  // [nw][16][64]
+  gemm_mfma_body<U, false>(a, nw, S, red);
+}
+
+template <int U>
+__global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q8_mfma_kernel(GemmArgs a, int nw, int S) {
+  extern __shared__ float red[];  // [nw][16][64]
+  gemm_mfma_body<U, true>(a, nw, S, red);
 }
 
 // fp32 x[z*x_z + b*x_b + k] -> packed fp16; one thread writes one 16-byte chunk
@@ -519,7 +597,7 @@ __global__ void __launch_bounds__(kAbsC) absorb_kernel(AbsorbArgs a) {
   }
 }
 
-// 4-bit W_UK on MFMA: q'[b][h][c] = sum_n W_UK[h][n][c] q_nope[b][h][n].
+// 4-bit or Q8_0 W_UK on MFMA: q'[b][h][c] = sum_n W_UK[h][n][c] q_nope[b][h][n].
 // grid (H, ceil(C/128), ceil(B/32)), 256 threads.  The workgroup first loads
 // its W_UK slice (128 n x 128 c, 16 bytes per row per thread, coalesced) and
 // dequantises it into LDS as fp16 transposed to [c][n], so one MFMA operand
@@ -527,11 +605,13 @@ __global__ void __launch_bounds__(kAbsC) absorb_kernel(AbsorbArgs a) {
 // columns c0..c0+31 (c0 = 128 blockIdx.y + 32 w) for 32 tokens: the token is
 // the MFMA M dimension and k-slot j of lane-half hh at step st is n = n0 +
 // 64hh + 8st + j on both operands.  Workgroups with blockIdx.y == 0 also
-// rotate q_pe of their tokens.
+// rotate q_pe of their tokens.  A staging thread's 32 columns of a row are
+// one Q8_0 block (d * q, exact in fp32, then rounded to fp16 like the 4-bit
+// values); its bytes are only 2-byte aligned, so they are read as 16-bit words.
 constexpr int kAbsN = 128, kAbsCols = 128, kAbsPitch = kAbsN + 8;  // LDS row pitch in halfs
 
-template <typename T>
-__global__ void __launch_bounds__(256) absorb_q4_mfma_kernel(AbsorbArgs a) {
+template <typename T, bool kQ8>
+__global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
   __shared__ _Float16 wt[kAbsCols * kAbsPitch];  // [c][n]
   const int h = blockIdx.x;
   const int b0 = blockIdx.z * 32;
@@ -566,7 +646,28 @@ __global__ void __launch_bounds__(256) absorb_q4_mfma_kernel(AbsorbArgs a) {
   const bool st_on = cst < a.C;
   f32x16_t acc = f32x16_t{};
   for (int n0 = 0; n0 < a.N; n0 += kAbsN) {
-    if (st_on) {
+    if (kQ8 && st_on) {
+      const uint8_t* kvb = static_cast<const uint8_t*>(a.kv_b.data);
+      const int64_t nblk = a.kv_b.cols >> 5;
+      float d[2];
+      uint16_t qw[2][16];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint16_t* blk = reinterpret_cast<const uint16_t*>(
+            kvb + ((row0 + n0 + 2 * np + r) * nblk + (cst >> 5)) * 34);
+        d[r] = (float)__builtin_bit_cast(_Float16, blk[0]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qw[r][i] = blk[1 + i];
+      }
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const int8_t q0 = (int8_t)(qw[0][c >> 1] >> (8 * (c & 1)));
+        const int8_t q1 = (int8_t)(qw[1][c >> 1] >> (8 * (c & 1)));
+        const _Float16 pr[2] = {(_Float16)(d[0] * (float)q0), (_Float16)(d[1] * (float)q1)};
+        *reinterpret_cast<uint32_t*>(&wt[(32 * cq + c) * kAbsPitch + 2 * np]) =
+            __builtin_bit_cast(uint32_t, pr);
+      }
+    } else if (st_on) {
       uint4 wv[2];
       float sc[2], bi[2];
 #pragma unroll
@@ -623,6 +724,16 @@ constexpr int kMaxU = 16;
 hipError_t launch_q4(const GemmArgs& a, int U, int nw, int S, hipStream_t s) {
   dim3 grid((a.O + 31) / 32, (a.B + 31) / 32, a.Z * S);
   const size_t lds = (size_t)nw * 16 * 64 * sizeof(float);
+  if (a.w.dtype == MLA_Q8_0) {
+    switch (U) {
+      case 1: hipLaunchKernelGGL(gemm_q8_mfma_kernel<1>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+      case 2: hipLaunchKernelGGL(gemm_q8_mfma_kernel<2>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+      case 4: hipLaunchKernelGGL(gemm_q8_mfma_kernel<4>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+      case 8: hipLaunchKernelGGL(gemm_q8_mfma_kernel<8>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+      default: hipLaunchKernelGGL(gemm_q8_mfma_kernel<16>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
+    }
+    return hipGetLastError();
+  }
   switch (U) {
     case 1: hipLaunchKernelGGL(gemm_q4_mfma_kernel<1>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
     case 2: hipLaunchKernelGGL(gemm_q4_mfma_kernel<2>, grid, dim3(nw * 64), lds, s, a, nw, S); break;
@@ -636,9 +747,13 @@ hipError_t launch_q4(const GemmArgs& a, int U, int nw, int S, hipStream_t s) {
 
 bool gemm_mfma_ok(const GemmArgs& a) {
   // 32-bit byte offsets inside the kernel: weights and packed activations under 2 GiB
-  const int64_t wbytes = (int64_t)a.w.rows * a.w.cols / 2;
+  const bool q8 = a.w.dtype == MLA_Q8_0;
+  const int64_t wbytes = q8 ? (int64_t)a.w.rows * (a.w.cols / 32) * 34 : (int64_t)a.w.rows * a.w.cols / 2;
   const int64_t xbytes = (int64_t)packed_bytes(a.Z, a.B, a.K);
-  return a.w.dtype == MLA_Q4G64 && a.K > 0 && (a.K % 128) == 0 && (a.w.cols % 64) == 0 &&
+  // Q8_0 blocks are read with aligned dword loads from a 4-byte aligned base
+  if (q8 && (reinterpret_cast<uintptr_t>(a.w.data) & 3) != 0) return false;
+  return (a.w.dtype == MLA_Q4G64 || q8) && a.K > 0 && (a.K % 128) == 0 &&
+         (a.w.cols % (q8 ? 32 : 64)) == 0 &&
          a.K <= a.w.cols && (a.K / 128) <= kQ4MaxWaves * kMaxU && wbytes < (1ll << 31) &&
          xbytes < (1ll << 31);
 }
@@ -734,12 +849,17 @@ hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  if (a.kv_b.dtype == MLA_Q4G64 && a.N % kAbsN == 0 && a.C % 32 == 0) {
+  const bool q8_ok = a.kv_b.dtype == MLA_Q8_0 && (reinterpret_cast<uintptr_t>(a.kv_b.data) & 1) == 0;
+  if ((a.kv_b.dtype == MLA_Q4G64 || q8_ok) && a.N % kAbsN == 0 && a.C % 32 == 0) {
     dim3 grid(a.H, (a.C + 127) / 128, (a.B + 31) / 32);
-    if (a.cache_dtype == MLA_F32)
-      hipLaunchKernelGGL(absorb_q4_mfma_kernel<float>, grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(absorb_q4_mfma_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+    const bool q8 = a.kv_b.dtype == MLA_Q8_0;
+    if (a.cache_dtype == MLA_F32) {
+      if (q8) hipLaunchKernelGGL((absorb_mfma_kernel<float, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((absorb_mfma_kernel<float, false>), grid, dim3(256), 0, s, a);
+    } else {
+      if (q8) hipLaunchKernelGGL((absorb_mfma_kernel<uint16_t, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((absorb_mfma_kernel<uint16_t, false>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
   }
   dim3 grid(a.H, (a.C + kAbsC - 1) / kAbsC);

@@ -399,10 +399,9 @@ def test_out_proj_q8_0_kv_b(cfg, kw):
         close_f32(got, ref, "out")
     else:
         close_bf16(got, ref, "out")
-        # Q8_0 decodes exactly in fp32 (binary16 scale x int8) and W_UV sums in
-        # fp32; a 4-bit o_proj adds its fp16-operand error (~4e-4 rms)
-        lim = 2e-3 if case.o_proj is not None and O.weight_dtype(case.o_proj) == O.Q4G64 else 1e-4
-        assert np.max(np.abs(got - ref)) <= lim * np.max(np.abs(ref))
+        # W_UV runs on fp16 MFMA operands (v_combine rounded to binary16, d*q
+        # rounded to binary16) with fp32 sums: ~4e-4 rms relative per stage
+        assert np.max(np.abs(got - ref)) <= 2e-3 * np.max(np.abs(ref))
 
 
 @pytest.mark.parametrize("cfg,kw", [(2, dict(lens=[1000, 37], batch=2)),
