@@ -143,6 +143,9 @@ class Case:
     o_proj: object = None            # [hidden, H*V] fp32 | Q4Weight | None
     q_abs: Optional[np.ndarray] = None       # [B, H, W] in cache dtype (attention-only cases)
     appended: bool = True            # row at position lens-1 is written by the append step
+    # several tokens per sequence: token t belongs to table row token_seq[t] and
+    # sees its first lens[t] rows (batch, lens, x, q, q_abs are per token)
+    token_seq: Optional[np.ndarray] = None
 
     @property
     def positions(self) -> np.ndarray:
@@ -160,14 +163,15 @@ def _store(v, dtype):
     return np.asarray(v, dtype=np.float32) if dtype == F32 else to_bf16_bits(v)
 
 
-def build_pool(rng, dims: Dims, lens, *, std=1.0, paged=False, appended=True):
+def build_pool(rng, dims: Dims, lens, *, std=1.0, paged=False, appended=True, fresh=None):
     """Allocate the paged pool, the block table and fill the prior rows per sequence.
 
     Draw order: (if paged) one permutation of all blocks; then per sequence, in
     order, the values of its allocated blocks (block-major, standard normals
     scaled by ``std``).  Rows past the last valid row inside allocated blocks
     are set to NaN so that any read of them shows up in the output.  With
-    ``appended`` the row at ``len - 1`` is NaN too: it is the append target.
+    ``appended`` the row at ``len - 1`` is NaN too: it is the append target;
+    ``fresh`` (per sequence) sets how many trailing rows are append targets.
     """
     W, blk = dims.width, dims.block_size
     lens = np.asarray(lens, dtype=np.int64)
@@ -185,7 +189,8 @@ def build_pool(rng, dims: Dims, lens, *, std=1.0, paged=False, appended=True):
         table[b, :nb] = ids
         vals = _cache_values(rng, (int(nb), blk, W), std, dims.cache_dtype)
         pool[ids] = vals
-        first_unset = int(lens[b]) - (1 if appended else 0)
+        nf = (1 if appended else 0) if fresh is None else int(np.broadcast_to(fresh, lens.shape)[b])
+        first_unset = int(lens[b]) - nf
         if first_unset < nb * blk:
             flat = pool[ids].reshape(-1, W)
             flat[first_unset:] = np.nan if dims.cache_dtype == F32 else BF16_NAN
@@ -230,8 +235,42 @@ def with_q8_0_kv_b(case: "Case", seed: int = 808) -> "Case":
     return out
 
 
+def _pool_for(rng, d: Dims, L, token_seq, *, std, paged, appended=True):
+    """Pool and table for per-sequence ``L`` or, with ``token_seq``, for the
+    sequences the tokens belong to: a sequence's length is the largest
+    ``L[t]`` of its tokens, and each of its tokens leaves one row to append."""
+    if token_seq is None:
+        return build_pool(rng, d, L, std=std, paged=paged, appended=appended)
+    ns = int(np.max(token_seq)) + 1
+    final = np.zeros(ns, dtype=np.int64)
+    fresh = np.zeros(ns, dtype=np.int64)
+    for t, sq in enumerate(token_seq):
+        final[sq] = max(final[sq], int(L[t]))
+        fresh[sq] += 1
+    return build_pool(rng, d, final, std=std, paged=paged, fresh=fresh if appended else 0)
+
+
+def make_chunk_case(cfg: int, prior, chunk, *, seed: Optional[int] = None,
+                    paged: Optional[bool] = None) -> Case:
+    """Several new tokens per sequence in one step (chunked prefill, multi-token decode).
+
+    Sequence s holds ``prior[s]`` rows and gains ``chunk[s]`` tokens at positions
+    prior[s] .. prior[s] + chunk[s] - 1, stacked sequence by sequence; token t
+    sees ``lens[t]`` = its position + 1 rows.  The draws are those of
+    ``make_case(cfg)`` with one x / q (or q_abs) per token; the pool holds every
+    sequence's prior rows and NaN in the rows its tokens append.
+    """
+    prior = np.asarray(prior, dtype=np.int64)
+    chunk = np.broadcast_to(np.asarray(chunk, dtype=np.int64), prior.shape)
+    token_seq = np.repeat(np.arange(len(prior)), chunk).astype(np.int32)
+    lens = np.concatenate([p + 1 + np.arange(c) for p, c in zip(prior, chunk)]).astype(np.int32)
+    case = make_case(cfg, lens=lens, seed=seed, paged=paged, token_seq=token_seq)
+    case.name += "_chunk"
+    return case
+
+
 def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optional[int] = None,
-              paged: Optional[bool] = None, sharp: bool = False) -> Case:
+              paged: Optional[bool] = None, sharp: bool = False, token_seq=None) -> Case:
     """Build configuration ``cfg`` (1..5) with optional size overrides.
 
     The five configurations, in the storage forms the library takes:
@@ -249,6 +288,7 @@ def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optiona
          latent form, rows ~ N(0, 1), scale 1/sqrt(192).
       5  full layer, batch 32, L 16384: hidden 7168, q_lora 1536, all five
          projections 4-bit affine group 64, bf16 norms; YaRN softmax scale.
+    With ``token_seq`` the batch is of tokens (see ``make_chunk_case``).
     """
     seed = 1000 + cfg if seed is None else seed
     if lens is not None and batch is None:
@@ -261,13 +301,13 @@ def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optiona
         B = 1 if batch is None else batch
         L = np.full(B, 128, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
         std = 1.0 if sharp else 0.02
-        if paged is None and B == 1 and lens is None:
+        if paged is None and B == 1 and lens is None and token_seq is None:
             # the fixed two-block layout: logical block 0 -> physical 1, 1 -> 0
             pool, table = build_pool(rng, d, L, std=std, paged=False)
             pool = pool[::-1].copy()
             table = np.array([[1, 0]], dtype=np.int32)
         else:
-            pool, table = build_pool(rng, d, L, std=std, paged=bool(paged))
+            pool, table = _pool_for(rng, d, L, token_seq, std=std, paged=bool(paged))
         H, N, R, V, C, W = 16, 32, 16, 32, 64, 80
         x = rng.standard_normal((B, d.hidden))
         kv_a = rng.standard_normal((W, d.hidden)) * 0.02
@@ -277,7 +317,8 @@ def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optiona
         o_proj = rng.standard_normal((d.hidden, H * V)) * 0.02
         return Case("cfg1" + ("_sharp" if sharp else ""), d, yarn, B, L, pool, table, None,
                     x=_store(x, F32), kv_a=_store(kv_a, F32), kv_a_norm=_store(gamma, F32),
-                    q=_store(q, F32), kv_b=_store(kv_b, F32), o_proj=_store(o_proj, F32))
+                    q=_store(q, F32), kv_b=_store(kv_b, F32), o_proj=_store(o_proj, F32),
+                    token_seq=token_seq)
     if cfg in (2, 3):
         d = Dims(**DEEPSEEK_V3, hidden=0, q_lora=0, cache_dtype=BF16)
         if cfg == 2:
@@ -289,7 +330,7 @@ def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optiona
             L = (rng.integers(1024, 8192, size=B, endpoint=True).astype(np.int32)
                  if lens is None else np.asarray(lens, dtype=np.int32))
             pg = True if paged is None else paged
-        pool, table = build_pool(rng, d, L, std=1.0, paged=pg)
+        pool, table = _pool_for(rng, d, L, token_seq, std=1.0, paged=pg)
         H, N, R, V, C, W = 128, 128, 64, 128, 512, 576
         x = rng.standard_normal((B, W))
         gamma = 1.0 + 0.1 * rng.standard_normal(C)
@@ -297,20 +338,20 @@ def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optiona
         kv_b = rng.standard_normal((H * (N + V), C)) * 0.02
         return Case(f"cfg{cfg}", d, yarn, B, L, pool, table, 1.0 / np.sqrt(192.0),
                     x=_store(x, F32), kv_a=None, kv_a_norm=to_bf16_bits(gamma),
-                    q=_store(q, F32), kv_b=to_bf16_bits(kv_b))
+                    q=_store(q, F32), kv_b=to_bf16_bits(kv_b), token_seq=token_seq)
     if cfg == 4:
         d = Dims(**DEEPSEEK_V3, hidden=0, q_lora=0, cache_dtype=BF16)
         B = 4 if batch is None else batch
         L = np.full(B, 131072, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
-        pool, table = build_pool(rng, d, L, std=1.0, paged=bool(paged), appended=False)
+        pool, table = _pool_for(rng, d, L, token_seq, std=1.0, paged=bool(paged), appended=False)
         q_abs = to_bf16_bits(rng.standard_normal((B, 128, 576), dtype=np.float32))
         return Case("cfg4", d, yarn, B, L, pool, table, 1.0 / np.sqrt(192.0),
-                    q_abs=q_abs, appended=False)
+                    q_abs=q_abs, appended=False, token_seq=token_seq)
     if cfg == 5:
         d = Dims(**DEEPSEEK_V3, hidden=7168, q_lora=1536, cache_dtype=BF16)
         B = 32 if batch is None else batch
         L = np.full(B, 16384, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
-        pool, table = build_pool(rng, d, L, std=1.0, paged=bool(paged))
+        pool, table = _pool_for(rng, d, L, token_seq, std=1.0, paged=bool(paged))
         H, N, R, V, C, W = 128, 128, 64, 128, 512, 576
         x = rng.standard_normal((B, d.hidden), dtype=np.float32)
         q_a = draw_q4(rng, d.q_lora, d.hidden)
@@ -322,5 +363,5 @@ def make_case(cfg: int, *, batch: Optional[int] = None, lens=None, seed: Optiona
         o_proj = draw_q4(rng, d.hidden, H * V)
         return Case("cfg5", d, yarn, B, L, pool, table, None,
                     x=x, kv_a=kv_a, kv_a_norm=kv_a_norm, q_a=q_a, q_a_norm=q_a_norm, q_b=q_b,
-                    kv_b=kv_b, o_proj=o_proj)
+                    kv_b=kv_b, o_proj=o_proj, token_seq=token_seq)
     raise ValueError(f"unknown configuration {cfg}")

@@ -52,6 +52,14 @@ Readings of points the pages leave open (each also listed in the design doc):
     is 32 values): the pages name the format without its byte layout; it is
     read as GGUF's Q8_0, each block a little-endian binary16 scale d followed
     by 32 signed 8-bit q, element = d * q (34 bytes per block).
+  * Several tokens per sequence in one step (chunked prefill, multi-token
+    decode): [moeflux/matvec] ``encode_matvec_n_tokens`` applies each
+    projection to stacked tokens with per-token arithmetic unchanged; the
+    pages say nothing about attention over several new tokens.  Read plainly:
+    every new row is appended first, and the token at position p attends rows
+    0..p of its own sequence, so a chunk gives what the same tokens give one
+    decode step at a time.  ``token_seq[t]`` names the block-table row of
+    token t; without it token t owns row t.
 """
 from __future__ import annotations
 
@@ -256,13 +264,14 @@ def gather_rows(pool, table, b: int, length: int, block: int) -> np.ndarray:
 # the four calls
 # ----------------------------------------------------------------------------
 def cache_append(dims, x, kv_a, kv_a_dtype, kv_a_norm, norm_dtype, inv_freq, rope_mscale,
-                 positions, pool, table):
+                 positions, pool, table, token_seq=None):
     """kv_a projection -> RMSNorm of the latent half -> RoPE of k_pe -> one rounded row.
 
     [moeflux/forward] ``mla_attn_layer_forward_gpu``: KV-A chain, split,
     ``kv_a_layernorm``, YaRN rope on k_pe, ``mla_kv_cache_append`` into row[pos];
     [ts/deepseek2]: kv_a writes the fused row ``[latent ; k_pe]``, then norm and
     rope run on it.  With ``dims.hidden == 0`` the row before the norm is ``x``.
+    Token b writes into sequence ``token_seq[b]`` (``b`` when it is None).
     Returns (new pool, the appended rows as float64 before rounding).
     """
     C, R, W, blk = dims.kv_lora, dims.qk_rope, dims.width, dims.block_size
@@ -279,7 +288,8 @@ def cache_append(dims, x, kv_a, kv_a_dtype, kv_a_norm, norm_dtype, inv_freq, rop
     out = np.array(pool, copy=True)
     stored = round_to(rows, dims.cache_dtype)
     for b, pos in enumerate(positions):
-        pb, r = slot(table, b, int(pos), blk)
+        seq = b if token_seq is None else int(token_seq[b])
+        pb, r = slot(table, seq, int(pos), blk)
         out[pb, r] = stored[b]
     return out, rows
 
@@ -314,15 +324,16 @@ def absorb_q(dims, q, kv_b64, inv_freq, rope_mscale, positions) -> np.ndarray:
     return np.concatenate([qp, qpe], axis=2)
 
 
-def attention_latent(dims, q_abs64, pool, table, lens, scale: float):
+def attention_latent(dims, q_abs64, pool, table, lens, scale: float, token_seq=None):
     """Latent-form decode attention: the absorbed path.
 
     s[t] = scale * q_abs_h . row_t over the full row [c_kv ; k_pe]; p = softmax
     over t < len (max-subtracted); v_combine_h = sum_t p[t] c_kv[t]; lse_h =
     log sum_t exp(s[t]).  [moeflux/forward] ``mla_sdpa_folded``;
     [ts/deepseek2] ``encode_mla_attention_decode`` (V is the row's first C).
-    Returns (v_combine [B, H, C], lse [B, H], list of p [H, len] per sequence).
-    A sequence of length 0 gives v_combine = 0 and lse = -inf.
+    Returns (v_combine [B, H, C], lse [B, H], list of p [H, len] per query).
+    A query that sees 0 rows gives v_combine = 0 and lse = -inf.  Query b reads
+    the rows of sequence ``token_seq[b]`` (``b`` when it is None).
     """
     C, blk = dims.kv_lora, dims.block_size
     B, H = q_abs64.shape[0], q_abs64.shape[1]
@@ -334,7 +345,8 @@ def attention_latent(dims, q_abs64, pool, table, lens, scale: float):
         if L == 0:
             ps.append(np.zeros((H, 0)))
             continue
-        rows = widen(gather_rows(pool, table, b, L, blk), dims.cache_dtype)   # [L, W]
+        seq = b if token_seq is None else int(token_seq[b])
+        rows = widen(gather_rows(pool, table, seq, L, blk), dims.cache_dtype)  # [L, W]
         s = scale * (q_abs64[b] @ rows.T)                                    # [H, L]
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
@@ -445,6 +457,9 @@ def attention_query(case, res=None, model_q_abs_storage=True) -> np.ndarray:
 def decode_step(case, *, model_q_abs_storage=True):
     """Run append -> absorb (q chain) -> latent attention -> out_proj on a case.
 
+    A case with ``token_seq`` holds several tokens per sequence: all their rows
+    are appended, then token t attends its sequence's first ``lens[t]`` rows.
+
     Returns a dict with the new pool, q (float64), q_abs (float64, and its
     stored form), v_combine, lse and out.  With ``model_q_abs_storage`` the
     attention consumes q_abs rounded to the cache dtype, as the library stores it.
@@ -453,15 +468,16 @@ def decode_step(case, *, model_q_abs_storage=True):
     inv, rm, sc = tables_for(case)
     res = {"inv_freq": inv, "rope_mscale": rm, "softmax_scale": sc}
     pool = case.pool
+    tseq = getattr(case, "token_seq", None)
     if case.appended:
         kdt = weight_dtype(case.kv_a) if case.kv_a is not None else F32
         ndt = weight_dtype(case.kv_a_norm)
         pool, rows = cache_append(d, case.x, case.kv_a, kdt, case.kv_a_norm, ndt, inv, rm,
-                                  case.positions, case.pool, case.table)
+                                  case.positions, case.pool, case.table, tseq)
         res["appended_rows"] = rows
     res["pool"] = pool
     q_abs64 = attention_query(case, res, model_q_abs_storage)
-    vc, lse, ps = attention_latent(d, q_abs64, pool, case.table, case.lens, sc)
+    vc, lse, ps = attention_latent(d, q_abs64, pool, case.table, case.lens, sc, tseq)
     res.update(v_combine=vc, lse=lse, p=ps)
     if case.kv_b is not None:
         o64 = None

@@ -505,3 +505,49 @@ def test_q_chain_brute_force_tiny():
     want = [sum(deq(qb, o, k) * latn[k] for k in range(ql)) for o in range(H * (N + R))]
     got = O.q_chain(d, x[None], qa, g, qb)
     assert np.allclose(got.reshape(-1), want, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# several tokens per sequence (chunked prefill / multi-token decode)
+# ----------------------------------------------------------------------------
+def _token_subcase(case, idx, pool):
+    """Tokens ``idx`` of a multi-token case as a case of their own, on ``pool``."""
+    import copy
+    sub = copy.copy(case)
+    idx = np.asarray(idx)
+    sub.batch = len(idx)
+    sub.lens = case.lens[idx]
+    sub.token_seq = case.token_seq[idx]
+    sub.pool = pool
+    for f in ("x", "q", "q_abs"):
+        v = getattr(case, f)
+        if v is not None:
+            setattr(sub, f, np.asarray(v)[idx])
+    return sub
+
+
+@pytest.mark.parametrize("cfg,prior,chunk", [(1, [5, 70], [4, 3]), (2, [64, 3], [2, 5])])
+def test_chunk_equals_token_by_token_decode(cfg, prior, chunk):
+    """A step over several new tokens per sequence gives, token by token, what
+    single-token decode steps give when run in position order: the causal
+    reading (token at position p sees rows 0..p, all rows appended first)."""
+    case = S.make_chunk_case(cfg, prior, chunk)
+    res = O.decode_step(case)
+    pool = case.pool
+    for t in range(case.batch):
+        r = O.decode_step(_token_subcase(case, [t], pool))
+        pool = r["pool"]
+        for key in ("v_combine", "lse", "out"):
+            np.testing.assert_allclose(r[key][0], res[key][t], rtol=1e-12, atol=1e-14,
+                                       err_msg=f"{key} token {t}")
+    np.testing.assert_array_equal(O.widen(pool, case.dims.cache_dtype),
+                                  O.widen(res["pool"], case.dims.cache_dtype))
+
+
+def test_chunk_token_sees_only_its_prefix():
+    """Each token's softmax spans exactly its position + 1 rows and sums to 1."""
+    case = S.make_chunk_case(1, [6], [3])
+    res = O.decode_step(case)
+    assert [p.shape[1] for p in res["p"]] == [7, 8, 9]
+    for p in res["p"]:
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-13)
