@@ -74,7 +74,8 @@ enum {
 /* ---- device status flags OR-ed by mla_cache_append (dev_status) ---- */
 enum {
   MLA_DEV_POS_RANGE = 1,  /* positions[b] < 0 or >= max_blocks_per_seq * block_size */
-  MLA_DEV_BAD_BLOCK = 2   /* block_table entry for that row is < 0 or >= num_blocks */
+  MLA_DEV_BAD_BLOCK = 2,  /* block_table entry for that row is < 0 or >= num_blocks */
+  MLA_DEV_BAD_SEQ = 4     /* mla_cache_append_tokens: token_seq[t] < 0 or >= num_seqs */
 };
 
 /* Model geometry.  W = kv_lora + qk_rope is the cache row width. */
@@ -246,6 +247,54 @@ int mla_decode_attn(const mla_dims* dims, int32_t batch, const void* q_abs,
 int mla_out_proj(const mla_dims* dims, int32_t batch, const float* v_combine,
                  const mla_weight* kv_b, const mla_weight* o_proj, float* out,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---- several tokens per sequence (chunked prefill, multi-token decode) ----
+ * moeflux gpu_matvec.rs, encode_matvec_n_tokens: one weight matrix is applied
+ * to stacked tokens, each token's arithmetic unchanged.  mla_absorb_q and
+ * mla_out_proj already take a batch of tokens (batch = tokens, positions per
+ * token); the two calls below add the token -> sequence map that the cache
+ * needs.  The pages do not describe attention over several new tokens; the
+ * reading taken: every new row is appended first, then the token at position
+ * p attends rows 0..p of its sequence (seq_lens[t] = positions[t] + 1), which
+ * is what the same tokens give one decode step at a time. */
+
+/* mla_cache_append_tokens -- mla_cache_append for n_tokens tokens that may
+ * share sequences: token t's row goes to position positions[t] of
+ * block-table row token_seq[t].
+ *   token_seq  device int32 [n_tokens], values in [0, num_seqs)
+ *   num_seqs   rows of cache->block_table (>= 1 when n_tokens > 0)
+ * Other arguments, and the row's arithmetic, are those of mla_cache_append
+ * with batch = n_tokens.  A token whose token_seq is out of range is skipped
+ * and MLA_DEV_BAD_SEQ is OR-ed into dev_status.  Two tokens naming the same
+ * (sequence, position) race.
+ * Errors: as mla_cache_append; DIMS also for num_seqs < 1 with tokens. */
+int mla_cache_append_tokens(const mla_dims* dims, int32_t n_tokens, const float* x,
+                            const mla_weight* kv_a, const mla_weight* kv_a_norm,
+                            const mla_rope* rope, const int32_t* positions,
+                            const int32_t* token_seq, int32_t num_seqs,
+                            const mla_cache* cache, int32_t* dev_status,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* mla_attn_tokens -- mla_decode_attn for n_tokens queries that may share
+ * sequences: query t attends the first seq_lens[t] rows of block-table row
+ * token_seq[t] (a causal chunk sets seq_lens[t] = positions[t] + 1).
+ *   q_abs      device [n_tokens, H, W] of cache_dtype
+ *   token_seq  device int32 [n_tokens], values in [0, num_seqs)
+ *   num_seqs   rows of cache->block_table (>= 1 when n_tokens > 0)
+ *   seq_lens   device int32 [n_tokens]
+ *   v_combine  device float [n_tokens, H, C]; lse device float
+ *              [n_tokens, H] or NULL
+ * Other arguments as mla_decode_attn with batch = n_tokens, and the
+ * workspace is mla_workspace_bytes(dims, n_tokens, max_seq_len, split_rows).
+ * A query whose token_seq is out of range gets NaN outputs, as a bad
+ * block-table entry does.  Each query is its own workgroups' work, as in
+ * decode; queries of one sequence read the same rows, mostly from L2.
+ * Errors: as mla_decode_attn; DIMS also for num_seqs < 1 with tokens. */
+int mla_attn_tokens(const mla_dims* dims, int32_t n_tokens, const void* q_abs,
+                    const mla_cache* cache, const int32_t* token_seq, int32_t num_seqs,
+                    const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                    int32_t split_rows, float* v_combine, float* lse, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* mla_validate_q8_0_kv_b -- host-side check of a Q8_0 kv_b tensor before it
  * is wrapped as an mla_weight (turbospark deepseek2/attn.rs,

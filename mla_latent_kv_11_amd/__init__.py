@@ -25,11 +25,11 @@ MLA_OK = 0
 MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE, MLA_ERR_UNSUPPORTED = -1, -2, -3, -4
 MLA_ERR_CAPACITY, MLA_ERR_WORKSPACE, MLA_ERR_HIP = -5, -6, -7
 MLA_F32, MLA_BF16, MLA_Q4G64, MLA_Q8_0 = 0, 1, 2, 3
-MLA_DEV_POS_RANGE, MLA_DEV_BAD_BLOCK = 1, 2
+MLA_DEV_POS_RANGE, MLA_DEV_BAD_BLOCK, MLA_DEV_BAD_SEQ = 1, 2, 4
 
 EXPORTED = ("mla_yarn_tables", "mla_cache_append", "mla_absorb_q", "mla_decode_attn",
-            "mla_out_proj", "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan",
-            "mla_status_str")
+            "mla_out_proj", "mla_cache_append_tokens", "mla_attn_tokens",
+            "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan", "mla_status_str")
 
 
 class MLAError(RuntimeError):
@@ -91,6 +91,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_decode_attn": ([PD, I32, P, PC, P, I32, ctypes.c_float, I32, P, P, P, SZ, P],
                             ctypes.c_int),
         "mla_out_proj": ([PD, I32, P, PW, PW, P, P, SZ, P], ctypes.c_int),
+        "mla_cache_append_tokens": ([PD, I32, P, PW, PW, PR, P, P, I32, PC, P, P, SZ, P],
+                                    ctypes.c_int),
+        "mla_attn_tokens": ([PD, I32, P, PC, P, I32, P, I32, ctypes.c_float, I32, P, P, P, SZ,
+                             P], ctypes.c_int),
         "mla_validate_q8_0_kv_b": ([I32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, I32, I32,
                                     I32, I32], ctypes.c_int),
         "mla_workspace_bytes": ([PD, I32, I32, I32], SZ),
@@ -255,6 +259,42 @@ def decode_attn(dims: Dims, q_abs, pool, table, seq_lens, max_seq_len: int,
                              ws.numel() * ws.element_size() if ws is not None else 0,
                              _stream(stream))
     _check(st, "mla_decode_attn")
+
+
+def cache_append_tokens(dims: Dims, x, kv_a: Optional[Weight], kv_a_norm: Weight, inv_freq,
+                        rope_mscale: float, positions, token_seq, pool, table, dev_status=None,
+                        ws=None, stream=None) -> None:
+    """``cache_append`` for tokens that may share sequences: token t writes
+    position ``positions[t]`` of table row ``token_seq[t]``."""
+    lib = load_library()
+    rope = CRope(_ptr(inv_freq), float(rope_mscale))
+    cache = _cache(pool, table)
+    n = int(positions.shape[0])
+    st = lib.mla_cache_append_tokens(ctypes.byref(dims.c()), n, _ptr(x),
+                                     _c_or_null(kv_a, CWeight), ctypes.byref(kv_a_norm.c()),
+                                     ctypes.byref(rope), _ptr(positions), _ptr(token_seq),
+                                     int(table.shape[0]), ctypes.byref(cache), _ptr(dev_status),
+                                     _ptr(ws),
+                                     ws.numel() * ws.element_size() if ws is not None else 0,
+                                     _stream(stream))
+    _check(st, "mla_cache_append_tokens")
+
+
+def attn_tokens(dims: Dims, q_abs, pool, table, token_seq, seq_lens, max_seq_len: int,
+                softmax_scale: float, v_combine, lse=None, split_rows: int = 0, ws=None,
+                stream=None) -> None:
+    """``decode_attn`` for queries that may share sequences: query t attends
+    the first ``seq_lens[t]`` rows of table row ``token_seq[t]``."""
+    lib = load_library()
+    cache = _cache(pool, table)
+    n = int(seq_lens.shape[0])
+    st = lib.mla_attn_tokens(ctypes.byref(dims.c()), n, _ptr(q_abs), ctypes.byref(cache),
+                             _ptr(token_seq), int(table.shape[0]), _ptr(seq_lens),
+                             int(max_seq_len), float(softmax_scale), int(split_rows),
+                             _ptr(v_combine), _ptr(lse), _ptr(ws),
+                             ws.numel() * ws.element_size() if ws is not None else 0,
+                             _stream(stream))
+    _check(st, "mla_attn_tokens")
 
 
 def out_proj(dims: Dims, v_combine, kv_b: Weight, out, o_proj: Optional[Weight] = None,

@@ -235,13 +235,16 @@ int mla_attn_plan(const mla_dims* d, int32_t B, int32_t max_len, int32_t split_r
   return plan(d, B, max_len, split_rows, rows_per_split, num_splits);
 }
 
-int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_weight* kv_a,
-                     const mla_weight* kv_a_norm, const mla_rope* rope, const int32_t* positions,
-                     const mla_cache* cache, int32_t* dev_status, void* ws, size_t ws_bytes,
-                     void* stream) {
+// token_seq null: token b owns table row b (num_seqs = B).
+static int cache_append_impl(const mla_dims* d, int32_t B, const float* x, const mla_weight* kv_a,
+                             const mla_weight* kv_a_norm, const mla_rope* rope,
+                             const int32_t* positions, const int32_t* token_seq, int32_t num_seqs,
+                             const mla_cache* cache, int32_t* dev_status, void* ws,
+                             size_t ws_bytes, void* stream) {
   int st = dims_status(d);
   if (st) return st;
   if (B < 0) return MLA_ERR_DIMS;
+  if (B > 0 && num_seqs < 1) return MLA_ERR_DIMS;
   const int W = d->kv_lora + d->qk_rope;
   if (!x || !rope || !rope->inv_freq || !positions || !cache || !cache->pool ||
       !cache->block_table)
@@ -288,6 +291,8 @@ int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_wei
   a.positions = positions;
   a.pool = cache->pool;
   a.table = cache->block_table;
+  a.q_seq = token_seq;
+  a.num_seqs = num_seqs;
   a.dev_status = dev_status;
   a.B = B;
   a.C = d->kv_lora;
@@ -298,6 +303,24 @@ int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_wei
   a.cache_dtype = d->cache_dtype;
   a.eps = d->rms_eps;
   return hip_status(launch_append_rows(a, s));
+}
+
+int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_weight* kv_a,
+                     const mla_weight* kv_a_norm, const mla_rope* rope, const int32_t* positions,
+                     const mla_cache* cache, int32_t* dev_status, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return cache_append_impl(d, B, x, kv_a, kv_a_norm, rope, positions, nullptr, B, cache,
+                           dev_status, ws, ws_bytes, stream);
+}
+
+int mla_cache_append_tokens(const mla_dims* d, int32_t n_tokens, const float* x,
+                            const mla_weight* kv_a, const mla_weight* kv_a_norm,
+                            const mla_rope* rope, const int32_t* positions,
+                            const int32_t* token_seq, int32_t num_seqs, const mla_cache* cache,
+                            int32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
+  if (!token_seq) return MLA_ERR_NULL;
+  return cache_append_impl(d, n_tokens, x, kv_a, kv_a_norm, rope, positions, token_seq, num_seqs,
+                           cache, dev_status, ws, ws_bytes, stream);
 }
 
 int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weight* q_a,
@@ -388,13 +411,15 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
   return hip_status(launch_absorb(a, s));
 }
 
-int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_cache* cache,
-                    const int32_t* seq_lens, int32_t max_len, float softmax_scale,
-                    int32_t split_rows, float* v_combine, float* lse, void* ws, size_t ws_bytes,
-                    void* stream) {
+// token_seq null: query b reads table row b (num_seqs = B).
+static int attn_impl(const mla_dims* d, int32_t B, const void* q_abs, const mla_cache* cache,
+                     const int32_t* token_seq, int32_t num_seqs, const int32_t* seq_lens,
+                     int32_t max_len, float softmax_scale, int32_t split_rows, float* v_combine,
+                     float* lse, void* ws, size_t ws_bytes, void* stream) {
   int st = dims_status(d);
   if (st) return st;
   if (B < 0 || max_len < 0) return MLA_ERR_DIMS;
+  if (B > 0 && num_seqs < 1) return MLA_ERR_DIMS;
   if (!q_abs || !cache || !cache->pool || !cache->block_table || !seq_lens || !v_combine)
     return MLA_ERR_NULL;
   if (cache->num_blocks < 1 || cache->max_blocks_per_seq < 1) return MLA_ERR_DIMS;
@@ -419,6 +444,8 @@ int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_c
   a.q_abs = q_abs;
   a.pool = cache->pool;
   a.table = cache->block_table;
+  a.q_seq = token_seq;
+  a.num_seqs = num_seqs;
   a.seq_lens = seq_lens;
   a.v_combine = v_combine;
   a.lse = lse;
@@ -445,6 +472,24 @@ int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_c
   if (st) return st;
   if (splits > 1) st = hip_status(launch_attn_combine(a, s));
   return st;
+}
+
+int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_cache* cache,
+                    const int32_t* seq_lens, int32_t max_len, float softmax_scale,
+                    int32_t split_rows, float* v_combine, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
+                   v_combine, lse, ws, ws_bytes, stream);
+}
+
+int mla_attn_tokens(const mla_dims* d, int32_t n_tokens, const void* q_abs,
+                    const mla_cache* cache, const int32_t* token_seq, int32_t num_seqs,
+                    const int32_t* seq_lens, int32_t max_len, float softmax_scale,
+                    int32_t split_rows, float* v_combine, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!token_seq) return MLA_ERR_NULL;
+  return attn_impl(d, n_tokens, q_abs, cache, token_seq, num_seqs, seq_lens, max_len,
+                   softmax_scale, split_rows, v_combine, lse, ws, ws_bytes, stream);
 }
 
 int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla_weight* kv_b,

@@ -53,7 +53,9 @@ __global__ void __launch_bounds__(64) attn_generic_kernel(AttnArgs a) {
   __syncthreads();
 
   const float* pool = static_cast<const float*>(a.pool);
-  const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+  const int sq = a.q_seq ? a.q_seq[b] : b;
+  const bool seq_ok = sq >= 0 && sq < a.num_seqs;  // else every row reads as a bad entry
+  const int32_t* trow = a.table + (size_t)(seq_ok ? sq : 0) * a.max_blocks;
   float o[kMaxCPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxCPerLane; ++i) o[i] = 0.f;
@@ -65,7 +67,7 @@ __global__ void __launch_bounds__(64) attn_generic_kernel(AttnArgs a) {
     int phys = -1;
     float s = -INFINITY;
     if (t < row_end) {
-      const int blk = trow[t / a.block];
+      const int blk = seq_ok ? trow[t / a.block] : -1;
       if (blk >= 0 && blk < a.num_blocks) {
         phys = blk * a.block + t % a.block;
         const float* row = pool + (size_t)phys * W;

@@ -113,11 +113,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   }
   const int ntiles = (row_end - row_begin + kTile - 1) / kTile;
 
-  // Physical first row of every tile of this split; -1 marks a bad table entry.
-  const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+  // Physical first row of every tile of this split; -1 marks a bad table entry
+  // (or a query whose sequence index is out of range).
+  const int sq = a.q_seq ? a.q_seq[b] : b;
+  const bool seq_ok = sq >= 0 && sq < a.num_seqs;
+  const int32_t* trow = a.table + (size_t)(seq_ok ? sq : 0) * a.max_blocks;
   for (int i = tid; i < ntiles; i += kThreads) {
     const int t0 = row_begin + i * kTile;
-    const int blk = trow[t0 / a.block];
+    const int blk = seq_ok ? trow[t0 / a.block] : -1;
     tile_base[i] = (blk >= 0 && blk < a.num_blocks) ? blk * a.block + (t0 % a.block) : -1;
   }
   // Byte offset, inside a tile of 32 consecutive rows, of granule copy k of
@@ -570,9 +573,17 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   if (h >= a.H) return;  // odd head counts: the second half-block is idle (whole waves)
   const float* lse_s = a.part_lse + (size_t)b * S * a.H + h;  // stride H over s
 
+  // A split that read a bad table entry has lse NaN, which fmaxf would drop:
+  // it makes the whole merge NaN instead.
   float m = -INFINITY;
-  for (int s = lane; s < S; s += 64) m = fmaxf(m, lse_s[(size_t)s * a.H]);
+  bool nan_lse = false;
+  for (int s = lane; s < S; s += 64) {
+    const float l = lse_s[(size_t)s * a.H];
+    m = fmaxf(m, l);
+    nan_lse |= l != l;
+  }
   m = wave_max(m);
+  if (__ballot(nan_lse) != 0) m = NAN;
   float* dst = a.v_combine + ((size_t)b * a.H + h) * a.C;
   if (m == -INFINITY) {  // empty sequence
     for (int c = c0; c < a.C; c += 512) *reinterpret_cast<f32x4_t*>(dst + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -611,8 +622,14 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   const float* exp_s = a.part_exp + (size_t)b * S * kH + h;
 
   float m = -INFINITY;
-  for (int s = lane; s < S; s += 64) m = fmaxf(m, lse_s[(size_t)s * kH]);
+  bool nan_lse = false;  // a bad table entry: NaN through the merge, as above
+  for (int s = lane; s < S; s += 64) {
+    const float l = lse_s[(size_t)s * kH];
+    m = fmaxf(m, l);
+    nan_lse |= l != l;
+  }
   m = wave_max(m);
+  if (__ballot(nan_lse) != 0) m = NAN;
   float* dst = a.v_combine + ((size_t)b * kH + h) * kC + lane * 8;
   if (m == -INFINITY) {  // empty sequence
     *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{0.f, 0.f, 0.f, 0.f};

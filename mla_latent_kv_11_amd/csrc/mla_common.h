@@ -83,15 +83,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct AttnArgs {
   const void* q_abs;        // [B, H, W] cache dtype
   const void* pool;         // [num_blocks, block, W]
-  const int32_t* table;     // [B, max_blocks]
-  const int32_t* seq_lens;  // [B]
+  const int32_t* table;     // [num_seqs, max_blocks]
+  const int32_t* q_seq;     // [B] table row of query b, or null: row b
+  const int32_t* seq_lens;  // [B] rows query b attends
   float* v_combine;         // [B, H, C]
   float* lse;               // [B, H] or null
   float* part_o;            // [B, S, H, C] fp32 partials (fp32 kernel, S > 1)
   _Float16* part_oh;        // [B, S, H, C] fp16 partials * 2^-part_exp (MFMA kernel, S > 1)
   float* part_exp;          // [B, S, H]    the exponent e of each fp16 partial
   float* part_lse;          // [B, S, H]   (S > 1)
-  int32_t B, H, C, R, block, max_blocks, num_blocks;
+  int32_t B, H, C, R, block, max_blocks, num_blocks, num_seqs;
   int32_t max_len, split_rows, num_splits;
   float scale_log2;         // softmax_scale * log2(e)
 };
@@ -164,9 +165,10 @@ struct AppendArgs {
   float rope_mscale;
   const int32_t* positions; // [B]
   void* pool;
-  const int32_t* table;
+  const int32_t* table;     // [num_seqs, max_blocks]
+  const int32_t* q_seq;     // [B] table row of token b, or null: row b
   int32_t* dev_status;
-  int32_t B, C, R, block, max_blocks, num_blocks, cache_dtype;
+  int32_t B, C, R, block, max_blocks, num_blocks, cache_dtype, num_seqs;
   float eps;
 };
 hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s);

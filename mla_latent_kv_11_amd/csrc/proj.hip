@@ -470,7 +470,12 @@ __global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
     if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_POS_RANGE);
     return;
   }
-  const int blk = a.table[(size_t)b * a.max_blocks + pos / a.block];
+  const int sq = a.q_seq ? a.q_seq[b] : b;
+  if (sq < 0 || sq >= a.num_seqs) {
+    if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_BAD_SEQ);
+    return;
+  }
+  const int blk = a.table[(size_t)sq * a.max_blocks + pos / a.block];
   if (blk < 0 || blk >= a.num_blocks) {
     if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_BAD_BLOCK);
     return;
@@ -508,7 +513,12 @@ __global__ void __launch_bounds__(256) append_rows_vec_kernel(AppendArgs a) {
     if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_POS_RANGE);
     return;
   }
-  const int blk = a.table[(size_t)b * a.max_blocks + pos / a.block];
+  const int sq = a.q_seq ? a.q_seq[b] : b;
+  if (sq < 0 || sq >= a.num_seqs) {
+    if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_BAD_SEQ);
+    return;
+  }
+  const int blk = a.table[(size_t)sq * a.max_blocks + pos / a.block];
   if (blk < 0 || blk >= a.num_blocks) {
     if (a.dev_status && threadIdx.x == 0) atomicOr(a.dev_status, (int)MLA_DEV_BAD_BLOCK);
     return;

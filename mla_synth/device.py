@@ -50,6 +50,7 @@ def stage(case: Case, device="cuda") -> types.SimpleNamespace:
     ns.table = t(case.table, device)
     ns.lens = t(case.lens.astype(np.int32), device)
     ns.positions = t(case.positions, device)
+    ns.token_seq = t(case.token_seq, device) if case.token_seq is not None else None
     ns.max_len = int(case.lens.max()) if len(case.lens) else 0
     ns.x = t(case.x, device) if case.x is not None else None
     ns.kv_a = weight(case.kv_a, d.width, d.hidden, device) if case.kv_a is not None else None
@@ -84,12 +85,32 @@ def workspace(ns, split_rows: int = 0, device="cuda") -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+def append(ns, ws, stream=None) -> None:
+    """The append call of the staged case (per-token sequence map when it has one)."""
+    if ns.token_seq is None:
+        mla.cache_append(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq, ns.rope_mscale,
+                         ns.positions, ns.pool, ns.table, ns.status, ws, stream)
+    else:
+        mla.cache_append_tokens(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq,
+                                ns.rope_mscale, ns.positions, ns.token_seq, ns.pool, ns.table,
+                                ns.status, ws, stream)
+
+
+def attend(ns, q_abs, split_rows, ws, stream=None) -> None:
+    """The attention call of the staged case (per-token sequence map when it has one)."""
+    if ns.token_seq is None:
+        mla.decode_attn(ns.dims, q_abs, ns.pool, ns.table, ns.lens, ns.max_len, ns.softmax_scale,
+                        ns.v_combine, ns.lse, split_rows, ws, stream)
+    else:
+        mla.attn_tokens(ns.dims, q_abs, ns.pool, ns.table, ns.token_seq, ns.lens, ns.max_len,
+                        ns.softmax_scale, ns.v_combine, ns.lse, split_rows, ws, stream)
+
+
 def run_step(case: Case, ns, split_rows: int = 0, ws=None, stream=None) -> None:
     """append -> absorb -> attention -> out_proj on the staged case (library calls only)."""
     ws = workspace(ns, split_rows) if ws is None else ws
     if case.appended:
-        mla.cache_append(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq, ns.rope_mscale,
-                         ns.positions, ns.pool, ns.table, ns.status, ws, stream)
+        append(ns, ws, stream)
     if ns.q_abs_given is not None:
         q_abs = ns.q_abs_given
     else:
@@ -97,8 +118,7 @@ def run_step(case: Case, ns, split_rows: int = 0, ws=None, stream=None) -> None:
         mla.absorb_q(ns.dims, q_in, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
                      ns.q_a, ns.q_a_norm, ns.q_b, ws, stream)
         q_abs = ns.q_abs
-    mla.decode_attn(ns.dims, q_abs, ns.pool, ns.table, ns.lens, ns.max_len, ns.softmax_scale,
-                    ns.v_combine, ns.lse, split_rows, ws, stream)
+    attend(ns, q_abs, split_rows, ws, stream)
     if ns.kv_b is not None:
         mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws, stream)
 
@@ -138,15 +158,12 @@ class GraphStep:
                 mla.absorb_q(ns.dims, q_in, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions,
                              ns.q_abs, ns.q_a, ns.q_a_norm, ns.q_b, self.ws_b)
         if case.appended:
-            mla.cache_append(ns.dims, ns.x, ns.kv_a, ns.kv_a_norm, ns.inv_freq, ns.rope_mscale,
-                             ns.positions, ns.pool, ns.table, ns.status, self.ws_a)
+            append(ns, self.ws_a)
         if side:
             cur.wait_stream(self.side)
 
     def attn(self):
-        ns = self.ns
-        mla.decode_attn(ns.dims, self.q_abs, ns.pool, ns.table, ns.lens, ns.max_len,
-                        ns.softmax_scale, ns.v_combine, ns.lse, self.split_rows, self.ws_a)
+        attend(self.ns, self.q_abs, self.split_rows, self.ws_a)
 
     def post(self):
         ns = self.ns

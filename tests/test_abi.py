@@ -213,3 +213,32 @@ def test_yarn_validation(lib):
     assert lib.mla_yarn_tables(None, 64, 192, None, None, None) == mla.MLA_ERR_NULL
     y0 = mla.CYarn(1.0, 40, 4096, 32, 1, 1, 1)
     assert lib.mla_yarn_tables(ctypes.byref(y0), 64, 192, None, None, None) == mla.MLA_ERR_DIMS
+
+
+def test_token_calls_validation_before_launch(lib):
+    """The several-tokens-per-sequence calls: a map is required, num_seqs must
+    cover at least one sequence when there are tokens; the rest is checked as
+    in the one-token calls.  All return before any HIP call."""
+    cache = mla.CCache(0x2000, 0x3000, 4, 2)
+
+    def attn(tseq=0x6000, nseq=2, n=3, max_len=100, q=0x1000):
+        return lib.mla_attn_tokens(ctypes.byref(DS.c()), n, q, ctypes.byref(cache), tseq, nseq,
+                                   0x4000, max_len, 0.1, 0, 0x5000, None, None, 0, None)
+    assert attn(tseq=None) == mla.MLA_ERR_NULL
+    assert attn(nseq=0) == mla.MLA_ERR_DIMS
+    assert attn(q=None) == mla.MLA_ERR_NULL
+    assert attn(max_len=129) == mla.MLA_ERR_CAPACITY
+    assert attn(n=0, nseq=0) == mla.MLA_OK
+
+    d = mla.Dims(16, 32, 16, 32, 64, hidden=0, q_lora=0, cache_dtype=mla.MLA_F32)
+    rope = mla.CRope(0x100, 1.0)
+    norm = _w(mla.MLA_F32, 1, 64)
+
+    def app(tseq=0x600, nseq=2, n=3, x=0x400):
+        return lib.mla_cache_append_tokens(ctypes.byref(d.c()), n, x, None, ctypes.byref(norm),
+                                           ctypes.byref(rope), 0x500, tseq, nseq,
+                                           ctypes.byref(cache), None, None, 0, None)
+    assert app(tseq=None) == mla.MLA_ERR_NULL
+    assert app(nseq=-1) == mla.MLA_ERR_DIMS
+    assert app(x=None) == mla.MLA_ERR_NULL
+    assert app(n=0, nseq=0) == mla.MLA_OK

@@ -453,3 +453,35 @@ def test_chain(cfg, kw):
             close_f32(got, o1, "out vs unabsorbed")
         else:
             close_bf16(got, o1, "out vs unabsorbed")
+
+
+@pytest.mark.parametrize("cfg,lens", [(4, [100, 2000]), (1, [100, 600])])
+def test_bad_table_entry_gives_nan_through_the_merge(cfg, lens):
+    """A block-table entry out of range inside a sequence's length makes that
+    sequence's outputs NaN, also when its only non-empty split is the bad one
+    and the merge sees the other splits empty; the other sequence is exact."""
+    case = S.make_case(cfg, lens=lens, paged=False)
+    ref = O.decode_step(case)
+    ns = D.stage(case)
+    bad = case.table.copy()
+    bad[0, 0] = case.pool.shape[0] + 5          # rows 0..63 of sequence 0
+    ns.table = D.t(bad)
+    q_abs = ns.q_abs_given
+    if q_abs is None:                           # fp32 case: q through the absorb
+        ws0 = D.workspace(ns)
+        D.append(ns, ws0)
+        mla.absorb_q(ns.dims, ns.q, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions,
+                     ns.q_abs, ws=ws0)
+        q_abs = ns.q_abs
+    split = 64 if cfg == 1 else 256
+    ws = D.workspace(ns, split)
+    mla.decode_attn(ns.dims, q_abs, ns.pool, ns.table, ns.lens, ns.max_len, ns.softmax_scale,
+                    ns.v_combine, ns.lse, split, ws)
+    sync()
+    assert mla.attn_plan(ns.dims, 2, ns.max_len, split)[1] > 1
+    vc, lse = host(ns.v_combine), host(ns.lse)
+    assert np.isnan(vc[0]).all() and np.isnan(lse[0]).all()
+    if case.dims.cache_dtype == O.F32:
+        close_f32(vc[1], ref["v_combine"][1], "other sequence")
+    else:
+        close_bf16(vc[1], ref["v_combine"][1], "other sequence")
