@@ -162,9 +162,9 @@ def oracle_threads():
 
 
 def time_kv_b_formats(case, torch, D, S, mla, iters=20):
-    """absorb_q and out_proj of the same layer with kv_b as 4-bit affine (MFMA
-    kernels) and as Q8_0 (read in place by the VALU kernels); HIP events around
-    ``iters`` back-to-back calls of each."""
+    """absorb_q and out_proj of the same layer with kv_b as 4-bit affine and as
+    Q8_0 (both read in place by the MFMA kernels); HIP events around ``iters``
+    back-to-back calls of each."""
     import numpy as np
     out = {}
     stream = torch.cuda.current_stream()
@@ -195,6 +195,62 @@ def time_kv_b_formats(case, torch, D, S, mla, iters=20):
                               if hasattr(kv, "packed") else np.asarray(kv).nbytes)
         out[name] = r
         del ns, ws
+    return out
+
+
+def time_tokens(torch, D, S, mla, iters=10):
+    """The whole layer (4-bit projections) over several new tokens per sequence,
+    through the token calls: multi-token decode (32 sequences x 4 tokens on
+    16380 prior rows) and a prefill chunk (4 sequences x 512 tokens on 8192
+    prior rows).  Step: HIP events around ``iters`` replays of the captured
+    step; attention: events around the attention call inside ``iters`` eager
+    steps.  Algorithmic attention bytes count each sequence's rows once."""
+    import numpy as np
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, prior, chunk in (("decode_b32_t4_L16384", [16380] * 32, 4),
+                               ("prefill_b4_t512_L8192", [8192] * 4, 512)):
+        case = S.make_chunk_case(5, prior, chunk)
+        ns = D.stage(case)
+        step = D.GraphStep(case, ns)
+        for _ in range(3):
+            step.run(eager=True)
+        step.capture()
+        for _ in range(3):
+            step.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            step.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / iters
+        ta = []
+        for _ in range(iters):
+            step.pre()
+            e0.record(stream)
+            step.attn()
+            e1.record(stream)
+            step.post()
+            torch.cuda.synchronize()
+            ta.append(e0.elapsed_time(e1))
+        ms_attn = float(np.mean(ta))
+        n = case.batch
+        rows_unique = int(np.sum(np.asarray(prior) + chunk))
+        byts = rows_unique * ROW_BYTES + n * 128 * 576 * 2 + n * 128 * 512 * 4
+        flops = int(case.lens.astype(np.int64).sum()) * ROW_FLOPS
+        t = ms_attn * 1e-3
+        out[name] = {
+            "seqs": len(prior), "tokens": n, "ms_per_step": round(ms_step, 4),
+            "tokens_per_s": round(n / (ms_step * 1e-3), 1), "attn_ms": round(ms_attn, 4),
+            "attn_tflops": round(flops / t / 1e12, 1),
+            "attn_f_mfma": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
+            "attn_gbps_unique_rows": round(byts / t / 1e9, 1),
+            "attn_f_roof": round(max(byts / (HBM_PEAK_GBS * 1e9),
+                                     flops / (BF16_PEAK_TFLOPS * 1e12)) / t, 3),
+        }
+        del step, ns
     return out
 
 
@@ -392,6 +448,7 @@ def main():
             extra[name] = time_attn_only(cfg, torch, D, S, mla, oracle=not args.no_cpu)
         line["attn_only"] = extra
         line["kv_b_formats"] = time_kv_b_formats(case, torch, D, S, mla)
+        line["several_tokens"] = time_tokens(torch, D, S, mla)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seqs)
     print(json.dumps(line), flush=True)
