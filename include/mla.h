@@ -217,7 +217,8 @@ int mla_absorb_q(const mla_dims* dims, int32_t batch, const float* q_in,
  *   max_seq_len  host: upper bound of seq_lens (sizes the split grid);
  *                values above it are clamped to it on the device
  *   softmax_scale  multiplies the fp32 scores
- *   split_rows   rows per split-K partition (multiple of 64), 0 = automatic
+ *   split_rows   rows per split-K partition (multiple of 64; at most 32768
+ *                on a bf16 cache), 0 = automatic
  *   v_combine    device float [batch, H, C], written
  *   lse          device float [batch, H] or NULL: natural-log sum of exp of
  *                the scaled scores

@@ -36,6 +36,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "mla_common.h"
 
@@ -54,10 +55,14 @@ constexpr int kThreads = 256;                 // 4 waves x 32 heads
 constexpr int kLoads = kTileGran / kThreads;  // 9 granules per thread per tile
 constexpr int kBufs = 3;
 constexpr int kTileBytes = kTileGran * 16;    // 36864
-constexpr int kMaxSplitTiles = 4096;          // 131072 rows per split
+constexpr int kMaxSplitTiles = 1024;          // 32768 rows per split
+constexpr int kQLds = 4;                      // k-blocks of the query kept in LDS (the rope part)
+constexpr int kQReg = kW / 16 - kQLds;        // k-blocks of the query kept in VGPRs
 constexpr int kPRow = 80;                     // bytes per head row of P in LDS (64 + 16 pad)
+constexpr int kPBuf = kH * kPRow;             // one P buffer; two alternate by tile parity
 constexpr size_t kSmemBytes =
-    kBufs * kTileBytes + (kMaxSplitTiles + 8) * 4 + kH * 4 + kH * kPRow + kLoads * kThreads * 4;
+    kBufs * kTileBytes + (kMaxSplitTiles + 8) * 4 + kH * 4 + 2 * kPBuf + kLoads * kThreads * 4 +
+    kQLds * kThreads * 16;
 constexpr float kRestartLog2 = 32.0f;         // restart when the max grows by > 2^32
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -76,8 +81,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   MLA_LDS int* tile_base = (MLA_LDS int*)(smem + kBufs * kTileBytes);
   MLA_LDS int* votes = tile_base + kMaxSplitTiles;         // [2][4] restart votes, by tile parity
   MLA_LDS float* l_heads = (MLA_LDS float*)(votes + 8);    // [128] softmax denominators
-  MLA_LDS char* p_lds = (MLA_LDS char*)(l_heads + kH);     // [128 heads][kPRow] bf16 P, slot order
-  MLA_LDS uint32_t* goff_lds = (MLA_LDS uint32_t*)(p_lds + kH * kPRow);  // [kLoads][256]
+  MLA_LDS char* p_lds = (MLA_LDS char*)(l_heads + kH);     // [2][128 heads][kPRow] bf16 P, slot order
+  MLA_LDS uint32_t* goff_lds = (MLA_LDS uint32_t*)(p_lds + 2 * kPBuf);  // [kLoads][256]
+  // [4 waves][kQLds][64 lanes] query fragments, in the order the lanes read them
+  MLA_LDS bf16x8_t* qpe_lds = (MLA_LDS bf16x8_t*)(goff_lds + kLoads * kThreads);
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
@@ -136,23 +143,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   }
 
   // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
-  // 16*kb + 8*hf .. +7 of the 576.
-  bf16x8_t qf[kW / 16];
+  // 16*kb + 8*hf .. +7 of the 576.  The first kQReg k-blocks stay in VGPRs;
+  // the rope k-blocks go to LDS (the register file holds O, Q and the
+  // pipeline's fragments, and no more).
+  bf16x8_t qf[kQReg];
   {
     const uint16_t* q = static_cast<const uint16_t*>(a.q_abs) + ((size_t)b * kH + head) * kW + 8 * hf;
 #pragma unroll
-    for (int kb = 0; kb < kW / 16; ++kb)
+    for (int kb = 0; kb < kQReg; ++kb)
       qf[kb] = *reinterpret_cast<const bf16x8_t*>(q + 16 * kb);
+#pragma unroll
+    for (int j = 0; j < kQLds; ++j)
+      qpe_lds[(wave * kQLds + j) * 64 + lane] = *reinterpret_cast<const bf16x8_t*>(q + 16 * (kQReg + j));
   }
   // Consume the Q loads here, so that the only vector-memory operations in
   // flight inside the tile loop are the tile copies counted by hand below.
   asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
                "v"(qf[6]), "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]),
-               "v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]), "v"(qf[16]), "v"(qf[17]));
-  asm volatile("" ::"v"(qf[18]), "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]),
-               "v"(qf[23]), "v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]),
-               "v"(qf[29]), "v"(qf[30]), "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]),
-               "v"(qf[35]));
+               "v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]));
+  asm volatile("" ::"v"(qf[16]), "v"(qf[17]), "v"(qf[18]), "v"(qf[19]), "v"(qf[20]), "v"(qf[21]),
+               "v"(qf[22]), "v"(qf[23]), "v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]),
+               "v"(qf[28]), "v"(qf[29]), "v"(qf[30]), "v"(qf[31]));
+  static_assert(kQReg == 32, "the asm above names every register-resident k-block");
   __syncthreads();
 
   const char* pool = static_cast<const char*>(a.pool);
@@ -171,21 +183,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   const uint32_t p_row = (uint32_t)(l32 * kPRow + hf * 16);  // + head block * 32 * kPRow
 
   // Source of tile i: the address of its first row (a bad table entry reads
-  // row 0 and makes the output NaN) and its last valid row; rows past it
-  // re-read that row and get probability 0.
-  auto tile_src = [&](int i, const char** src, int* rlast) {
+  // row 0 and makes the output NaN).  A tile never crosses a block, so all its
+  // 32 rows lie inside the pool even where the split ends first.
+  auto tile_src = [&](int i) -> const char* {
     const int base = __builtin_amdgcn_readfirstlane(tile_base[i]);
-    *src = pool + (size_t)(base < 0 ? 0 : base) * (kW * 2);
-    const int t0 = row_begin + i * kTile;
-    *rlast = (t0 + kTile <= row_end) ? kTile - 1 : row_end - 1 - t0;
+    return pool + (size_t)(base < 0 ? 0 : base) * (kW * 2);
   };
   // Copy granule k of tile i: 16 bytes per lane straight into LDS at
   // M0 + 16 * lane.  Issued from asm so that the compiler does not treat every
   // later LDS read as aliasing the copy; the explicit vmcnt waits order them.
-  auto clamp_rows = [&](uint32_t off, int rlast) {  // rows past rlast re-read row rlast
-    const int r = (int)(off / (kW * 2));
-    return r > rlast ? off - (uint32_t)((r - rlast) * (kW * 2)) : off;
-  };
   auto issue_load = [&](int i, int k, uint32_t off, const char* src) {
     const uint32_t lds = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes + (k * 4 + wave) * 1024);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -193,37 +199,45 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
                  : "v"(off), "s"(src), "s"(lds)
                  : "memory");
   };
+  // Tiles past the split's end (the pipeline's look-ahead) re-read the pool's
+  // first 32 rows into the buffer they would use.
   auto issue_tile = [&](int i) {
-    const char* src;
-    int rlast;
-    tile_src(i, &src, &rlast);
+    const char* src = i < ntiles ? tile_src(i) : pool;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) issue_load(i, k, goff_lds[k * kThreads + tid], src);
+  };
+  // Rows of tile i past the split's end hold whatever the pool has there
+  // (possibly NaN).  They get probability 0, but 0 * NaN would still reach O
+  // through P*V, so once this wave's copies of the tile have landed it
+  // overwrites its own granules of those rows with zeros; the barrier that
+  // publishes the tile follows.  Once per split at most.
+  auto zero_tail = [&](int i) {
+    const int t0 = row_begin + i * kTile;
+    if (i >= ntiles || t0 + kTile <= row_end) return;
+    const int rlast = row_end - 1 - t0;
+    MLA_LDS char* buf = tiles + (i % kBufs) * kTileBytes;
+    int slot = wave * 64 + lane;
+    asm volatile("" : "+v"(slot));  // computed here, not kept live across the tile loop
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
-      uint32_t off = goff_lds[k * kThreads + tid];
-      if (rlast < kTile - 1) off = clamp_rows(off, rlast);
-      issue_load(i, k, off, src);
+      if ((slot + k * 256) / kGran > rlast)
+        *(MLA_LDS f32x4_t*)(buf + (slot + k * 256) * 16) = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
 
-  f32x16_t o[kC / 32];
-#pragma unroll
-  for (int cb = 0; cb < kC / 32; ++cb) o[cb] = f32x16_t{};
+  f32x16_t o[kC / 32];  // cleared by MFMAs at every (re)start
   // p = 2^(s*scale*log2e - m_ref) with a per-head reference m_ref taken from
   // the first tile.  If a later tile's maximum exceeds it by more than
   // kRestartLog2 (p would leave the safe range), the workgroup restarts the
-  // split with the largest maximum seen as the new reference.  The restart
-  // never touches O in registers: the next accumulation simply takes C = 0.
+  // split with the largest maximum seen as the new reference.  O is never
+  // rescaled or cleared: the first P*V after every (re)start takes C = 0.
   const float c = a.scale_log2;
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;
   float l_run = 0.f;
   bool bad = false;
-  bool pending = false;
-  bool fresh = true;     // the next tile is the first since the (re)start
-  int zero_c = 0;        // 1: the next accumulation starts from C = 0
+  bool fresh = true;  // the next tile is the first since the (re)start
 
-  issue_tile(0);
-  if (ntiles > 1) issue_tile(1);
   // K fragment of k-block kb: base qa[kb & 3] of the tile, + (kb >> 2) * 128.
   // The bases are made opaque so that the constant offsets fold into the
   // reads instead of becoming 36 hoisted addresses.
@@ -237,120 +251,128 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   auto kaddr = [&](const uint32_t* qa, int kb) {
     return (const MLA_LDS bf16x8_t*)(uintptr_t)(qa[kb & 3] + (kb >> 2) * 128);
   };
-  bf16x8_t kf[5];  // K fragments of the next five k-blocks
-  // Iteration ntiles only collects the last tile's restart vote.
-  for (int i = 0; i <= ntiles; ++i) {
-    // Tile i > 0 was waited for before the previous tile's P barrier.
-    if (i + 1 >= ntiles) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else if (i == 0) {
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 (tile 1's copies are newer)
-    }
-    if (lane == 0) votes[(i & 1) * 4 + wave] = __ballot(pending) != 0;
-    __syncthreads();
-    bool restart;
-    {
-      const MLA_LDS int* v = votes + (i & 1) * 4;
-      restart = (v[0] | v[1] | v[2] | v[3]) != 0;
-    }
-    if (restart) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      m_ref = m_seen;
-      l_run = 0.f;
-      pending = false;
-      fresh = true;
-      zero_c = 1;
-      issue_tile(0);
-      if (ntiles > 1) issue_tile(1);
-      i = -1;
-      continue;
-    }
-    if (i == ntiles) break;
-    bad |= tile_base[i] < 0;
-    // Copies of tile i + 2 go out between the score MFMAs.  Past the split's
-    // end they still go out (no branch in the MFMA sequence): they re-read the
-    // pool's first 32 rows into the idle third buffer, and the vmcnt(0) at
-    // the top of the last passes drains them.
+  // V^T fragment for this wave's column block 4*wave + cbl and k-block kb:
+  // two transpose reads of 4 rows x 4 columns each.
+  auto vread = [&](const uint32_t* va, int cbl, int kb) {
+    const uint32_t off = kb * (16 * kGran * 16) + (cbl >> 1) * 128;
+    const s16x4_t lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4_t*)(uintptr_t)(va[(cbl & 1) * 2] + off));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MLA_LDS s16x4_t*)(uintptr_t)(va[(cbl & 1) * 2 + 1] + off));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  // V^T fragments of the tile whose P*V comes next (column blocks 4*wave ..
+  // +3 as (cb >> 1) = 2*wave + (cbl >> 1), cb & 1 = cbl & 1; two k-blocks).
+  s16x8_t vf[2][4];
+
+  // One MFMA phase of the pipeline, after the barrier that published tile
+  // `it` and the P of tile it - 1:
+  //   scores of tile it: S^T = K Q^T, 36 MFMAs in one accumulator chain;
+  //   P*V of tile it - 1 (kMode > 0): O^T += V^T P^T, 32 MFMAs, one between
+  //     every two score MFMAs, so neither chain waits on its own results;
+  //     head block outer, so one P fragment serves four MFMAs in a row;
+  //   the nine copies of tile it + 2 into the buffer tile it - 1 has left;
+  //   the V^T fragments of tile it, each read as soon as the P*V MFMAs of
+  //     tile it - 1 are done with its registers.
+  // kMode 0: no P*V (the first tile of a (re)start); 1: the first P*V after
+  // a (re)start, whose first k-block starts from C = 0; 2: steady state.
+  // Tiles past the split's end are read and scored like any other (their
+  // copies re-read the pool's first rows into the free buffer) and their
+  // scores are dropped, so the sequence has no branch.
+  auto mfma_phase = [&](auto mode, int it) -> f32x16_t {
+    constexpr int kMode = decltype(mode)::value;
+    const uint32_t tile = tiles_lds + (uint32_t)((it % kBufs) * kTileBytes);
     const char* nsrc = pool;
-    int nrlast = kTile - 1;
-    uint32_t noff[kLoads];
+    if (it + 2 < ntiles) nsrc = tile_src(it + 2);
+    uint32_t qa[4];
+    kbases(tile, qa);
+    uint32_t va[4];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) noff[k] = goff_lds[k * kThreads + tid];
-    if (i + 2 < ntiles) {
-      tile_src(i + 2, &nsrc, &nrlast);
-      if (nrlast < kTile - 1) {  // the split's last tile: once per split
+    for (int c1 = 0; c1 < 2; ++c1)
 #pragma unroll
-        for (int k = 0; k < kLoads; ++k) noff[k] = clamp_rows(noff[k], nrlast);
-      }
+      for (int rr = 0; rr < 2; ++rr)
+        va[c1 * 2 + rr] = tile + (((pv0 ^ (uint32_t)(64 * c1)) ^ (uint32_t)(32 * rr)) + 9216u * rr) +
+                          (uint32_t)(wave * 256);
+    const uint32_t pbuf = p_row + (uint32_t)(((it - 1) & 1) * kPBuf);
+    auto pread = [&](int x, int kb) {
+      return *(const MLA_LDS bf16x8_t*)(p_lds + pbuf + x * (32 * kPRow) + kb * 32);
+    };
+    bf16x8_t kf[3];
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) kf[kb] = *kaddr(qa, kb);
+    bf16x8_t pf[2];  // P fragments (k-block, head block) in MFMA order, two in flight
+    if (kMode > 0) {
+      pf[0] = pread(0, 0);
+      pf[1] = pread(1, 0);
     }
-
-    const uint32_t tile = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes);
-
-    // ---- scores S^T (rows x heads): two accumulators (even / odd k-block),
-    // K fragments read five k-blocks ahead; the next tile's copies are issued
-    // between the MFMAs ----
+    uint32_t noff = goff_lds[tid];
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t qp[kQLds];  // the LDS-resident query k-blocks, read in the phase's last quarter
+    const MLA_LDS bf16x8_t* qsrc = qpe_lds + wave * (kQLds * 64) + lane;
+    // The score MFMAs are asm too (an exact-register accumulate chain needs
+    // no wait states between its links), which keeps the compiler from moving
+    // the resident query between registers around the P*V asm.
     f32x16_t s;
-    {
-      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-      uint32_t qa[4];
-      kbases(tile, qa);
-      if (i == 0) {  // otherwise read during the previous tile's P*V
 #pragma unroll
-        for (int kb = 0; kb < 5; ++kb) kf[kb] = *kaddr(qa, kb);
+    for (int n = 0; n < kW / 16; ++n) {
+      const bf16x8_t qn = n < kQReg ? qf[n < kQReg ? n : 0] : qp[n < kQReg ? 0 : n - kQReg];
+      if (n == 0)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(kf[0]), "v"(qn));
+      else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[n % 3]), "v"(qn));
+      if (n + 3 < kW / 16) kf[n % 3] = *kaddr(qa, n + 3);
+      if (n >= 24 && n < 24 + 2 * kQLds && (n & 1) == 0) qp[(n - 24) >> 1] = qsrc[((n - 24) >> 1) * 64];
+      if (n < 32) {
+        // n = kb*16 + hb*4 + cbl
+        const int kb = n >> 4, hb = (n >> 2) & 3, cbl = n & 3, f = (n >> 2) & 1;
+        if (kMode == 1 && kb == 0) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                       : "+a"(o[cbl * 4 + hb])
+                       : "v"(vf[0][cbl]), "v"(pf[f]));
+        } else if (kMode > 0) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+a"(o[cbl * 4 + hb])
+                       : "v"(vf[kb][cbl]), "v"(pf[f]));
+        }
+        // the P fragment two steps on replaces the one just finished
+        if (kMode > 0 && cbl == 3 && n + 8 < 32) pf[f] = pread(((n >> 2) + 2) & 3, (n + 8) >> 4);
+        // vf[kb][cbl] is free after the last head block: read tile it's fragment
+        if (hb == 3) vf[kb][cbl] = vread(va, cbl, kb);
       }
-#pragma unroll
-      for (int kb = 0; kb < kW / 16; ++kb) {
-        if (kb & 1)
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 5], qf[kb], s1, 0, 0, 0);
-        else
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 5], qf[kb], s0, 0, 0, 0);
-        if (kb + 5 < kW / 16) kf[kb % 5] = *kaddr(qa, kb + 5);
-        if ((kb & 3) == 3) issue_load(i + 2, kb >> 2, noff[kb >> 2], nsrc);
-        __builtin_amdgcn_sched_barrier(0);
+      if ((n & 3) == 3) {  // copy n / 4 of tile it + 2; the next copy's offset
+        const int k = n >> 2;
+        const uint32_t off = noff;
+        if (k + 1 < kLoads) noff = goff_lds[(k + 1) * kThreads + tid];
+        issue_load(it + 2, k, off, nsrc);
       }
-      s = s0 + s1;
-    }
-
-    // ---- V^T fragments for this wave's 128 latent columns (column blocks
-    // 4*wave .. +3: (cb >> 1) = 2*wave + (cbl >> 1), cb & 1 = cbl & 1).  They do
-    // not depend on P, so they are read now and land while the softmax runs. ----
-    s16x8_t vf[2][4];
-    {
-      uint32_t va[2][2];
-#pragma unroll
-      for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-          va[c1][rr] = tile + (((pv0 ^ (uint32_t)(64 * c1)) ^ (uint32_t)(32 * rr)) + 9216u * rr) +
-                       (uint32_t)(wave * 256);
-      auto vread = [&](int cbl, int kb) {
-        const uint32_t off = kb * (16 * kGran * 16) + (cbl >> 1) * 128;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][0] + off));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (MLA_LDS s16x4_t*)(uintptr_t)(va[cbl & 1][1] + off));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) vf[kb][x] = vread(x, kb);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // VALU reads of an MFMA result wait 18 cycles after a 16-pass MFMA; the
+    // compiler does not see into asm, so pad here
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
+    return s;
+  };
 
-    // ---- softmax numerators: lane = head, 16 rows per lane (the rest in lane ^ 32) ----
-    const int t0 = row_begin + i * kTile;
-    const bool tail = t0 + kTile > row_end;
+  // Softmax numerators of tile it (lane = head, 16 rows per lane, the rest in
+  // lane ^ 32), written as bf16 into P buffer it & 1 in slot order: head row h
+  // holds slot kb*16 + hf*8 + j <-> row 16*kb + 8*(j/4) + 4*hf + j%4, the
+  // order both MFMA operands of P*V use.  The denominator sums the fp32
+  // numerators (so lse stays exact to fp32, independent of the split plan).
+  // Returns whether this lane's maximum left the reference's safe range.
+  auto softmax = [&](f32x16_t s, int it) -> bool {
+    bad |= tile_base[it] < 0;
+    // row (j >> 2) * 8 + (j & 3) + 4 * hf of the tile is valid iff that is < lim
+    const int lim = row_end - (row_begin + it * kTile);
+    const bool tail = lim < kTile;
     if (tail) {  // rows past the end do not take part in the maximum
+      int l = lim - 4 * hf;
+      asm volatile("" : "+v"(l));  // formed here, on the split's last tile only
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int t = t0 + (j >> 2) * 8 + hf * 4 + (j & 3);
-        s[j] = t < row_end ? s[j] : __builtin_nanf("");
-      }
+      for (int j = 0; j < 16; ++j) s[j] = (j >> 2) * 8 + (j & 3) < l ? s[j] : __builtin_nanf("");
     }
-    // extreme of the raw scores (max for a positive scale, min for a negative one);
-    // fmax/fmin ignore the NaN of masked rows
+    // extreme of the raw scores (max for a positive scale, min for a negative
+    // one); fmax/fmin ignore the NaN of masked rows
     float e;
     if (c >= 0.f) {
       e = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
@@ -371,112 +393,93 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     m_seen = fmaxf(m_seen, mt);
     if (fresh) m_ref = fmaxf(m_ref, mt);
     fresh = false;
-    pending = mt > m_ref + kRestartLog2;
-
-    // This lane's 16 numerators, bf16, into the shared P in slot order: head
-    // row h holds slot kb*16 + hf*8 + j <-> row 16*kb + 8*(j/4) + 4*hf + j%4,
-    // the order both MFMA operands of P*V use.  The denominator sums the fp32
-    // numerators (so lse stays exact to fp32, independent of the split plan).
-    {
-      float p[16];
+    float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c, -m_ref));
-      if (tail) {
+    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c, -m_ref));
+    if (tail) {
+      int l = lim - 4 * hf;
+      asm volatile("" : "+v"(l));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int t = t0 + (j >> 2) * 8 + hf * 4 + (j & 3);
-          p[j] = t < row_end ? p[j] : 0.f;
-        }
-      }
-      bf16x8_t pb[2];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)p[j];
-      float q0 = (p[0] + p[1]) + (p[2] + p[3]), q1 = (p[4] + p[5]) + (p[6] + p[7]);
-      float q2 = (p[8] + p[9]) + (p[10] + p[11]), q3 = (p[12] + p[13]) + (p[14] + p[15]);
-      l_run += (q0 + q1) + (q2 + q3);
-      MLA_LDS char* prow = p_lds + p_row + wave * (32 * kPRow);
-      *(MLA_LDS bf16x8_t*)prow = pb[0];
-      *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
+      for (int j = 0; j < 16; ++j) p[j] = (j >> 2) * 8 + (j & 3) < l ? p[j] : 0.f;
     }
-    // this wave's copies of tile i + 1 (all but the newest kLoads) have landed
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    __syncthreads();  // every head's P is visible, and so is tile i + 1
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)p[j];
+    float q0 = (p[0] + p[1]) + (p[2] + p[3]), q1 = (p[4] + p[5]) + (p[6] + p[7]);
+    float q2 = (p[8] + p[9]) + (p[10] + p[11]), q3 = (p[12] + p[13]) + (p[14] + p[15]);
+    l_run += (q0 + q1) + (q2 + q3);
+    MLA_LDS char* prow = p_lds + p_row + (uint32_t)((it & 1) * kPBuf) + wave * (32 * kPRow);
+    *(MLA_LDS bf16x8_t*)prow = pb[0];
+    *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
+    return mt > m_ref + kRestartLog2;
+  };
 
-    // ---- O^T += V^T P^T for this wave's 128 latent columns and all 128 heads:
-    // V is read from LDS once per workgroup ----
-    {
-      bf16x8_t pf[2][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {  // the first half's fragments first
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          pf[kb][x] = *(const MLA_LDS bf16x8_t*)(p_lds + p_row + x * (32 * kPRow) + kb * 32);
-        __builtin_amdgcn_sched_barrier(0);
+  // The pipeline, per (re)start: tiles 0 and 1 are copied, then phase it
+  // (it = 0 .. ntiles) runs the MFMAs of tile it's scores and tile it - 1's
+  // P*V, and tile it's softmax follows.  One barrier per tile publishes its
+  // P, its restart vote and tile it + 1 (whose copies this wave waits for
+  // just before it: the nine newer copies are tile it + 2's).  Buffers: tile
+  // it + 2 goes into the buffer of tile it - 1, whose K and V^T reads all
+  // ended before that barrier; P alternates between two buffers, so the
+  // barrier of tile it also separates the P*V reads of tile it - 1 from the
+  // writes of tile it + 1.  A restart vote is read after the barrier and
+  // acted on after the next MFMA phase (its P*V is then discarded).
+  const bf16x8_t zf = bf16x8_t{};
+  for (;;) {
+    // O = 0 at every (re)start: 0 x 0 + 0 for each 32 x 32 block
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %2, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %3, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %4, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %5, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %6, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %7, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %8, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %9, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %10, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %11, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %12, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %13, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %14, %16, %16, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %15, %16, %16, 0"
+        : "=a"(o[0]), "=a"(o[1]), "=a"(o[2]), "=a"(o[3]), "=a"(o[4]), "=a"(o[5]),
+          "=a"(o[6]), "=a"(o[7]), "=a"(o[8]), "=a"(o[9]), "=a"(o[10]), "=a"(o[11]),
+          "=a"(o[12]), "=a"(o[13]), "=a"(o[14]), "=a"(o[15])
+        : "v"(zf));
+    issue_tile(0);
+    issue_tile(1);
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 (tile 1's copies are newer)
+    zero_tail(0);
+    __syncthreads();
+    f32x16_t s = mfma_phase(std::integral_constant<int, 0>{}, 0);
+    bool pending = softmax(s, 0);
+    bool restart = false;
+    for (int it = 1;; ++it) {
+      if (lane == 0) votes[((it - 1) & 1) * 4 + wave] = __ballot(pending) != 0;
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's copies of tile it
+      zero_tail(it);
+      __syncthreads();
+      int vote;
+      {
+        const MLA_LDS int* v = votes + ((it - 1) & 1) * 4;
+        vote = v[0] | v[1] | v[2] | v[3];
       }
-      // first k-block, 16 MFMAs in one block; C = 0 right after a restart
-      // (one uniform branch per tile)
-      asm volatile(
-          "s_cmp_eq_u32 %24, 0\n\t"
-          "s_cbranch_scc1 1f\n\t"
-          "v_mfma_f32_32x32x16_bf16 %0, %16, %20, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %1, %16, %21, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %2, %16, %22, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %3, %16, %23, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %4, %17, %20, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %5, %17, %21, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %6, %17, %22, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %7, %17, %23, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %8, %18, %20, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %9, %18, %21, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %10, %18, %22, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %11, %18, %23, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %12, %19, %20, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %13, %19, %21, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %14, %19, %22, 0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %15, %19, %23, 0\n\t"
-          "s_branch 2f\n"
-          "1:\n\t"
-          "v_mfma_f32_32x32x16_bf16 %0, %16, %20, %0\n\t"
-          "v_mfma_f32_32x32x16_bf16 %1, %16, %21, %1\n\t"
-          "v_mfma_f32_32x32x16_bf16 %2, %16, %22, %2\n\t"
-          "v_mfma_f32_32x32x16_bf16 %3, %16, %23, %3\n\t"
-          "v_mfma_f32_32x32x16_bf16 %4, %17, %20, %4\n\t"
-          "v_mfma_f32_32x32x16_bf16 %5, %17, %21, %5\n\t"
-          "v_mfma_f32_32x32x16_bf16 %6, %17, %22, %6\n\t"
-          "v_mfma_f32_32x32x16_bf16 %7, %17, %23, %7\n\t"
-          "v_mfma_f32_32x32x16_bf16 %8, %18, %20, %8\n\t"
-          "v_mfma_f32_32x32x16_bf16 %9, %18, %21, %9\n\t"
-          "v_mfma_f32_32x32x16_bf16 %10, %18, %22, %10\n\t"
-          "v_mfma_f32_32x32x16_bf16 %11, %18, %23, %11\n\t"
-          "v_mfma_f32_32x32x16_bf16 %12, %19, %20, %12\n\t"
-          "v_mfma_f32_32x32x16_bf16 %13, %19, %21, %13\n\t"
-          "v_mfma_f32_32x32x16_bf16 %14, %19, %22, %14\n\t"
-          "v_mfma_f32_32x32x16_bf16 %15, %19, %23, %15\n\t"
-          "2:"
-          : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
-            "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
-            "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
-          : "v"(vf[0][0]), "v"(vf[0][1]), "v"(vf[0][2]), "v"(vf[0][3]), "v"(pf[0][0]),
-            "v"(pf[0][1]), "v"(pf[0][2]), "v"(pf[0][3]), "s"(zero_c)
-          : "scc");
-      __builtin_amdgcn_sched_barrier(0);
-      // the first K fragments of tile i + 1 go out between the second half's
-      // MFMAs, where the first half's fragments are dead
-      uint32_t nqa[4];
-      kbases(tiles_lds + (uint32_t)(((i + 1) % kBufs) * kTileBytes), nqa);
-#pragma unroll
-      for (int cbl = 0; cbl < 4; ++cbl)
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                       : "+a"(o[cbl * 4 + hb])
-                       : "v"(vf[1][cbl]), "v"(pf[1][hb]));
-          const int n = cbl * 4 + hb;
-          if (n % 3 == 0 && n / 3 < 5) kf[n / 3] = *kaddr(nqa, n / 3);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      s = mfma_phase(std::integral_constant<int, 2>{}, it);
+      if (vote != 0) {
+        restart = true;
+        break;
+      }
+      if (it == ntiles) break;
+      pending = softmax(s, it);
     }
-    zero_c = 0;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!restart) break;
+    __syncthreads();  // every wave's copies have landed before the buffers are reused
+    m_ref = m_seen;
+    l_run = 0.f;
+    fresh = true;
   }
 
   // The last accumulate MFMAs may still be in flight: pad before reading O.

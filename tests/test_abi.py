@@ -88,10 +88,11 @@ def test_plan_and_workspace(lib):
     assert mla.workspace_bytes(DS, 1, 100, 64 * 3) >= 0
     with pytest.raises(mla.MLAError):
         mla.attn_plan(DS, 1, 100, 65)
-    # the bf16 kernel's largest split is 131072 rows (4096 tiles); one more block is refused
-    assert mla.attn_plan(DS, 1, 131072, 131072) == (131072, 1)
+    # the bf16 kernel's largest split is 32768 rows (1024 tiles); one more block is refused
+    assert mla.attn_plan(DS, 1, 32768, 32768) == (32768, 1)
+    assert mla.attn_plan(DS, 1, 131072, 32768) == (32768, 4)
     with pytest.raises(mla.MLAError):
-        mla.attn_plan(DS, 1, 131072 + 64, 131072 + 64)
+        mla.attn_plan(DS, 1, 32768 + 64, 32768 + 64)
 
 
 def test_weight_validation(lib):
