@@ -101,13 +101,18 @@ def oracle_attn_seconds(case):
     return time.perf_counter() - t0
 
 
-def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50, oracle=True):
+def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50, oracle=True, lens_plan=False):
     """Attention call alone on a full-size configuration (q_abs given or absorbed
     once): hot (back-to-back calls) and cold (cache evicted before each call),
-    and the oracle's attention on the same inputs."""
+    and the oracle's attention on the same inputs.  ``lens_plan``: also the
+    split plan sized from the host-side lengths (mla_attn_plan_lens)."""
     case = S.make_case(cfg)
     ns = D.stage(case)
     ws = D.workspace(ns)
+    r_lens = mla.attn_plan_lens(ns.dims, case.lens)[0] if lens_plan else 0
+    if r_lens:
+        ws_l = D.workspace(ns, r_lens)
+        ws = ws if ws.numel() >= ws_l.numel() else ws_l
     if ns.q_abs_given is not None:
         q_abs = ns.q_abs_given
     else:
@@ -115,41 +120,48 @@ def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50, oracle=True):
                      ws=ws)
         q_abs = ns.q_abs
     stream = torch.cuda.current_stream()
-
-    def call():
-        mla.decode_attn(ns.dims, q_abs, ns.pool, ns.table, ns.lens, ns.max_len,
-                        ns.softmax_scale, ns.v_combine, ns.lse, 0, ws)
-    for _ in range(warm):
-        call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(iters):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
-    ms_cold = cold_call_ms(torch, call, stream)
     rows = int(case.lens.sum())
     byts, flops = attn_alg(case.batch, rows)
-    t = ms * 1e-3
-    out = {
-        "batch": case.batch, "rows": rows, "ms": round(ms, 4), "ms_cold": round(ms_cold, 4),
-        "gbps": round(byts / t / 1e9, 1), "tflops": round(flops / t / 1e12, 1),
-        "f_hbm": round(byts / t / 1e9 / HBM_PEAK_GBS, 3),
-        "f_mfma": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
-        "f_roof": round(max(byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)) / t, 3),
-        "tokens_per_s": round(case.batch / t, 1),
-        "f_roof_cold": round(max(byts / (HBM_PEAK_GBS * 1e9),
-                                 flops / (BF16_PEAK_TFLOPS * 1e12)) / (ms_cold * 1e-3), 3),
-    }
+
+    def measure(split_rows):
+        def call():
+            mla.decode_attn(ns.dims, q_abs, ns.pool, ns.table, ns.lens, ns.max_len,
+                            ns.softmax_scale, ns.v_combine, ns.lse, split_rows, ws)
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        ms_cold = cold_call_ms(torch, call, stream)
+        t = ms * 1e-3
+        return {
+            "split_rows": mla.attn_plan(ns.dims, case.batch, ns.max_len, split_rows)[0],
+            "ms": round(ms, 4), "ms_cold": round(ms_cold, 4),
+            "gbps": round(byts / t / 1e9, 1), "tflops": round(flops / t / 1e12, 1),
+            "f_hbm": round(byts / t / 1e9 / HBM_PEAK_GBS, 3),
+            "f_mfma": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
+            "f_roof": round(max(byts / (HBM_PEAK_GBS * 1e9),
+                                flops / (BF16_PEAK_TFLOPS * 1e12)) / t, 3),
+            "tokens_per_s": round(case.batch / t, 1),
+            "f_roof_cold": round(max(byts / (HBM_PEAK_GBS * 1e9),
+                                     flops / (BF16_PEAK_TFLOPS * 1e12)) / (ms_cold * 1e-3), 3),
+        }
+    out = {"batch": case.batch, "rows": rows, **measure(0)}
+    if r_lens:
+        out["plan_from_lengths"] = measure(r_lens)
     del ns, ws
     if oracle:
         sec = oracle_attn_seconds(case)
         out["oracle"] = {"seconds": round(sec, 3), "rows_per_s": round(rows / sec, 1),
                          "gbps_equiv": round(byts / sec / 1e9, 3),
                          "tokens_per_s": round(case.batch / sec, 3),
-                         "gpu_speedup": round(sec / t, 1), "cores": oracle_threads()}
+                         "gpu_speedup": round(sec / (out["ms"] * 1e-3), 1),
+                         "cores": oracle_threads()}
     return out
 
 
@@ -445,7 +457,8 @@ def main():
     if not args.no_extra:
         extra = {}
         for cfg, name in ((2, "b1_L4096"), (3, "b64_L1024-8192_paged"), (4, "b4_L131072")):
-            extra[name] = time_attn_only(cfg, torch, D, S, mla, oracle=not args.no_cpu)
+            extra[name] = time_attn_only(cfg, torch, D, S, mla, oracle=not args.no_cpu,
+                                         lens_plan=(cfg == 3))
         line["attn_only"] = extra
         line["kv_b_formats"] = time_kv_b_formats(case, torch, D, S, mla)
         line["several_tokens"] = time_tokens(torch, D, S, mla)

@@ -318,6 +318,20 @@ int mla_attn_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
                   int32_t split_rows, int32_t* rows_per_split,
                   int32_t* num_splits);
 
+/* A split-K plan for a batch whose lengths the caller knows on the host
+ * (host_lens, int32 [batch], each >= 0): the smallest split (a multiple of 64
+ * rows, at least 256) whose non-empty workgroups fit one per compute unit of
+ * the current device.  Pass *rows_per_split as split_rows to mla_decode_attn
+ * or mla_attn_tokens (and to mla_workspace_bytes).  A ragged batch then runs
+ * as one wave of workgroups of nearly equal size; the automatic plan sizes
+ * every split for the longest sequence.  Falls back to the automatic plan of
+ * the longest length when no split fits.  The flash-decoding split itself is
+ * the long-context step of the pages' MLA decode (turbospark deepseek2
+ * attn.rs; moeflux mla_attn_forward.rs, SDPA over the latent cache).
+ * Errors: NULL, DIMS (a negative length), UNSUPPORTED. */
+int mla_attn_plan_lens(const mla_dims* dims, int32_t batch, const int32_t* host_lens,
+                       int32_t* rows_per_split, int32_t* num_splits);
+
 /* Human-readable text for a status code (static storage). */
 const char* mla_status_str(int status);
 

@@ -29,7 +29,8 @@ MLA_DEV_POS_RANGE, MLA_DEV_BAD_BLOCK, MLA_DEV_BAD_SEQ = 1, 2, 4
 
 EXPORTED = ("mla_yarn_tables", "mla_cache_append", "mla_absorb_q", "mla_decode_attn",
             "mla_out_proj", "mla_cache_append_tokens", "mla_attn_tokens",
-            "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan", "mla_status_str")
+            "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan",
+            "mla_attn_plan_lens", "mla_status_str")
 
 
 class MLAError(RuntimeError):
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_workspace_bytes": ([PD, I32, I32, I32], SZ),
         "mla_attn_plan": ([PD, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
                           ctypes.c_int),
+        "mla_attn_plan_lens": ([PD, I32, P, ctypes.POINTER(I32), ctypes.POINTER(I32)],
+                               ctypes.c_int),
         "mla_status_str": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -214,6 +217,19 @@ def attn_plan(dims: Dims, batch: int, max_seq_len: int, split_rows: int = 0):
     r, s = ctypes.c_int32(), ctypes.c_int32()
     _check(load_library().mla_attn_plan(ctypes.byref(dims.c()), batch, max_seq_len, split_rows,
                                         ctypes.byref(r), ctypes.byref(s)), "mla_attn_plan")
+    return r.value, s.value
+
+
+def attn_plan_lens(dims: Dims, lens) -> tuple:
+    """(rows per split, splits per sequence) sized from host-side lengths: the
+    smallest split whose non-empty workgroups fit one per compute unit."""
+    import numpy as _np
+    arr = _np.ascontiguousarray(_np.asarray(lens, dtype=_np.int32))
+    r, s = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().mla_attn_plan_lens(ctypes.byref(dims.c()), int(arr.shape[0]),
+                                             arr.ctypes.data_as(ctypes.c_void_p),
+                                             ctypes.byref(r), ctypes.byref(s)),
+           "mla_attn_plan_lens")
     return r.value, s.value
 
 

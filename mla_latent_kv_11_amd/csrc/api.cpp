@@ -235,6 +235,39 @@ int mla_attn_plan(const mla_dims* d, int32_t B, int32_t max_len, int32_t split_r
   return plan(d, B, max_len, split_rows, rows_per_split, num_splits);
 }
 
+// Split plan from the lengths themselves (host copies): the smallest split
+// (a multiple of 64, at least 256 rows) whose non-empty workgroups,
+// sum_b ceil(len_b / rows), fit one per compute unit, so that a ragged batch
+// runs as one wave of workgroups of about equal size instead of splits sized
+// for its longest sequence.  If even the largest split needs more workgroups
+// than there are compute units, the automatic plan for the longest length.
+int mla_attn_plan_lens(const mla_dims* d, int32_t B, const int32_t* host_lens,
+                       int32_t* rows_per_split, int32_t* num_splits) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (!rows_per_split || !num_splits || (B > 0 && !host_lens)) return MLA_ERR_NULL;
+  if (B < 0) return MLA_ERR_DIMS;
+  int32_t max_len = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (host_lens[b] < 0) return MLA_ERR_DIMS;
+    max_len = host_lens[b] > max_len ? host_lens[b] : max_len;
+  }
+  const int64_t cus = device_cus();
+  auto workgroups = [&](int64_t r) {
+    int64_t n = 0;
+    for (int32_t b = 0; b < B; ++b) n += (host_lens[b] + r - 1) / r;
+    return n;
+  };
+  int64_t lo = 4, hi = max_split_rows(d) / 64;  // in units of 64 rows
+  if (hi > 1 << 24) hi = 1 << 24;
+  if (max_len == 0 || workgroups(hi * 64) > cus) return plan(d, B, max_len, 0, rows_per_split, num_splits);
+  while (lo < hi) {  // smallest r with workgroups(r) <= cus (monotone in r)
+    const int64_t mid = (lo + hi) / 2;
+    if (workgroups(mid * 64) <= cus) hi = mid; else lo = mid + 1;
+  }
+  return plan(d, B, max_len, (int32_t)(lo * 64), rows_per_split, num_splits);
+}
+
 // token_seq null: token b owns table row b (num_seqs = B).
 static int cache_append_impl(const mla_dims* d, int32_t B, const float* x, const mla_weight* kv_a,
                              const mla_weight* kv_a_norm, const mla_rope* rope,

@@ -56,6 +56,7 @@ constexpr int kLoads = kTileGran / kThreads;  // 9 granules per thread per tile
 constexpr int kBufs = 3;
 constexpr int kTileBytes = kTileGran * 16;    // 36864
 constexpr int kMaxSplitTiles = 1024;          // 32768 rows per split
+constexpr int kMaxPacked = 4096;              // queries a packed plan scans (more: one per grid row)
 constexpr int kQLds = 4;                      // k-blocks of the query kept in LDS (the rope part)
 constexpr int kQReg = kW / 16 - kQLds;        // k-blocks of the query kept in VGPRs
 constexpr int kPRow = 80;                     // bytes per head row of P in LDS (64 + 16 pad)
@@ -86,11 +87,55 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // [4 waves][kQLds][64 lanes] query fragments, in the order the lanes read them
   MLA_LDS bf16x8_t* qpe_lds = (MLA_LDS bf16x8_t*)(goff_lds + kLoads * kThreads);
 
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  int split = blockIdx.x;
+  int b = blockIdx.y;
+  if (a.num_splits > 1 && a.B <= kMaxPacked) {
+    // Packed plan: workgroup w (in dispatch order) takes the w-th non-empty
+    // (query, split) pair, query-major, so a ragged batch's work sits on the
+    // first workgroups (spread over the XCDs by the dispatcher) and the empty
+    // ones leave at once.  Query b has ceil(len_b / split_rows) non-empty splits;
+    // an exclusive scan over the queries finds this workgroup's pair.
+    const int w = blockIdx.y * gridDim.x + blockIdx.x;
+    MLA_LDS int* scan = (MLA_LDS int*)p_lds;  // [4] wave totals, [2] the pair; free until the loop
+    int cnts[kMaxPacked / kThreads];  // all lengths read up front: one latency, not one per chunk
+#pragma unroll
+    for (int i = 0; i < kMaxPacked / kThreads; ++i) {
+      const int q = i * kThreads + tid;
+      int lq = q < a.B ? a.seq_lens[q] : 0;
+      lq = lq < a.max_len ? lq : a.max_len;
+      cnts[i] = lq > 0 ? (lq + a.split_rows - 1) / a.split_rows : 0;
+    }
+    int carry = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPacked / kThreads; ++i) {
+      if (i * kThreads >= a.B) break;  // uniform
+      const int q = i * kThreads + tid;
+      const int cnt = cnts[i];
+      int x = cnt;  // inclusive scan inside the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        x += lane >= o ? y : 0;
+      }
+      if (lane == 63) scan[wave] = x;
+      __syncthreads();
+      int before = carry;
+      for (int v = 0; v < wave; ++v) before += scan[v];
+      const int excl = before + x - cnt;
+      if (w >= excl && w < excl + cnt) {
+        scan[4] = q;
+        scan[5] = w - excl;
+      }
+      carry += scan[0] + scan[1] + scan[2] + scan[3];
+      __syncthreads();  // the totals are read before the next chunk rewrites them
+    }
+    if (w >= carry) return;  // no work left for this workgroup (uniform)
+    b = scan[4];
+    split = scan[5];
+  }
   const int hf = lane >> 5;          // which half of the wave
   const int l32 = lane & 31;
   const int head = wave * 32 + l32;  // this lane's head in the S^T layout
@@ -120,6 +165,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   }
   const int ntiles = (row_end - row_begin + kTile - 1) / kTile;
 
+  // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
+  // 16*kb + 8*hf .. +7 of the 576.  The first kQReg k-blocks stay in VGPRs;
+  // the rope k-blocks go to LDS (the register file holds O, Q and the
+  // pipeline's fragments, and no more).  Issued before the block-table reads
+  // below, so that the two latencies overlap.
+  bf16x8_t qf[kQReg];
+  bf16x8_t qpe[kQLds];
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q_abs) + ((size_t)b * kH + head) * kW + 8 * hf;
+#pragma unroll
+    for (int kb = 0; kb < kQReg; ++kb)
+      qf[kb] = *reinterpret_cast<const bf16x8_t*>(q + 16 * kb);
+#pragma unroll
+    for (int j = 0; j < kQLds; ++j) qpe[j] = *reinterpret_cast<const bf16x8_t*>(q + 16 * (kQReg + j));
+  }
+
   // Physical first row of every tile of this split; -1 marks a bad table entry
   // (or a query whose sequence index is out of range).
   const int sq = a.q_seq ? a.q_seq[b] : b;
@@ -142,20 +203,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     goff_lds[k * kThreads + tid] = (uint32_t)(r * (kW * 2) + (x ^ (((j & 1) << 2) | (j >> 1))) * 16);
   }
 
-  // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
-  // 16*kb + 8*hf .. +7 of the 576.  The first kQReg k-blocks stay in VGPRs;
-  // the rope k-blocks go to LDS (the register file holds O, Q and the
-  // pipeline's fragments, and no more).
-  bf16x8_t qf[kQReg];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q_abs) + ((size_t)b * kH + head) * kW + 8 * hf;
 #pragma unroll
-    for (int kb = 0; kb < kQReg; ++kb)
-      qf[kb] = *reinterpret_cast<const bf16x8_t*>(q + 16 * kb);
-#pragma unroll
-    for (int j = 0; j < kQLds; ++j)
-      qpe_lds[(wave * kQLds + j) * 64 + lane] = *reinterpret_cast<const bf16x8_t*>(q + 16 * (kQReg + j));
-  }
+  for (int j = 0; j < kQLds; ++j) qpe_lds[(wave * kQLds + j) * 64 + lane] = qpe[j];
   // Consume the Q loads here, so that the only vector-memory operations in
   // flight inside the tile loop are the tile copies counted by hand below.
   asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
@@ -615,14 +664,21 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
 // fp16 times 2^-e_s: O_s = 2^e_s * (stored value), and 2^e_s folds into the
 // split's weight.  One wave per (sequence, head), 8 consecutive latent columns
 // per lane, so every split's partial row is one 1 KB coalesced read per wave;
-// four heads per workgroup.
+// four heads per workgroup.  Lane s % 64 forms split s's weight; the split
+// loop reads eight partial rows at a time, so a long context's many splits
+// are not one serial chain of loads.
 __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   const int b = blockIdx.y;
   const int h = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int S = a.num_splits;
-  const float* lse_s = a.part_lse + (size_t)b * S * kH + h;  // stride kH over s
-  const float* exp_s = a.part_exp + (size_t)b * S * kH + h;
+  // splits past ceil(len / split_rows) are empty: with a packed plan no
+  // workgroup wrote them, so they are not read
+  int len = a.seq_lens[b];
+  len = len < a.max_len ? len : a.max_len;
+  int S = len > 0 ? (len + a.split_rows - 1) / a.split_rows : 0;
+  S = S < a.num_splits ? S : a.num_splits;
+  const float* lse_s = a.part_lse + (size_t)b * a.num_splits * kH + h;  // stride kH over s
+  const float* exp_s = a.part_exp + (size_t)b * a.num_splits * kH + h;
 
   float m = -INFINITY;
   bool nan_lse = false;  // a bad table entry: NaN through the merge, as above
@@ -646,16 +702,39 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   const float inv = 1.0f / wsum;
 
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-  const _Float16* src = a.part_oh + ((size_t)b * S * kH + h) * kC + lane * 8;
+  const _Float16* src = a.part_oh + ((size_t)b * a.num_splits * kH + h) * kC + lane * 8;
   const size_t sstride = (size_t)kH * kC;
   f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float ls = lse_s[(size_t)s * kH];
-    if (ls == -INFINITY) continue;  // an empty split leaves its partial unwritten
-    const float w = ldexpf(expf(ls - m), (int)exp_s[(size_t)s * kH]);
-    const f16x8_t v = *reinterpret_cast<const f16x8_t*>(src + (size_t)s * sstride);
-    lo += w * f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-    hi += w * f32x4_t{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    // this lane's split s0 + lane: its weight, 0 for an empty split (whose
+    // partial is never written and is not read)
+    float w = 0.f;
+    if (s0 + lane < S) {
+      const float ls = lse_s[(size_t)(s0 + lane) * kH];
+      if (ls != -INFINITY) w = ldexpf(expf(ls - m), (int)exp_s[(size_t)(s0 + lane) * kH]);
+    }
+    const int n = S - s0 < 64 ? S - s0 : 64;
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      // eight loads in flight, no branches: a split past the end re-reads
+      // the last row and an empty split's unwritten row is read too, and
+      // both are dropped by a select (not multiplied by 0, which keeps NaN)
+      f16x8_t v[8];
+      float wj[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sj = j0 + j < n ? j0 + j : n - 1;  // uniform
+        wj[j] = j0 + j < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sj)) : 0.f;
+        v[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)(s0 + sj) * sstride);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4_t l4 = lo + wj[j] * f32x4_t{(float)v[j][0], (float)v[j][1], (float)v[j][2], (float)v[j][3]};
+        const f32x4_t h4 = hi + wj[j] * f32x4_t{(float)v[j][4], (float)v[j][5], (float)v[j][6], (float)v[j][7]};
+        const bool use = wj[j] != 0.f;
+        lo = use ? l4 : lo;
+        hi = use ? h4 : hi;
+      }
+    }
   }
   *reinterpret_cast<f32x4_t*>(dst) = lo * inv;
   *reinterpret_cast<f32x4_t*>(dst + 4) = hi * inv;

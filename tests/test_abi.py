@@ -95,6 +95,25 @@ def test_plan_and_workspace(lib):
         mla.attn_plan(DS, 1, 32768 + 64, 32768 + 64)
 
 
+def test_plan_from_lengths(lib):
+    # uniform batches get the automatic plan: one workgroup per compute unit (256 here)
+    assert mla.attn_plan_lens(DS, [16384] * 32) == mla.attn_plan(DS, 32, 16384, 0) == (2048, 8)
+    assert mla.attn_plan_lens(DS, [131072] * 4) == (2048, 64)
+    assert mla.attn_plan_lens(DS, [4096]) == (256, 16)
+    # a ragged batch: the smallest split whose non-empty workgroups fit 256 compute units
+    lens = np.random.default_rng(3).integers(1024, 8193, size=64)
+    r, s = mla.attn_plan_lens(DS, lens)
+    wgs = lambda r: int(np.sum((lens + r - 1) // r))
+    assert r % 64 == 0 and r >= 256 and s == -(-int(lens.max()) // r)
+    assert wgs(r) <= 256 < wgs(r - 64)
+    assert r < mla.attn_plan(DS, 64, int(lens.max()), 0)[0]  # shorter than the max-length plan
+    # empty sequences and an empty batch
+    assert mla.attn_plan_lens(DS, [0, 0]) == mla.attn_plan(DS, 2, 0, 0)
+    assert mla.attn_plan_lens(DS, []) == mla.attn_plan(DS, 0, 0, 0)
+    with pytest.raises(mla.MLAError):
+        mla.attn_plan_lens(DS, [5, -1])
+
+
 def test_weight_validation(lib):
     d = mla.Dims(16, 32, 16, 32, 64, hidden=256, q_lora=0, cache_dtype=mla.MLA_F32)
     rope = mla.CRope(0x100, 1.0)

@@ -76,6 +76,20 @@ def test_attn_bf16_ragged_paged(split_rows):
     close_bf16(lse, rlse, f"lse split={split_rows}")
 
 
+def test_attn_plan_from_lengths_ragged_paged():
+    # the length-aware plan on a ragged, paged batch (the batched-decode shape at
+    # reduced lengths, query given in latent form): exact against the oracle
+    lens = [int(x) for x in np.random.default_rng(21).integers(64, 2500, size=24)]
+    case = S.make_case(4, lens=lens, paged=True, seed=21)
+    ns = D.stage(case)
+    r, s = mla.attn_plan_lens(ns.dims, lens)
+    assert r < mla.attn_plan(ns.dims, 24, max(lens), 0)[0] or r == 256
+    vc, lse = attn_only(case, ns, r)
+    rvc, rlse = oracle_attn(case)
+    close_bf16(vc, rvc, f"v_combine plan ({r}, {s})")
+    close_bf16(lse, rlse, f"lse plan ({r}, {s})")
+
+
 def test_attn_more_splits_than_one_weight_chunk():
     # 71 splits of 64 rows for the long sequence: the combine walks its split
     # weights in chunks of 64; the short sequence leaves 69 splits empty.
