@@ -57,6 +57,7 @@ constexpr int kBufs = 3;
 constexpr int kTileBytes = kTileGran * 16;    // 36864
 constexpr int kMaxSplitTiles = 1024;          // 32768 rows per split
 constexpr int kMaxPacked = 4096;              // queries a packed plan scans (more: one per grid row)
+constexpr int kXcds = 8;                      // MI355X: 8 XCDs, each with its own L2
 constexpr int kQLds = 4;                      // k-blocks of the query kept in LDS (the rope part)
 constexpr int kQReg = kW / 16 - kQLds;        // k-blocks of the query kept in VGPRs
 constexpr int kPRow = 80;                     // bytes per head row of P in LDS (64 + 16 pad)
@@ -93,11 +94,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   int split = blockIdx.x;
   int b = blockIdx.y;
   if (a.num_splits > 1 && a.B <= kMaxPacked) {
-    // Packed plan: workgroup w (in dispatch order) takes the w-th non-empty
-    // (query, split) pair, query-major, so a ragged batch's work sits on the
-    // first workgroups (spread over the XCDs by the dispatcher) and the empty
-    // ones leave at once.  Query b has ceil(len_b / split_rows) non-empty splits;
-    // an exclusive scan over the queries finds this workgroup's pair.
+    // Packed plan: the non-empty (query, split) pairs, query-major, go to the
+    // first workgroups in dispatch order, so a ragged batch's work starts at
+    // once on every compute unit and the empty workgroups leave.  Query b has
+    // ceil(len_b / split_rows) non-empty splits; an exclusive scan over the
+    // queries finds this workgroup's pair.
     const int w = blockIdx.y * gridDim.x + blockIdx.x;
     MLA_LDS int* scan = (MLA_LDS int*)p_lds;  // [4] wave totals, [2] the pair; free until the loop
     int cnts[kMaxPacked / kThreads];  // all lengths read up front: one latency, not one per chunk
@@ -108,6 +109,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       lq = lq < a.max_len ? lq : a.max_len;
       cnts[i] = lq > 0 ? (lq + a.split_rows - 1) / a.split_rows : 0;
     }
+    // Workgroups go to the XCDs round robin (w % 8 on this chip).  The
+    // workgroups w < total take the pairs: XCD x's n_x = ceil((total - x) / 8)
+    // of them take one contiguous run of pairs, so the splits of a query share
+    // an XCD's L2 and its query is read from memory once per XCD, not per split.
+    int tsum = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPacked / kThreads; ++i) tsum += cnts[i];
+    for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
+    if (lane == 0) scan[6 + wave] = tsum;
+    __syncthreads();
+    const int total = scan[6] + scan[7] + scan[8] + scan[9];
+    if (w >= total) return;  // no work for this workgroup (uniform)
+    int p = w / kXcds;
+    for (int x = 0; x < w % kXcds; ++x) p += (total - x + kXcds - 1) / kXcds;
     int carry = 0;
 #pragma unroll
     for (int i = 0; i < kMaxPacked / kThreads; ++i) {
@@ -125,14 +140,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       int before = carry;
       for (int v = 0; v < wave; ++v) before += scan[v];
       const int excl = before + x - cnt;
-      if (w >= excl && w < excl + cnt) {
+      if (p >= excl && p < excl + cnt) {
         scan[4] = q;
-        scan[5] = w - excl;
+        scan[5] = p - excl;
       }
       carry += scan[0] + scan[1] + scan[2] + scan[3];
       __syncthreads();  // the totals are read before the next chunk rewrites them
     }
-    if (w >= carry) return;  // no work left for this workgroup (uniform)
     b = scan[4];
     split = scan[5];
   }
