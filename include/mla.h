@@ -320,7 +320,7 @@ int mla_attn_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
 
 /* A split-K plan for a batch whose lengths the caller knows on the host
  * (host_lens, int32 [batch], each >= 0): the smallest split (a multiple of 64
- * rows, at least 256) whose non-empty workgroups fit one per compute unit of
+ * rows, at least 128) whose non-empty workgroups fit one per compute unit of
  * the current device.  Pass *rows_per_split as split_rows to mla_decode_attn
  * or mla_attn_tokens (and to mla_workspace_bytes).  A ragged batch then runs
  * as one wave of workgroups of nearly equal size; the automatic plan sizes

@@ -80,8 +80,8 @@ def test_attn_validation_before_launch(lib):
 def test_plan_and_workspace(lib):
     r, s = mla.attn_plan(DS, 4, 131072, 2048)
     assert (r, s) == (2048, 64)
-    r, s = mla.attn_plan(DS, 1, 100, 0)   # automatic: splits of >= 256 rows covering the context
-    assert r % 64 == 0 and r >= 256 and r * s >= 100 and r * (s - 1) < 100
+    r, s = mla.attn_plan(DS, 1, 100, 0)   # automatic: splits of >= 128 rows covering the context
+    assert r % 64 == 0 and r >= 128 and r * s >= 100 and r * (s - 1) < 100
     need = mla.workspace_bytes(DS, 4, 131072, 2048)
     # bf16 cache: fp16 split partials, plus an lse and an exponent per (seq, split, head)
     assert need >= 4 * 64 * 128 * 512 * 2 + 2 * (4 * 64 * 128 * 4)
@@ -99,12 +99,12 @@ def test_plan_from_lengths(lib):
     # uniform batches get the automatic plan: one workgroup per compute unit (256 here)
     assert mla.attn_plan_lens(DS, [16384] * 32) == mla.attn_plan(DS, 32, 16384, 0) == (2048, 8)
     assert mla.attn_plan_lens(DS, [131072] * 4) == (2048, 64)
-    assert mla.attn_plan_lens(DS, [4096]) == (256, 16)
+    assert mla.attn_plan_lens(DS, [4096]) == mla.attn_plan(DS, 1, 4096, 0) == (128, 32)
     # a ragged batch: the smallest split whose non-empty workgroups fit 256 compute units
     lens = np.random.default_rng(3).integers(1024, 8193, size=64)
     r, s = mla.attn_plan_lens(DS, lens)
     wgs = lambda r: int(np.sum((lens + r - 1) // r))
-    assert r % 64 == 0 and r >= 256 and s == -(-int(lens.max()) // r)
+    assert r % 64 == 0 and r >= 128 and s == -(-int(lens.max()) // r)
     assert wgs(r) <= 256 < wgs(r - 64)
     assert r < mla.attn_plan(DS, 64, int(lens.max()), 0)[0]  # shorter than the max-length plan
     # empty sequences and an empty batch

@@ -101,3 +101,24 @@ def test_full_config5_layer():
     ref = O.decode_step(subset(case, sample))
     close(vc[sample], ref["v_combine"], f"v_combine, sequences {sample}")
     close(out[sample], ref["out"].reshape(len(sample), -1), f"out, sequences {sample}")
+
+
+def test_attn_more_queries_than_the_packed_scan():
+    # past 4096 queries the split kernel maps its grid directly (one row per
+    # query, empty splits written as empty) instead of packing the non-empty
+    # (query, split) pairs; ragged, several splits per query, checked on a sample
+    lens = [int(x) for x in np.random.default_rng(23).integers(1, 200, size=4100)]
+    case = S.make_case(4, lens=lens, paged=True, seed=23)
+    ns = D.stage(case)
+    ws = D.workspace(ns, 64)
+    mla.decode_attn(ns.dims, ns.q_abs_given, ns.pool, ns.table, ns.lens, ns.max_len,
+                    ns.softmax_scale, ns.v_combine, ns.lse, 64, ws)
+    torch.cuda.synchronize()
+    vc, lse = host(ns.v_combine), host(ns.lse)
+    for b in (0, 1, 2047, 4097, 4099):
+        sub = subset(case, [b])
+        q64 = O.widen(sub.q_abs, sub.dims.cache_dtype)
+        rvc, rlse, _ = O.attention_latent(sub.dims, q64, sub.pool, sub.table, sub.lens,
+                                          float(np.float32(case.softmax_scale)))
+        close(vc[b:b + 1], rvc, f"v_combine, query {b} (len {lens[b]})")
+        close(lse[b:b + 1], rlse, f"lse, query {b}")

@@ -83,7 +83,7 @@ def test_attn_plan_from_lengths_ragged_paged():
     case = S.make_case(4, lens=lens, paged=True, seed=21)
     ns = D.stage(case)
     r, s = mla.attn_plan_lens(ns.dims, lens)
-    assert r < mla.attn_plan(ns.dims, 24, max(lens), 0)[0] or r == 256
+    assert r < mla.attn_plan(ns.dims, 24, max(lens), 0)[0] or r == 128
     vc, lse = attn_only(case, ns, r)
     rvc, rlse = oracle_attn(case)
     close_bf16(vc, rvc, f"v_combine plan ({r}, {s})")
