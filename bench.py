@@ -325,6 +325,9 @@ def main():
                     help="launch every call eagerly on one stream (no graphs, no second stream)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="only the attention call on the other full-size workloads (one JSON "
+                         "object of them; not the benchmark line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -341,6 +344,13 @@ def main():
     globals()["S"] = S
 
     mla.load_library()
+    if args.attn_only:
+        extra = {}
+        for cfg, name in ((2, "b1_L4096"), (3, "b64_L1024-8192_paged"), (4, "b4_L131072")):
+            extra[name] = time_attn_only(cfg, torch, D, S, mla, oracle=not args.no_cpu,
+                                         lens_plan=(cfg == 3))
+        print(json.dumps({"attn_only": extra}), flush=True)
+        return
     case = S.make_case(5)
     ns = D.stage(case)
     B = case.batch
