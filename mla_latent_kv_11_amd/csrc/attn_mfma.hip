@@ -11,28 +11,34 @@
 //
 // Per 32-row tile and wave:
 //   S^T[t][h] = K[t][:] . Q^T[:][h]   36 x mfma_f32_32x32x16_bf16 (A = K from LDS,
-//                                      B = the wave's 32 q_abs rows kept in VGPRs)
+//                                      B = the wave's 32 q_abs rows: 32 k-blocks in
+//                                      VGPRs, the 4 rope k-blocks from LDS)
 //   softmax numerators in fp32, one head per lane, exp2 domain, against a
 //                                      per-head reference max (restart if exceeded)
 //   O^T[c][h] += V^T[c][t] . P^T[t][h] 32 x mfma (A = V^T via LDS transpose
-//                                      reads, B = P^T straight from the S^T registers)
-// The fp32 accumulator O^T (32 heads x 512) lives in the 256 AGPRs of each
-// lane (one head per lane); the resident Q (144 VGPRs), scores and fragments
-// share the 256 VGPRs.  O is only ever touched by MFMAs inside the loop.
+//                                      reads, B = every wave's P through LDS)
+// The fp32 accumulator O^T (128 latent columns x 128 heads per wave) lives in
+// the 256 AGPRs of each lane; the resident query (128 VGPRs), scores and
+// fragments share the 256 VGPRs.  O is only ever touched by MFMAs.
 //
-// Tiles stream HBM -> LDS with 16-byte direct-to-LDS loads, three buffers deep;
-// a wave waits for its copies of tile i + 1 just before the barrier that
-// publishes tile i's P, so the next tile's first K fragments are read during
-// tile i's P*V.
+// The tile loop is a software pipeline with one barrier per tile: after the
+// barrier that publishes tile i and the P of tile i - 1, one stream of MFMAs
+// alternates the scores of tile i with the P*V of tile i - 1, the copies of
+// tile i + 2 go out into the buffer tile i - 1 has left, and the V^T fragments
+// of tile i are read as registers free up; then tile i's softmax writes its P
+// (two P buffers by tile parity) and the wave waits for its copies of tile
+// i + 1 before the next barrier.  Tiles stream HBM -> LDS with 16-byte
+// direct-to-LDS loads, three buffers deep.
 // The LDS tile is 32 rows x 72 sixteen-byte granules with an XOR swizzle of the
 // granule index inside each aligned group of 8, chosen so that both the
 // row-wise K reads (16 rows, one granule each) and the transpose V reads (4
 // rows x 4 granules per 32 lanes) hit 16 distinct 16-byte bank groups.
 //
-// Split-K (flash decoding): grid = (splits, batch). A split with a single
-// partition writes v_combine/lse directly; otherwise it writes the normalised
-// partial O (fp16 with a power-of-two exponent per head) and its lse, merged
-// by attn_combine_f16_kernel.
+// Split-K (flash decoding): grid = (splits, queries).  With more than one split
+// the non-empty (query, split) pairs are packed onto the first workgroups, a
+// query's splits on one XCD; each writes the normalised partial O (fp16 with a
+// power-of-two exponent per head) and its lse, merged by
+// attn_combine_f16_kernel.  A single split writes v_combine and lse directly.
 #include <math.h>
 
 #include <mutex>
