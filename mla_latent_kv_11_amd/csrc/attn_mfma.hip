@@ -299,7 +299,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // the first tile.  If a later tile's maximum exceeds it by more than
   // kRestartLog2 (p would leave the safe range), the workgroup restarts the
   // split with the largest maximum seen as the new reference.  O is never
-  // rescaled or cleared: the first P*V after every (re)start takes C = 0.
+  // rescaled: MFMAs of zero operands clear it at every (re)start.
   const float c = a.scale_log2;
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;
@@ -344,8 +344,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   //   the nine copies of tile it + 2 into the buffer tile it - 1 has left;
   //   the V^T fragments of tile it, each read as soon as the P*V MFMAs of
   //     tile it - 1 are done with its registers.
-  // kMode 0: no P*V (the first tile of a (re)start); 1: the first P*V after
-  // a (re)start, whose first k-block starts from C = 0; 2: steady state.
+  // kMode 0: no P*V (the first tile of a (re)start); 2: with the P*V.
   // Tiles past the split's end are read and scored like any other (their
   // copies re-read the pool's first rows into the free buffer) and their
   // scores are dropped, so the sequence has no branch.
@@ -395,11 +394,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       if (n < 32) {
         // n = kb*16 + hb*4 + cbl
         const int kb = n >> 4, hb = (n >> 2) & 3, cbl = n & 3, f = (n >> 2) & 1;
-        if (kMode == 1 && kb == 0) {
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                       : "+a"(o[cbl * 4 + hb])
-                       : "v"(vf[0][cbl]), "v"(pf[f]));
-        } else if (kMode > 0) {
+        if (kMode > 0) {
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                        : "+a"(o[cbl * 4 + hb])
                        : "v"(vf[kb][cbl]), "v"(pf[f]));
