@@ -272,40 +272,38 @@ __global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q8_mfma_kernel(GemmArgs
 }
 
 // fp32 x[z*x_z + b*x_b + k] -> packed fp16; one thread writes one 16-byte chunk
-// (8 values of one token), so the stores are contiguous.
+// (8 values of one token), so the stores are contiguous.  blockIdx.x is the
+// (z, token tile) pair and y covers its units * 512 chunks, so the chunk's
+// coordinates come from shifts and masks (one division per workgroup).
 __global__ void __launch_bounds__(256) pack_f16_kernel(const float* x, int64_t x_b, int64_t x_z,
-                                                       int32_t B, int32_t K, int64_t chunks,
-                                                       bool vec, _Float16* xp) {
-  const int64_t units = K >> 7, tiles = (B + 31) >> 5;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
-       c += (int64_t)gridDim.x * 256) {
-    const int lane = (int)(c & 63);
-    const int64_t us = c >> 6;            // (unit_global * 8 + st)
-    const int st = (int)(us & 7);
-    const int64_t ug = us >> 3;           // (z * tiles + tile) * units + u
-    const int64_t u = ug % units, zt = ug / units;
-    const int64_t tile = zt % tiles, z = zt / tiles;
-    const int64_t b = tile * 32 + (lane & 31);
-    const int64_t k = u * 128 + (lane >> 5) * 64 + st * 8;
-    uint4 o = uint4{0u, 0u, 0u, 0u};
-    if (b < B) {
-      const float* src = x + z * x_z + b * x_b + k;
-      float v[8];
-      if (vec) {
-        const float4 v0 = reinterpret_cast<const float4*>(src)[0];
-        const float4 v1 = reinterpret_cast<const float4*>(src)[1];
-        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-      } else {
+                                                       int32_t B, int32_t K, bool vec,
+                                                       _Float16* xp) {
+  const int units = K >> 7, tiles = (B + 31) >> 5;
+  const int zt = blockIdx.x;  // z * tiles + tile
+  const int z = zt / tiles, tile = zt - z * tiles;
+  const int cz = blockIdx.y * 256 + threadIdx.x;  // chunk inside this (z, tile)
+  if (cz >= units * 512) return;
+  const int lane = cz & 63, st = (cz >> 6) & 7, u = cz >> 9;
+  const int64_t b = (int64_t)tile * 32 + (lane & 31);
+  const int64_t k = (int64_t)u * 128 + (lane >> 5) * 64 + st * 8;
+  uint4 o = uint4{0u, 0u, 0u, 0u};
+  if (b < B) {
+    const float* src = x + z * x_z + b * x_b + k;
+    float v[8];
+    if (vec) {
+      const float4 v0 = reinterpret_cast<const float4*>(src)[0];
+      const float4 v1 = reinterpret_cast<const float4*>(src)[1];
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = src[i];
-      }
-      const f16x8_t h = {(_Float16)v[0], (_Float16)v[4], (_Float16)v[1], (_Float16)v[5],
-                         (_Float16)v[2], (_Float16)v[6], (_Float16)v[3], (_Float16)v[7]};
-      o = __builtin_bit_cast(uint4, h);
+      for (int i = 0; i < 8; ++i) v[i] = src[i];
     }
-    reinterpret_cast<uint4*>(xp)[c] = o;
+    const f16x8_t h = {(_Float16)v[0], (_Float16)v[4], (_Float16)v[1], (_Float16)v[5],
+                       (_Float16)v[2], (_Float16)v[6], (_Float16)v[3], (_Float16)v[7]};
+    o = __builtin_bit_cast(uint4, h);
   }
+  reinterpret_cast<uint4*>(xp)[(int64_t)zt * units * 512 + cz] = o;
 }
 
 // Sum of S <= kMaxKSplits partials p[s * stride]; every load is issued
@@ -809,10 +807,11 @@ hipError_t launch_pack_f16(const float* x, int64_t x_b, int64_t x_z, int32_t Z, 
   if (Z <= 0 || B <= 0 || K <= 0) return hipSuccess;
   if (K % 128 != 0) return hipErrorInvalidValue;
   const bool vec = x_b % 4 == 0 && x_z % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-  const int64_t chunks = (int64_t)packed_bytes(Z, B, K) / 16;
-  const int64_t blocks = (chunks + 255) / 256 < 8192 ? (chunks + 255) / 256 : 8192;
-  hipLaunchKernelGGL(pack_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, x_b, x_z, B, K,
-                     chunks, vec, xp);
+  const int64_t zt = (int64_t)Z * ((B + 31) / 32);
+  const int64_t per = (int64_t)(K / 128) * 512;  // chunks per (z, token tile)
+  if (zt > (1ll << 31) - 1 || (per + 255) / 256 > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_f16_kernel, dim3((unsigned)zt, (unsigned)((per + 255) / 256)), dim3(256), 0,
+                     s, x, x_b, x_z, B, K, vec, xp);
   return hipGetLastError();
 }
 
