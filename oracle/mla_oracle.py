@@ -18,7 +18,7 @@ Every input is widened exactly to float64 from its stored bits (fp32, bf16, or
 rounded only where the method stores them (the cache row, and ``q_abs`` when
 the chain is modelled), with round-to-nearest-even.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * YaRN inverse frequencies: the ramp between two correction dimensions
     ([ts/gptoss] module doc, item 2; parameter list of ``MlaYarnTables::new``
     in [moeflux/forward]) is taken from the YaRN paper (Peng et al., 2023):
