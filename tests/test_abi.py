@@ -107,6 +107,13 @@ def test_plan_from_lengths(lib):
     assert r % 64 == 0 and r >= 128 and s == -(-int(lens.max()) // r)
     assert wgs(r) <= 256 < wgs(r - 64)
     assert r < mla.attn_plan(DS, 64, int(lens.max()), 0)[0]  # shorter than the max-length plan
+    # more sequences than compute units: no split fits, so the automatic plan is kept
+    assert mla.attn_plan_lens(DS, [1024] * 300) == mla.attn_plan(DS, 300, 1024, 0)
+    # one long sequence among short ones: the long one takes most of the workgroups
+    lens2 = np.array([131072] + [256] * 31)
+    r2, s2 = mla.attn_plan_lens(DS, lens2)
+    assert int(np.sum((lens2 + r2 - 1) // r2)) <= 256 and s2 == -(-131072 // r2)
+    assert int(np.sum((lens2 + r2 - 65) // (r2 - 64))) > 256
     # empty sequences and an empty batch
     assert mla.attn_plan_lens(DS, [0, 0]) == mla.attn_plan(DS, 2, 0, 0)
     assert mla.attn_plan_lens(DS, []) == mla.attn_plan(DS, 0, 0, 0)
