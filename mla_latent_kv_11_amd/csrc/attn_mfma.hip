@@ -23,11 +23,12 @@
 //
 // The tile loop is a software pipeline with one barrier per tile: after the
 // barrier that publishes tile i and the P of tile i - 1, one stream of MFMAs
-// alternates the scores of tile i with the P*V of tile i - 1, the copies of
-// tile i + 2 go out into the buffer tile i - 1 has left, and the V^T fragments
-// of tile i are read as registers free up; then tile i's softmax writes its P
-// (two P buffers by tile parity) and the wave waits for its copies of tile
-// i + 1 before the next barrier.  Tiles stream HBM -> LDS with 16-byte
+// runs the scores of tile i with half of the P*V of tile i - 1 between them,
+// then the other half of the P*V with tile i's softmax issued between those
+// MFMAs (it writes tile i's P into one of two P buffers, by tile parity); the
+// copies of tile i + 2 go out into the buffer tile i - 1 has left, the V^T
+// fragments of tile i are read as registers free up, and the wave waits for
+// its copies of tile i + 1 before the next barrier.  Tiles stream HBM -> LDS with 16-byte
 // direct-to-LDS loads, three buffers deep.
 // The LDS tile is 32 rows x 72 sixteen-byte granules with an XOR swizzle of the
 // granule index inside each aligned group of 8, chosen so that both the
@@ -338,17 +339,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // One MFMA phase of the pipeline, after the barrier that published tile
   // `it` and the P of tile it - 1:
   //   scores of tile it: S^T = K Q^T, 36 MFMAs in one accumulator chain;
-  //   P*V of tile it - 1 (kMode > 0): O^T += V^T P^T, 32 MFMAs, one between
-  //     every two score MFMAs, so neither chain waits on its own results;
-  //     head block outer, so one P fragment serves four MFMAs in a row;
+  //   P*V of tile it - 1 (kMode > 0): O^T += V^T P^T, 32 MFMAs; 16 of them
+  //     one after every second score MFMA, the other 16 after the score chain
+  //     has ended, with the softmax of tile it issued between them (its VALU
+  //     work runs while they execute); head block outer, so one P fragment
+  //     serves four MFMAs in a row;
   //   the nine copies of tile it + 2 into the buffer tile it - 1 has left;
   //   the V^T fragments of tile it, each read as soon as the P*V MFMAs of
   //     tile it - 1 are done with its registers.
-  // kMode 0: no P*V (the first tile of a (re)start); 2: with the P*V.
-  // Tiles past the split's end are read and scored like any other (their
-  // copies re-read the pool's first rows into the free buffer) and their
-  // scores are dropped, so the sequence has no branch.
-  auto mfma_phase = [&](auto mode, int it) -> f32x16_t {
+  // kMode 0: no P*V (the first tile of a (re)start); returns the scores for
+  // softmax().  kMode 2: with the P*V and tile it's softmax; `keep` is false
+  // for the look-ahead tile past the split's end and when a restart was voted,
+  // and then the numerators are formed but no state is updated; `pend` gets
+  // softmax()'s result.  Tiles past the split's end are read and scored like
+  // any other (their copies re-read the pool's first rows into the free
+  // buffer), so the sequence has no branch.
+  auto mfma_phase = [&](auto mode, int it, bool keep, bool& pend) -> f32x16_t {
     constexpr int kMode = decltype(mode)::value;
     const uint32_t tile = tiles_lds + (uint32_t)((it % kBufs) * kTileBytes);
     const char* nsrc = pool;
@@ -374,6 +380,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       pf[0] = pread(0, 0);
       pf[1] = pread(1, 0);
     }
+    // P*V step m of tile it - 1 (m = kb*16 + hb*4 + cbl), then tile it's V^T
+    // fragment in the registers the step has finished with
+    auto pv_step = [&](int m) {
+      const int kb = m >> 4, hb = (m >> 2) & 3, cbl = m & 3, f = (m >> 2) & 1;
+      if (kMode > 0) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(o[cbl * 4 + hb])
+                     : "v"(vf[kb][cbl]), "v"(pf[f]));
+      }
+      // the P fragment two steps on replaces the one just finished
+      if (kMode > 0 && cbl == 3 && m + 8 < 32) pf[f] = pread(((m >> 2) + 2) & 3, (m + 8) >> 4);
+      if (hb == 3) vf[kb][cbl] = vread(va, cbl, kb);
+    };
     uint32_t noff = goff_lds[tid];
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t qp[kQLds];  // the LDS-resident query k-blocks, read in the phase's last quarter
@@ -391,19 +410,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[n % 3]), "v"(qn));
       if (n + 3 < kW / 16) kf[n % 3] = *kaddr(qa, n + 3);
       if (n >= 24 && n < 24 + 2 * kQLds && (n & 1) == 0) qp[(n - 24) >> 1] = qsrc[((n - 24) >> 1) * 64];
-      if (n < 32) {
-        // n = kb*16 + hb*4 + cbl
-        const int kb = n >> 4, hb = (n >> 2) & 3, cbl = n & 3, f = (n >> 2) & 1;
-        if (kMode > 0) {
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                       : "+a"(o[cbl * 4 + hb])
-                       : "v"(vf[kb][cbl]), "v"(pf[f]));
-        }
-        // the P fragment two steps on replaces the one just finished
-        if (kMode > 0 && cbl == 3 && n + 8 < 32) pf[f] = pread(((n >> 2) + 2) & 3, (n + 8) >> 4);
-        // vf[kb][cbl] is free after the last head block: read tile it's fragment
-        if (hb == 3) vf[kb][cbl] = vread(va, cbl, kb);
-      }
+      if (kMode == 0 && n < 32) pv_step(n);  // the V^T reads only
+      if (kMode > 0 && (n & 1) && n < 32) pv_step(n >> 1);
       if ((n & 3) == 3) {  // copy n / 4 of tile it + 2; the next copy's offset
         const int k = n >> 2;
         const uint32_t off = noff;
@@ -412,10 +420,82 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // VALU reads of an MFMA result wait 18 cycles after a 16-pass MFMA; the
-    // compiler does not see into asm, so pad here
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
-    return s;
+    if constexpr (kMode == 0) {
+      // VALU reads of an MFMA result wait 18 cycles after a 16-pass MFMA; the
+      // compiler does not see into asm, so pad here
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
+      return s;
+    } else {
+      // softmax() of tile it in slices between the last 16 P*V steps (the
+      // reference max is fixed after a (re)start's first tile, so it is read
+      // here, never raised)
+      const int lim = row_end - (row_begin + it * kTile);
+      const bool tail = lim < kTile;
+      float e = 0.f, mt = 0.f;
+      float p[16];
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        pv_step(16 + t);
+        if (t == 0) {
+          asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
+          if (tail) {  // rows past the end do not take part in the maximum
+            int l = lim - 4 * hf;
+            asm volatile("" : "+v"(l));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[j] = (j >> 2) * 8 + (j & 3) < l ? s[j] : __builtin_nanf("");
+          }
+        }
+        if (t == 0 || t == 1) {  // extreme of 8 raw scores (fmax/fmin skip the masked NaNs)
+          const int j0 = 8 * t;
+          float x;
+          if (c >= 0.f)
+            x = fmaxf(fmaxf(fmaxf(s[j0], s[j0 + 1]), fmaxf(s[j0 + 2], s[j0 + 3])),
+                      fmaxf(fmaxf(s[j0 + 4], s[j0 + 5]), fmaxf(s[j0 + 6], s[j0 + 7])));
+          else
+            x = fminf(fminf(fminf(s[j0], s[j0 + 1]), fminf(s[j0 + 2], s[j0 + 3])),
+                      fminf(fminf(s[j0 + 4], s[j0 + 5]), fminf(s[j0 + 6], s[j0 + 7])));
+          e = t == 0 ? x : (c >= 0.f ? fmaxf(e, x) : fminf(e, x));
+        }
+        if (t == 2) {
+          float lo, hi;
+          wave_halves(e, &lo, &hi);
+          mt = (c >= 0.f ? fmaxf(lo, hi) : fminf(lo, hi)) * c;
+          if (keep) {
+            m_seen = fmaxf(m_seen, mt);
+            bad |= tile_base[it] < 0;
+          }
+        }
+        if (t >= 3 && t < 11) {
+          const int j = 2 * (t - 3);
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c, -m_ref));
+          p[j + 1] = __builtin_amdgcn_exp2f(fmaf(s[j + 1], c, -m_ref));
+        }
+        if (t == 11) {
+          if (tail) {
+            int l = lim - 4 * hf;
+            asm volatile("" : "+v"(l));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) p[j] = (j >> 2) * 8 + (j & 3) < l ? p[j] : 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)p[j];
+        }
+        if (t == 12) {
+          const float q0 = (p[0] + p[1]) + (p[2] + p[3]), q1 = (p[4] + p[5]) + (p[6] + p[7]);
+          const float q2 = (p[8] + p[9]) + (p[10] + p[11]), q3 = (p[12] + p[13]) + (p[14] + p[15]);
+          if (keep) l_run += (q0 + q1) + (q2 + q3);
+        }
+        if (t == 13) {
+          MLA_LDS char* prow = p_lds + p_row + (uint32_t)((it & 1) * kPBuf) + wave * (32 * kPRow);
+          *(MLA_LDS bf16x8_t*)prow = pb[0];
+          *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pend = mt > m_ref + kRestartLog2;
+      return s;
+    }
   };
 
   // Softmax numerators of tile it (lane = head, 16 rows per lane, the rest in
@@ -480,7 +560,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 
   // The pipeline, per (re)start: tiles 0 and 1 are copied, then phase it
   // (it = 0 .. ntiles) runs the MFMAs of tile it's scores and tile it - 1's
-  // P*V, and tile it's softmax follows.  One barrier per tile publishes its
+  // P*V, with tile it's softmax inside its tail (after it for tile 0, whose
+  // phase has no P*V).  One barrier per tile publishes its
   // P, its restart vote and tile it + 1 (whose copies this wave waits for
   // just before it: the nine newer copies are tile it + 2's).  Buffers: tile
   // it + 2 goes into the buffer of tile it - 1, whose K and V^T reads all
@@ -517,8 +598,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 (tile 1's copies are newer)
     zero_tail(0);
     __syncthreads();
-    f32x16_t s = mfma_phase(std::integral_constant<int, 0>{}, 0);
-    bool pending = softmax(s, 0);
+    bool pending = false;
+    f32x16_t s = mfma_phase(std::integral_constant<int, 0>{}, 0, true, pending);
+    pending = softmax(s, 0);
     bool restart = false;
     for (int it = 1;; ++it) {
       if (lane == 0) votes[((it - 1) & 1) * 4 + wave] = __ballot(pending) != 0;
@@ -530,13 +612,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         const MLA_LDS int* v = votes + ((it - 1) & 1) * 4;
         vote = v[0] | v[1] | v[2] | v[3];
       }
-      s = mfma_phase(std::integral_constant<int, 2>{}, it);
+      mfma_phase(std::integral_constant<int, 2>{}, it, vote == 0 && it < ntiles, pending);
       if (vote != 0) {
         restart = true;
         break;
       }
       if (it == ntiles) break;
-      pending = softmax(s, it);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!restart) break;
