@@ -165,6 +165,22 @@ def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50, oracle=True, lens_p
     return out
 
 
+def settle(run, torch, min_ms=150.0):
+    """Untimed steps until at least ``min_ms`` of wall time has passed, whatever
+    the warm-up count: the GPU needs some tens of ms of sustained load before
+    its clocks settle.  Returns (milliseconds, steps)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(10):
+            run()
+        n += 10
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= min_ms:
+            return el, n
+
+
 def oracle_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -314,8 +330,8 @@ def S_sub(case, seqs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU needs some tens of ms of sustained load to reach steady clocks;
-    # 200 steps are about 60 ms
+    # the clocks settle under some tens of ms of sustained load: besides the
+    # warm-up steps, at least 150 ms of untimed steps run before the timing
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extra", action="store_true", help="skip the per-configuration attention lines")
@@ -367,6 +383,7 @@ def main():
         for _ in range(args.warmup):
             step.run()
     torch.cuda.synchronize()
+    settle_ms, settle_steps = settle(lambda: step.run(eager=args.eager), torch)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step.run(eager=args.eager)
@@ -441,6 +458,9 @@ def main():
                       "one HIP graph per step; append | absorb on two streams",
             "global_batch": B, "seq_len": int(ns.max_len), "parallelism": "none (1 GPU)",
             "split_rows": r_split, "splits_per_seq": n_split,
+            "precision": "attention: bf16 MFMA operands, fp32 accumulate, fp32 softmax; "
+                         "4-bit projections: fp16 MFMA operands, fp32 accumulate",
+            "settle": f"{settle_steps} untimed steps ({settle_ms:.0f} ms) after the warm-up",
         },
         "roofline": {
             "bound": "hbm",

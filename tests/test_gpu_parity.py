@@ -4,6 +4,9 @@ Inputs come from the seeded generators in ``mla_synth`` and are fed to both
 sides.  Tolerances (stated by the target, applied elementwise):
   * fp32 caches: max |gpu - ref| <= 1e-4, and (non-replacing) <= 1e-3 max|ref|
   * bf16 caches: |gpu - ref| <= 2e-2 + 1e-2 |ref|
+  * decode attention on a bf16 cache, beside that bar: per query every lse
+    within 1e-4 + 1e-6 |lse| and max |v_combine error| <= 2e-3 max |v_combine|
+    (``tests/parity.py``), so that a missing tile or split cannot pass
   * integer work (slots, untouched pool rows, paged == contiguous): bit-exact
 """
 import copy
@@ -19,25 +22,9 @@ import mla_synth as S
 from mla_synth import device as D
 from oracle import mla_oracle as O
 
+from parity import attn_check, attn_tight, close_bf16, close_f32
+
 pytestmark = pytest.mark.gpu
-
-ATOL_BF16, RTOL_BF16 = 2e-2, 1e-2
-
-
-def close_bf16(got, ref, what):
-    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, what
-    bad = ~(np.abs(got - ref) <= ATOL_BF16 + RTOL_BF16 * np.abs(ref))
-    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance, "
-                           f"max abs err {np.nanmax(np.abs(got - ref)):.3e}")
-
-
-def close_f32(got, ref, what):
-    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
-    err = np.max(np.abs(got - ref))
-    assert err <= 1e-4, f"{what}: max abs err {err:.3e} > 1e-4"
-    assert err <= 1e-3 * np.max(np.abs(ref)) + 1e-12, f"{what}: err {err:.3e} vs scale"
-
 
 def host(x):
     a = x.detach().cpu().numpy()
@@ -51,6 +38,19 @@ def sync():
 # ----------------------------------------------------------------------------
 # decode attention alone (q_abs drawn by the generator)
 # ----------------------------------------------------------------------------
+def attn_on_oracle_query(case, ns, res, what, split_rows=0):
+    """Run decode attention on the GPU's cache (after its append) with the
+    query the oracle stored, and apply the tight checks against the oracle's
+    attention.  The oracle attends its own appended row, the GPU the row it
+    appended: one row of the sequence, whose small rounding difference moves
+    lse by far less than the tolerance."""
+    q = D.t(res["q_abs_stored"])
+    ws = D.workspace(ns, split_rows)
+    D.attend(ns, q, split_rows, ws)
+    sync()
+    attn_check(host(ns.v_combine), host(ns.lse), res["v_combine"], res["lse"],
+               f"{what}: attention on the oracle's query")
+
 def attn_only(case, ns, split_rows=0):
     ws = D.workspace(ns, split_rows)
     mla.decode_attn(ns.dims, ns.q_abs_given, ns.pool, ns.table, ns.lens, ns.max_len,
@@ -72,8 +72,7 @@ def test_attn_bf16_ragged_paged(split_rows):
     ns = D.stage(case)
     vc, lse = attn_only(case, ns, split_rows)
     rvc, rlse = oracle_attn(case)
-    close_bf16(vc, rvc, f"v_combine split={split_rows}")
-    close_bf16(lse, rlse, f"lse split={split_rows}")
+    attn_check(vc, lse, rvc, rlse, f"split={split_rows}")
 
 
 def test_attn_plan_from_lengths_ragged_paged():
@@ -86,8 +85,7 @@ def test_attn_plan_from_lengths_ragged_paged():
     assert r < mla.attn_plan(ns.dims, 24, max(lens), 0)[0] or r == 128
     vc, lse = attn_only(case, ns, r)
     rvc, rlse = oracle_attn(case)
-    close_bf16(vc, rvc, f"v_combine plan ({r}, {s})")
-    close_bf16(lse, rlse, f"lse plan ({r}, {s})")
+    attn_check(vc, lse, rvc, rlse, f"plan ({r}, {s})")
 
 
 def test_attn_more_splits_than_one_weight_chunk():
@@ -97,8 +95,7 @@ def test_attn_more_splits_than_one_weight_chunk():
     ns = D.stage(case)
     vc, lse = attn_only(case, ns, 64)
     rvc, rlse = oracle_attn(case)
-    close_bf16(vc, rvc, "v_combine")
-    close_bf16(lse, rlse, "lse")
+    attn_check(vc, lse, rvc, rlse, "attention")
 
 
 def repage(case, block, seed):
@@ -138,7 +135,7 @@ def test_attn_block_sizes(block):
     a, l = attn_only(other, ns2, 128)
     assert np.array_equal(a, a64) and np.array_equal(l, l64), f"block {block} != block 64"
     rvc, rlse = oracle_attn(other)
-    close_bf16(a, rvc, f"v_combine block={block}")
+    attn_check(a, l, rvc, rlse, f"block={block}")
 
 
 def test_attn_longest_single_split():
@@ -147,8 +144,7 @@ def test_attn_longest_single_split():
     ns = D.stage(case)
     vc, lse = attn_only(case, ns, 32768)
     rvc, rlse = oracle_attn(case)
-    close_bf16(vc, rvc, "v_combine")
-    close_bf16(lse, rlse, "lse")
+    attn_check(vc, lse, rvc, rlse, "attention")
 
 
 def test_attn_bf16_invariances():
@@ -182,7 +178,7 @@ def test_attn_empty_sequences():
     assert np.all(vc[1] == 0) and np.all(np.isneginf(lse[1]))
     case.lens = np.array([64, 0, 64], dtype=np.int32)
     rvc, rlse = oracle_attn(case)
-    close_bf16(vc[[0, 2]], rvc[[0, 2]], "v_combine")
+    attn_check(vc, lse, rvc, rlse, "with an empty sequence")
     # max_seq_len 0: everything empty
     ws = D.workspace(ns)
     mla.decode_attn(ns.dims, ns.q_abs_given, ns.pool, ns.table, ns.lens, 0, ns.softmax_scale,
@@ -212,8 +208,7 @@ def test_attn_growing_scores_restart_path():
     for split in (0, 128):
         vc, lse = attn_only(case, ns, split)
         rvc, rlse = oracle_attn(case)
-        close_bf16(vc, rvc, f"v_combine split={split}")
-        close_bf16(lse, rlse, f"lse split={split}")
+        attn_check(vc, lse, rvc, rlse, f"split={split}")
 
 
 def test_attn_split_partials_beyond_fp16_range():
@@ -234,7 +229,7 @@ def test_attn_split_partials_beyond_fp16_range():
         vc, lse = attn_only(case, ns, split)
         assert np.isfinite(vc).all()
         close_bf16(vc * 2.0 ** -17, rvc * 2.0 ** -17, f"v_combine / 2^17 split={split}")
-        close_bf16(lse, rlse, f"lse split={split}")
+        attn_tight(vc, lse, rvc, rlse, f"split={split}")
 
 
 def test_attn_f32_kernel_config1_shapes():
@@ -429,6 +424,7 @@ def test_chain_q8_0_kv_b(cfg, kw):
     res = O.decode_step(case)
     close_bf16(host(ns.v_combine), res["v_combine"], "v_combine")
     close_bf16(host(ns.out), res["out"].reshape(case.batch, -1), "out")
+    attn_on_oracle_query(case, ns, res, "Q8_0 chain")
 
 
 # ----------------------------------------------------------------------------
@@ -467,6 +463,28 @@ def test_chain(cfg, kw):
             close_f32(got, o1, "out vs unabsorbed")
         else:
             close_bf16(got, o1, "out vs unabsorbed")
+    if d.cache_dtype == O.F32:
+        return
+    if case.o_proj is not None:
+        # the 4-bit layer against the unabsorbed definition: the per-head W_UV
+        # outputs (o_proj not applied) on the sampled heads, and o_proj applied
+        # to the unabsorbed attention of every head against the layer's output
+        ws = D.workspace(ns)
+        per_head = torch.empty((case.batch, d.num_heads * d.v_head), dtype=torch.float32,
+                               device="cuda")
+        mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, per_head, None, ws)
+        sync()
+        got = host(per_head).reshape(case.batch, d.num_heads, d.v_head)
+        close_bf16(got[:, heads], o1, "per-head W_UV output vs unabsorbed")
+        o_all, _ = O.attention_unabsorbed(d, res_u["q"], res_u["kv_b64"], res_u["pool"],
+                                          case.table, case.lens, res_u["softmax_scale"],
+                                          res_u["inv_freq"], res_u["rope_mscale"], case.positions)
+        o64 = O.weight_f64(case.o_proj, O.weight_dtype(case.o_proj), d.hidden,
+                           d.num_heads * d.v_head)
+        y1 = O.matvec(o64, o_all.reshape(case.batch, -1))
+        close_bf16(out, y1, "layer output vs o_proj of the unabsorbed attention")
+    # the attention call alone, tight, on the GPU's cache with the oracle's query
+    attn_on_oracle_query(case, ns, res, "chain")
 
 
 @pytest.mark.parametrize("cfg,lens", [(4, [100, 2000]), (1, [100, 600])])
@@ -498,4 +516,4 @@ def test_bad_table_entry_gives_nan_through_the_merge(cfg, lens):
     if case.dims.cache_dtype == O.F32:
         close_f32(vc[1], ref["v_combine"][1], "other sequence")
     else:
-        close_bf16(vc[1], ref["v_combine"][1], "other sequence")
+        attn_check(vc[1:], lse[1:], ref["v_combine"][1:], ref["lse"][1:], "other sequence")

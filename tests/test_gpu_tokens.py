@@ -4,7 +4,8 @@ multi-token decode): ``mla_cache_append_tokens`` and ``mla_attn_tokens``, with
 
 Reading under test (the pages give the batched projections, not the
 attention): all new rows are appended first, and the token at position p
-attends rows 0..p of its own sequence.  Tolerances as in test_gpu_parity.
+attends rows 0..p of its own sequence.  Tolerances as in test_gpu_parity,
+with the tight per-query attention checks of ``tests/parity.py``.
 """
 import copy
 
@@ -18,7 +19,8 @@ import mla_synth as S
 from mla_synth import device as D
 from oracle import mla_oracle as O
 
-from test_gpu_parity import close_bf16, close_f32, host, sync
+from parity import attn_check, close_bf16, close_f32
+from test_gpu_parity import attn_on_oracle_query, host, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +54,8 @@ def test_chunk_step(cfg, prior, chunk, paged):
                O.widen(res["pool"][pb, r], d.cache_dtype), f"row of token {t}")
     _close(d.cache_dtype, host(ns.v_combine), res["v_combine"], "v_combine")
     _close(d.cache_dtype, host(ns.out), res["out"].reshape(case.batch, -1), "out")
+    if d.cache_dtype != O.F32:
+        attn_on_oracle_query(case, ns, res, f"chunk cfg {cfg}")
 
 
 def test_attn_tokens_equals_decode_on_an_expanded_table():
@@ -70,7 +74,7 @@ def test_attn_tokens_equals_decode_on_an_expanded_table():
     assert np.array_equal(host(ns.v_combine), host(vc2))
     assert np.array_equal(host(ns.lse), host(lse2))
     res = O.decode_step(case)
-    close_bf16(host(ns.v_combine), res["v_combine"], "v_combine")
+    attn_check(host(ns.v_combine), host(ns.lse), res["v_combine"], res["lse"], "tokens")
 
 
 def _token_view(ns, t):
