@@ -8,12 +8,12 @@ Two kinds of check are applied to GPU results against the fp64 oracle:
   cannot pass.  At 131072 rows the stated bar leaves lse about 0.15 of slack,
   while dropping one 32-row tile moves lse by only ~32 / 131072 = 2.4e-4, so
   per query every head's lse must agree to 1e-4 + 1e-6 |lse| and the largest
-  v_combine error must stay under 2e-3 of the query's largest |v_combine|.
-  The kernel's own error budget sits well inside both: its lse is fp32 over
-  exact bf16 products (no rounding of p enters the denominator), and the only
-  rounding in v_combine is p to bf16 as an MFMA operand (2^-9 relative per
-  term, ~1.1e-3 relative rms on a weighted mean) plus a 2^-11 fp16 split
-  partial.  ``tests/test_parity_checker.py`` shows on the CPU that these checks
+  v_combine error must stay under 4e-3 of the query's largest |v_combine|.
+  The kernel's own error budget sits inside both: its lse is fp32 over exact
+  bf16 products (no rounding of p enters the denominator), and the only
+  rounding in v_combine is p to bf16 as an MFMA operand (at most 2^-9 relative
+  per term) plus the fp16 split partial (2^-11): at most 2.44e-3 of |v| where
+  one row dominates a short query, ~1.1e-3 rms where many rows average out.  ``tests/test_parity_checker.py`` shows on the CPU that these checks
   reject the oracle's own result with one tile or one split removed at 131072
   rows and accept a model of the kernel's rounding.
 """
@@ -21,7 +21,7 @@ import numpy as np
 
 ATOL_BF16, RTOL_BF16 = 2e-2, 1e-2
 LSE_ATOL, LSE_RTOL = 1e-4, 1e-6
-VC_REL = 2e-3
+VC_REL = 4e-3
 
 
 def close_bf16(got, ref, what):

@@ -5,7 +5,7 @@ The GPU runs the whole batch; the fp64 oracle recomputes a few sampled sequences
 (sequences are independent, so the oracle runs on a sub-case holding just those
 sequences, sharing the cache pool).  Tolerances: the bf16-cache bar,
 |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise, and for the attention call the
-tight per-query checks of ``tests/parity.py`` (lse to 1e-4, v_combine to 2e-3 of
+tight per-query checks of ``tests/parity.py`` (lse to 1e-4, v_combine to 4e-3 of
 its largest value), which a missing tile or split at 131072 rows cannot pass.
 Where the layer computes the query itself, the attention call is checked again
 on the GPU's cache with the oracle's stored query in the sampled rows.

@@ -5,7 +5,7 @@ sides.  Tolerances (stated by the target, applied elementwise):
   * fp32 caches: max |gpu - ref| <= 1e-4, and (non-replacing) <= 1e-3 max|ref|
   * bf16 caches: |gpu - ref| <= 2e-2 + 1e-2 |ref|
   * decode attention on a bf16 cache, beside that bar: per query every lse
-    within 1e-4 + 1e-6 |lse| and max |v_combine error| <= 2e-3 max |v_combine|
+    within 1e-4 + 1e-6 |lse| and max |v_combine error| <= 4e-3 max |v_combine|
     (``tests/parity.py``), so that a missing tile or split cannot pass
   * integer work (slots, untouched pool rows, paged == contiguous): bit-exact
 """
