@@ -80,6 +80,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"MLA HIP library not built ({path} missing); "
                            "run `python -m mla_latent_kv_11_amd.build`")
+    # torch brings its own HIP runtime (same soname as the system one).  Load
+    # it first so that the library binds to that runtime: loaded the other way
+    # round, the process holds two HIP runtimes, and kernels launched by one on
+    # the other's streams and memory fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     PD, PW = ctypes.POINTER(CDims), ctypes.POINTER(CWeight)

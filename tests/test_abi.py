@@ -269,3 +269,17 @@ def test_token_calls_validation_before_launch(lib):
     assert app(nseq=-1) == mla.MLA_ERR_DIMS
     assert app(x=None) == mla.MLA_ERR_NULL
     assert app(n=0, nseq=0) == mla.MLA_OK
+
+
+def test_one_hip_runtime_in_the_process():
+    """Loading the library (even before torch is imported) leaves a single
+    HIP runtime mapped: torch's, which owns the memory and streams passed in."""
+    import re
+    import subprocess
+    import sys
+    code = ("import mla_latent_kv_11_amd as m; m.load_library(); import torch, re; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len(set(re.findall(r'/\\S*libamdhip64\\S*', maps))))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

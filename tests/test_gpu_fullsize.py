@@ -8,7 +8,7 @@ sequences, sharing the cache pool).  Tolerances: the bf16-cache bar,
 tight per-query checks of ``tests/parity.py`` (lse to 1e-4, v_combine to 4e-3 of
 its largest value), which a missing tile or split at 131072 rows cannot pass.
 Where the layer computes the query itself, the attention call is checked again
-on the GPU's cache with the oracle's stored query in the sampled rows.
+on the oracle's cache and stored query in the sampled rows.
 """
 import copy
 
@@ -54,12 +54,15 @@ def run_layer(case):
 
 
 def attn_on_oracle_query(ns, sample, ref, what):
-    """decode_attn over the whole batch (automatic plan) on the GPU's cache,
-    with the oracle's stored query in the sampled rows; tight checks there."""
+    """decode_attn over the whole batch (automatic plan) on the oracle's cache
+    (its own appended rows), with the oracle's stored query in the sampled
+    rows; tight checks there."""
     q = ns.q_abs.clone()
     q[torch.as_tensor(sample, device=q.device)] = D.t(ref["q_abs_stored"])
+    view = copy.copy(ns)
+    view.pool = D.t(ref["pool"])
     ws = D.workspace(ns)
-    D.attend(ns, q, 0, ws)
+    D.attend(view, q, 0, ws)
     torch.cuda.synchronize()
     attn_check(host(ns.v_combine)[sample], host(ns.lse)[sample], ref["v_combine"], ref["lse"],
                f"{what}, sequences {sample}")
