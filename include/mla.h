@@ -249,6 +249,29 @@ int mla_out_proj(const mla_dims* dims, int32_t batch, const float* v_combine,
                  const mla_weight* kv_b, const mla_weight* o_proj, float* out,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* mla_decode_attn_noalloc -- mla_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and arguments, with the
+ * split partials kept in a static device array of MLA_NOALLOC_SCRATCH_BYTES
+ * that each device holds from the library's load until the process ends,
+ * instead of a caller workspace.  The call allocates and frees nothing.
+ *   Arguments: as mla_decode_attn, without ws / ws_bytes.
+ *   Limit: the split plan's partials (mla_workspace_bytes of an attention-only
+ *   geometry, i.e. batch * splits * H * (C * 2 + 8) bytes on a bf16 cache) must
+ *   fit the array, else MLA_ERR_WORKSPACE and nothing is enqueued.  The
+ *   automatic plan at H = 128, C = 512 needs at most about (256 + batch)
+ *   partials of 129 KB while batch < 256, and none from batch 256 up.
+ *   Concurrency: every call on one device uses the same array, so calls that
+ *   overlap in time on one device (other streams, other threads) race; order
+ *   them on one stream.
+ * Errors: as mla_decode_attn; WORKSPACE when the plan exceeds the array;
+ * HIP when the array's device address cannot be obtained. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+int mla_decode_attn_noalloc(const mla_dims* dims, int32_t batch, const void* q_abs,
+                            const mla_cache* cache, const int32_t* seq_lens,
+                            int32_t max_seq_len, float softmax_scale, int32_t split_rows,
+                            float* v_combine, float* lse, void* stream);
+
 /* ---- several tokens per sequence (chunked prefill, multi-token decode) ----
  * moeflux gpu_matvec.rs, encode_matvec_n_tokens: one weight matrix is applied
  * to stacked tokens, each token's arithmetic unchanged.  mla_absorb_q and

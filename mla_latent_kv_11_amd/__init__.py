@@ -30,7 +30,8 @@ MLA_DEV_POS_RANGE, MLA_DEV_BAD_BLOCK, MLA_DEV_BAD_SEQ = 1, 2, 4
 EXPORTED = ("mla_yarn_tables", "mla_cache_append", "mla_absorb_q", "mla_decode_attn",
             "mla_out_proj", "mla_cache_append_tokens", "mla_attn_tokens",
             "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan",
-            "mla_attn_plan_lens", "mla_status_str")
+            "mla_attn_plan_lens", "mla_status_str", "mla_decode_attn_noalloc")
+MLA_NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
 class MLAError(RuntimeError):
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_decode_attn": ([PD, I32, P, PC, P, I32, ctypes.c_float, I32, P, P, P, SZ, P],
                             ctypes.c_int),
         "mla_out_proj": ([PD, I32, P, PW, PW, P, P, SZ, P], ctypes.c_int),
+        "mla_decode_attn_noalloc": ([PD, I32, P, PC, P, I32, ctypes.c_float, I32, P, P, P],
+                                    ctypes.c_int),
         "mla_cache_append_tokens": ([PD, I32, P, PW, PW, PR, P, P, I32, PC, P, P, SZ, P],
                                     ctypes.c_int),
         "mla_attn_tokens": ([PD, I32, P, PC, P, I32, P, I32, ctypes.c_float, I32, P, P, P, SZ,
@@ -283,6 +286,21 @@ def decode_attn(dims: Dims, q_abs, pool, table, seq_lens, max_seq_len: int,
                              ws.numel() * ws.element_size() if ws is not None else 0,
                              _stream(stream))
     _check(st, "mla_decode_attn")
+
+
+def decode_attn_noalloc(dims: Dims, q_abs, pool, table, seq_lens, max_seq_len: int,
+                        softmax_scale: float, v_combine, lse=None, split_rows: int = 0,
+                        stream=None) -> None:
+    """decode_attn with the split partials in the library's static device
+    scratch (no workspace; calls overlapping on one device race)."""
+    lib = load_library()
+    cache = _cache(pool, table)
+    B = int(seq_lens.shape[0])
+    st = lib.mla_decode_attn_noalloc(ctypes.byref(dims.c()), B, _ptr(q_abs), ctypes.byref(cache),
+                                     _ptr(seq_lens), int(max_seq_len), float(softmax_scale),
+                                     int(split_rows), _ptr(v_combine), _ptr(lse),
+                                     _stream(stream))
+    _check(st, "mla_decode_attn_noalloc")
 
 
 def cache_append_tokens(dims: Dims, x, kv_a: Optional[Weight], kv_a_norm: Weight, inv_freq,

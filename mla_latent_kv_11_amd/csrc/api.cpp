@@ -15,9 +15,17 @@
 
 int attn_mfma_max_split_rows();
 
+// Scratch of mla_decode_attn_noalloc: the split partials live in this static
+// device array instead of a caller workspace.  Each device holds its own copy
+// at its own address, found once per device with hipGetSymbolAddress; host
+// code only ever passes that address (the array's name is a host-side
+// stand-in).  Calls on one device share it, so overlapping calls race.
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
 // Smallest automatic split: 128 rows (4 tiles).  Shorter splits cost a query
 // load and a partial write each; on one 4096-row context 64-, 128-, 256- and
 // 512-row splits took 35.9, 34.0, 38.0 and 50.0 us.
@@ -153,6 +161,21 @@ size_t ws_out(const mla_dims* d, int32_t B) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Device address of this device's scratch, or nullptr if it cannot be found.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
 
 double yarn_get(double s, double m) { return s <= 1.0 ? 1.0 : 0.1 * m * log(s) + 1.0; }
 
@@ -517,6 +540,22 @@ int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_c
                     void* stream) {
   return attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
                    v_combine, lse, ws, ws_bytes, stream);
+}
+
+int mla_decode_attn_noalloc(const mla_dims* d, int32_t B, const void* q_abs,
+                            const mla_cache* cache, const int32_t* seq_lens, int32_t max_len,
+                            float softmax_scale, int32_t split_rows, float* v_combine, float* lse,
+                            void* stream) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (B < 0 || max_len < 0) return MLA_ERR_DIMS;
+  int32_t rows = 0, splits = 1;
+  if ((st = plan(d, B, max_len, split_rows, &rows, &splits))) return st;
+  if (ws_attn(d, B, splits) > kScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (splits > 1 && !(ws = scratch_ptr())) return MLA_ERR_HIP;
+  return attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
+                   v_combine, lse, ws, ws ? kScratchBytes : 0, stream);
 }
 
 int mla_attn_tokens(const mla_dims* d, int32_t n_tokens, const void* q_abs,
