@@ -207,10 +207,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   const int sq = a.q_seq ? a.q_seq[b] : b;
   const bool seq_ok = sq >= 0 && sq < a.num_seqs;
   const int32_t* trow = a.table + (size_t)(seq_ok ? sq : 0) * a.max_blocks;
+  int bad_tile = 0;
   for (int i = tid; i < ntiles; i += kThreads) {
     const int t0 = row_begin + i * kTile;
     const int blk = seq_ok ? trow[t0 / a.block] : -1;
-    tile_base[i] = (blk >= 0 && blk < a.num_blocks) ? blk * a.block + (t0 % a.block) : -1;
+    const bool ok = blk >= 0 && blk < a.num_blocks;
+    tile_base[i] = ok ? blk * a.block + (t0 % a.block) : -1;
+    bad_tile |= !ok;
   }
   // Byte offset, inside a tile of 32 consecutive rows, of granule copy k of
   // this thread: LDS slot p = (k*4 + wave)*64 + lane holds granule
@@ -235,7 +238,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
                "v"(qf[22]), "v"(qf[23]), "v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]),
                "v"(qf[28]), "v"(qf[29]), "v"(qf[30]), "v"(qf[31]));
   static_assert(kQReg == 32, "the asm above names every register-resident k-block");
-  __syncthreads();
+  // any bad table entry in the split makes its outputs NaN
+  const bool bad = __syncthreads_or(bad_tile) != 0;
 
   const char* pool = static_cast<const char*>(a.pool);
   const uint32_t tiles_lds = (uint32_t)(uintptr_t)tiles;
@@ -255,10 +259,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // Source of tile i: the address of its first row (a bad table entry reads
   // row 0 and makes the output NaN).  A tile never crosses a block, so all its
   // 32 rows lie inside the pool even where the split ends first.
-  auto tile_src = [&](int i) -> const char* {
-    const int base = __builtin_amdgcn_readfirstlane(tile_base[i]);
+  auto base_src = [&](int raw) -> const char* {
+    const int base = __builtin_amdgcn_readfirstlane(raw);
     return pool + (size_t)(base < 0 ? 0 : base) * (kW * 2);
   };
+  auto tile_src = [&](int i) -> const char* { return base_src(tile_base[i]); };
   // Copy granule k of tile i: 16 bytes per lane straight into LDS at
   // M0 + 16 * lane.  Issued from asm so that the compiler does not treat every
   // later LDS read as aliasing the copy; the explicit vmcnt waits order them.
@@ -305,7 +310,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;
   float l_run = 0.f;
-  bool bad = false;
   bool fresh = true;  // the next tile is the first since the (re)start
 
   // K fragment of k-block kb: base qa[kb & 3] of the tile, + (kb >> 2) * 128.
@@ -332,6 +336,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
+  const char* src2 = pool;  // source of the tile two ahead of the current phase
+
   // V^T fragments of the tile whose P*V comes next (column blocks 4*wave ..
   // +3 as (cb >> 1) = 2*wave + (cbl >> 1), cb & 1 = cbl & 1; two k-blocks).
   s16x8_t vf[2][4];
@@ -354,11 +360,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // softmax()'s result.  Tiles past the split's end are read and scored like
   // any other (their copies re-read the pool's first rows into the free
   // buffer), so the sequence has no branch.
-  auto mfma_phase = [&](auto mode, int it, bool keep, bool& pend) -> f32x16_t {
+  auto mfma_phase = [&](auto mode, int it, bool keep, bool& pend, int& vote) -> f32x16_t {
     constexpr int kMode = decltype(mode)::value;
     const uint32_t tile = tiles_lds + (uint32_t)((it % kBufs) * kTileBytes);
-    const char* nsrc = pool;
-    if (it + 2 < ntiles) nsrc = tile_src(it + 2);
+    // the copies of tile it + 2 read from src2 (found during the previous
+    // phase); tile it + 3's base is read now and turned into the next src2 at
+    // the end, so no LDS round trip stands between the barrier and the MFMAs
+    const char* nsrc = src2;
+    const int raw3 = tile_base[it + 3 < ntiles ? it + 3 : 0];
+    // the restart votes of tile it - 1, read now, used in the softmax slices
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    i32x4_t vv{0, 0, 0, 0};
+    if (kMode > 0) vv = *(const MLA_LDS i32x4_t*)(votes + ((it - 1) & 1) * 4);
     uint32_t qa[4];
     kbases(tile, qa);
     uint32_t va[4];
@@ -424,14 +437,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       // VALU reads of an MFMA result wait 18 cycles after a 16-pass MFMA; the
       // compiler does not see into asm, so pad here
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
+      src2 = it + 3 < ntiles ? base_src(raw3) : pool;
       return s;
     } else {
       // softmax() of tile it in slices between the last 16 P*V steps (the
       // reference max is fixed after a (re)start's first tile, so it is read
-      // here, never raised)
+      // here, never raised).  u = s * scale * log2e - m_ref is the exponent of
+      // every numerator; rows past the split's end get u = -inf (numerator 0,
+      // no part in the maximum).  The tile's largest u only feeds the restart
+      // vote and the reference of a restart.
       const int lim = row_end - (row_begin + it * kTile);
       const bool tail = lim < kTile;
-      float e = 0.f, mt = 0.f;
+      float e = 0.f;
+      float u[16];
       float p[16];
       bf16x8_t pb[2];
 #pragma unroll
@@ -439,61 +457,55 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         pv_step(16 + t);
         if (t == 0) {
           asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
-          if (tail) {  // rows past the end do not take part in the maximum
-            int l = lim - 4 * hf;
-            asm volatile("" : "+v"(l));
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[j] = (j >> 2) * 8 + (j & 3) < l ? s[j] : __builtin_nanf("");
-          }
+          for (int j = 0; j < 8; ++j) u[j] = fmaf(s[j], c, -m_ref);
         }
-        if (t == 0 || t == 1) {  // extreme of 8 raw scores (fmax/fmin skip the masked NaNs)
-          const int j0 = 8 * t;
-          float x;
-          if (c >= 0.f)
-            x = fmaxf(fmaxf(fmaxf(s[j0], s[j0 + 1]), fmaxf(s[j0 + 2], s[j0 + 3])),
-                      fmaxf(fmaxf(s[j0 + 4], s[j0 + 5]), fmaxf(s[j0 + 6], s[j0 + 7])));
-          else
-            x = fminf(fminf(fminf(s[j0], s[j0 + 1]), fminf(s[j0 + 2], s[j0 + 3])),
-                      fminf(fminf(s[j0 + 4], s[j0 + 5]), fminf(s[j0 + 6], s[j0 + 7])));
-          e = t == 0 ? x : (c >= 0.f ? fmaxf(e, x) : fminf(e, x));
-        }
-        if (t == 2) {
-          float lo, hi;
-          wave_halves(e, &lo, &hi);
-          mt = (c >= 0.f ? fmaxf(lo, hi) : fminf(lo, hi)) * c;
-          if (keep) {
-            m_seen = fmaxf(m_seen, mt);
-            bad |= tile_base[it] < 0;
-          }
-        }
-        if (t >= 3 && t < 11) {
-          const int j = 2 * (t - 3);
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c, -m_ref));
-          p[j + 1] = __builtin_amdgcn_exp2f(fmaf(s[j + 1], c, -m_ref));
-        }
-        if (t == 11) {
+        if (t == 1) {
+#pragma unroll
+          for (int j = 8; j < 16; ++j) u[j] = fmaf(s[j], c, -m_ref);
           if (tail) {
             int l = lim - 4 * hf;
             asm volatile("" : "+v"(l));
 #pragma unroll
-            for (int j = 0; j < 16; ++j) p[j] = (j >> 2) * 8 + (j & 3) < l ? p[j] : 0.f;
+            for (int j = 0; j < 16; ++j) u[j] = (j >> 2) * 8 + (j & 3) < l ? u[j] : -INFINITY;
           }
+        }
+        if (t == 2) {
+          e = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(u[4], u[5]), fmaxf(u[6], u[7])));
+          e = fmaxf(e, fmaxf(fmaxf(fmaxf(u[8], u[9]), fmaxf(u[10], u[11])),
+                             fmaxf(fmaxf(u[12], u[13]), fmaxf(u[14], u[15]))));
+        }
+        if (t == 3) {
+          float lo, hi;
+          wave_halves(e, &lo, &hi);
+          e = fmaxf(lo, hi);
+          vote = __builtin_amdgcn_readfirstlane(vv.x | vv.y | vv.z | vv.w);
+          keep = keep && vote == 0;
+          if (keep) m_seen = fmaxf(m_seen, e + m_ref);
+        }
+        if (t >= 4 && t < 12) {
+          const int j = 2 * (t - 4);
+          p[j] = __builtin_amdgcn_exp2f(u[j]);
+          p[j + 1] = __builtin_amdgcn_exp2f(u[j + 1]);
+        }
+        if (t == 12) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)p[j];
         }
-        if (t == 12) {
+        if (t == 13) {
           const float q0 = (p[0] + p[1]) + (p[2] + p[3]), q1 = (p[4] + p[5]) + (p[6] + p[7]);
           const float q2 = (p[8] + p[9]) + (p[10] + p[11]), q3 = (p[12] + p[13]) + (p[14] + p[15]);
           if (keep) l_run += (q0 + q1) + (q2 + q3);
         }
-        if (t == 13) {
+        if (t == 14) {
           MLA_LDS char* prow = p_lds + p_row + (uint32_t)((it & 1) * kPBuf) + wave * (32 * kPRow);
           *(MLA_LDS bf16x8_t*)prow = pb[0];
           *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      pend = mt > m_ref + kRestartLog2;
+      pend = e > kRestartLog2;
+      src2 = it + 3 < ntiles ? base_src(raw3) : pool;
       return s;
     }
   };
@@ -505,47 +517,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // numerators (so lse stays exact to fp32, independent of the split plan).
   // Returns whether this lane's maximum left the reference's safe range.
   auto softmax = [&](f32x16_t s, int it) -> bool {
-    bad |= tile_base[it] < 0;
     // row (j >> 2) * 8 + (j & 3) + 4 * hf of the tile is valid iff that is < lim
     const int lim = row_end - (row_begin + it * kTile);
     const bool tail = lim < kTile;
-    if (tail) {  // rows past the end do not take part in the maximum
+    float u[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) u[j] = s[j] * c;
+    if (tail) {  // rows past the end: numerator 0, no part in the maximum
       int l = lim - 4 * hf;
       asm volatile("" : "+v"(l));  // formed here, on the split's last tile only
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[j] = (j >> 2) * 8 + (j & 3) < l ? s[j] : __builtin_nanf("");
+      for (int j = 0; j < 16; ++j) u[j] = (j >> 2) * 8 + (j & 3) < l ? u[j] : -INFINITY;
     }
-    // extreme of the raw scores (max for a positive scale, min for a negative
-    // one); fmax/fmin ignore the NaN of masked rows
-    float e;
-    if (c >= 0.f) {
-      e = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-      e = fmaxf(e, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
-                         fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-      float lo, hi;
-      wave_halves(e, &lo, &hi);
-      e = fmaxf(lo, hi);
-    } else {
-      e = fminf(fminf(fminf(s[0], s[1]), fminf(s[2], s[3])), fminf(fminf(s[4], s[5]), fminf(s[6], s[7])));
-      e = fminf(e, fminf(fminf(fminf(s[8], s[9]), fminf(s[10], s[11])),
-                         fminf(fminf(s[12], s[13]), fminf(s[14], s[15]))));
-      float lo, hi;
-      wave_halves(e, &lo, &hi);
-      e = fminf(lo, hi);
-    }
-    const float mt = e * c;
+    float e = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(u[4], u[5]), fmaxf(u[6], u[7])));
+    e = fmaxf(e, fmaxf(fmaxf(fmaxf(u[8], u[9]), fmaxf(u[10], u[11])),
+                       fmaxf(fmaxf(u[12], u[13]), fmaxf(u[14], u[15]))));
+    float lo, hi;
+    wave_halves(e, &lo, &hi);
+    const float mt = fmaxf(lo, hi);
     m_seen = fmaxf(m_seen, mt);
     if (fresh) m_ref = fmaxf(m_ref, mt);
     fresh = false;
     float p[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c, -m_ref));
-    if (tail) {
-      int l = lim - 4 * hf;
-      asm volatile("" : "+v"(l));
-#pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = (j >> 2) * 8 + (j & 3) < l ? p[j] : 0.f;
-    }
+    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(u[j] - m_ref);
     bf16x8_t pb[2];
 #pragma unroll
     for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)p[j];
@@ -595,11 +590,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         : "v"(zf));
     issue_tile(0);
     issue_tile(1);
+    src2 = 2 < ntiles ? tile_src(2) : pool;
     asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 (tile 1's copies are newer)
     zero_tail(0);
     __syncthreads();
     bool pending = false;
-    f32x16_t s = mfma_phase(std::integral_constant<int, 0>{}, 0, true, pending);
+    int vote = 0;
+    f32x16_t s = mfma_phase(std::integral_constant<int, 0>{}, 0, true, pending, vote);
     pending = softmax(s, 0);
     bool restart = false;
     for (int it = 1;; ++it) {
@@ -607,12 +604,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's copies of tile it
       zero_tail(it);
       __syncthreads();
-      int vote;
-      {
-        const MLA_LDS int* v = votes + ((it - 1) & 1) * 4;
-        vote = v[0] | v[1] | v[2] | v[3];
-      }
-      mfma_phase(std::integral_constant<int, 2>{}, it, vote == 0 && it < ntiles, pending);
+      mfma_phase(std::integral_constant<int, 2>{}, it, it < ntiles, pending, vote);
       if (vote != 0) {
         restart = true;
         break;
