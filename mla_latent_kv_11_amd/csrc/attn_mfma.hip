@@ -73,6 +73,7 @@ constexpr size_t kSmemBytes =
     kBufs * kTileBytes + (kMaxSplitTiles + 8) * 4 + kH * 4 + 2 * kPBuf + kLoads * kThreads * 4 +
     kQLds * kThreads * 16;
 constexpr float kRestartLog2 = 32.0f;         // restart when the max grows by > 2^32
+constexpr int kMaxRestarts = 16;              // after that, one last pass that does not vote
 constexpr float kLn2 = 0.69314718055994530942f;
 
 static_assert(kLoads * kThreads == kTileGran, "tile must split evenly over the threads");
@@ -302,15 +303,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 
   f32x16_t o[kC / 32];  // cleared by MFMAs at every (re)start
   // p = 2^(s*scale*log2e - m_ref) with a per-head reference m_ref taken from
-  // the first tile.  If a later tile's maximum exceeds it by more than
-  // kRestartLog2 (p would leave the safe range), the workgroup restarts the
-  // split with the largest maximum seen as the new reference.  O is never
-  // rescaled: MFMAs of zero operands clear it at every (re)start.
+  // the first tile (0 if that tile has no finite score for the head, so that
+  // later exponents stay finite).  If a later tile's maximum exceeds it by
+  // more than kRestartLog2 (p would leave the safe range), the workgroup
+  // restarts the split with the largest maximum seen as the new reference;
+  // each restart raises some head's reference by more than kRestartLog2, and
+  // after kMaxRestarts the last pass runs without voting, so the loop always
+  // ends.  O is never rescaled: MFMAs of zero operands clear it at every
+  // (re)start.
   const float c = a.scale_log2;
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;
   float l_run = 0.f;
   bool fresh = true;  // the next tile is the first since the (re)start
+  bool may_vote = true;
 
   // K fragment of k-block kb: base qa[kb & 3] of the tile, + (kb >> 2) * 128.
   // The bases are made opaque so that the constant offsets fold into the
@@ -504,7 +510,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      pend = e > kRestartLog2;
+      pend = may_vote && e > kRestartLog2;
       src2 = it + 3 < ntiles ? base_src(raw3) : pool;
       return s;
     }
@@ -536,7 +542,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     wave_halves(e, &lo, &hi);
     const float mt = fmaxf(lo, hi);
     m_seen = fmaxf(m_seen, mt);
-    if (fresh) m_ref = fmaxf(m_ref, mt);
+    if (fresh) {
+      m_ref = fmaxf(m_ref, mt);
+      if (m_ref == -INFINITY) m_ref = 0.f;  // no finite score yet (fmaxf drops NaN)
+    }
     fresh = false;
     float p[16];
 #pragma unroll
@@ -550,7 +559,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     MLA_LDS char* prow = p_lds + p_row + (uint32_t)((it & 1) * kPBuf) + wave * (32 * kPRow);
     *(MLA_LDS bf16x8_t*)prow = pb[0];
     *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
-    return mt > m_ref + kRestartLog2;
+    return may_vote && mt > m_ref + kRestartLog2;
   };
 
   // The pipeline, per (re)start: tiles 0 and 1 are copied, then phase it
@@ -565,6 +574,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // writes of tile it + 1.  A restart vote is read after the barrier and
   // acted on after the next MFMA phase (its P*V is then discarded).
   const bf16x8_t zf = bf16x8_t{};
+  int restarts = 0;
   for (;;) {
     // O = 0 at every (re)start: 0 x 0 + 0 for each 32 x 32 block
     asm volatile(
@@ -615,6 +625,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     if (!restart) break;
     __syncthreads();  // every wave's copies have landed before the buffers are reused
     m_ref = m_seen;
+    if (++restarts >= kMaxRestarts) may_vote = false;
     l_run = 0.f;
     fresh = true;
   }

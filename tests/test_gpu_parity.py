@@ -213,6 +213,48 @@ def test_attn_growing_scores_restart_path():
         attn_check(vc, lse, rvc, rlse, f"split={split}")
 
 
+@pytest.mark.parametrize("split", [0, 64])
+def test_attn_first_tile_without_finite_scores(split):
+    """Rows 0..31 of sequence 0 score -inf for every head (a -inf in a rope
+    column that every head's query weights by +1; V is the latent part, so
+    those rows only get probability 0).  A split whose first tile has no
+    finite score must still end and match the oracle.  The latent part of
+    the query is scaled by 16 so that later tiles' scores reach past the
+    restart threshold and vote restarts from that state."""
+    case = S.make_case(4, lens=[300, 100], seed=24)
+    d = case.dims
+    q = S.bf16_bits_to_f32(case.q_abs)
+    q[:, :, :d.kv_lora] *= 16.0
+    q[:, :, d.kv_lora] = 1.0
+    case.q_abs = S.to_bf16_bits(q)
+    nbk = (int(case.lens[0]) + 63) // 64
+    flat = case.pool[case.table[0, :nbk]].reshape(-1, d.width)
+    flat[:32, d.kv_lora] = 0xFF80                # bf16 -inf
+    case.pool[case.table[0, :nbk]] = flat.reshape(nbk, 64, d.width)
+    ns = D.stage(case)
+    vc, lse = attn_only(case, ns, split)
+    rvc, rlse = oracle_attn(case)
+    assert np.isfinite(rvc).all() and np.isfinite(vc).all()
+    attn_check(vc, lse, rvc, rlse, f"split={split}")
+
+
+def test_attn_nan_first_tile_ends_with_nan():
+    """NaN rows fill the first tile of sequence 0: its outputs are NaN (as in
+    the oracle) and the call ends; sequence 1 is exact."""
+    case = S.make_case(4, lens=[300, 100], seed=25)
+    d = case.dims
+    nbk = (int(case.lens[0]) + 63) // 64
+    flat = case.pool[case.table[0, :nbk]].reshape(-1, d.width)
+    flat[:32, :] = S.BF16_NAN
+    case.pool[case.table[0, :nbk]] = flat.reshape(nbk, 64, d.width)
+    ns = D.stage(case)
+    for split in (0, 64):
+        vc, lse = attn_only(case, ns, split)
+        assert np.isnan(vc[0]).all() and np.isnan(lse[0]).all()
+        rvc, rlse = oracle_attn(case)
+        attn_check(vc[1:], lse[1:], rvc[1:], rlse[1:], f"other sequence, split={split}")
+
+
 def test_attn_split_partials_beyond_fp16_range():
     # Latent values scaled by 2^17 (exact in bf16) and the latent part of q by
     # 2^-17: the scores are unchanged and v_combine scales by 2^17, past the
