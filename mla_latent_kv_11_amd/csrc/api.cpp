@@ -150,10 +150,13 @@ size_t ws_attn_o(const mla_dims* d, int32_t B, int32_t splits) {
   const size_t elem = d->cache_dtype == MLA_BF16 ? 2 : 4;
   return align_up((size_t)B * splits * d->num_heads * d->kv_lora * elem);
 }
+// For a bf16 cache also the slot table (first partial slot of each query and
+// the rows per split the kernel chose).
 size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
   if (splits <= 1) return 0;
   const size_t lse = align_up((size_t)B * splits * d->num_heads * 4);
-  return ws_attn_o(d, B, splits) + lse * (d->cache_dtype == MLA_BF16 ? 2 : 1);
+  if (d->cache_dtype != MLA_BF16) return ws_attn_o(d, B, splits) + lse;
+  return ws_attn_o(d, B, splits) + 2 * lse + align_up(((size_t)B + 1) * 4);
 }
 size_t ws_out(const mla_dims* d, int32_t B) {
   const size_t vc = align_up(packed_bytes(d->num_heads, B, d->kv_lora));
@@ -515,7 +518,18 @@ static int attn_impl(const mla_dims* d, int32_t B, const void* q_abs, const mla_
     else a.part_o = reinterpret_cast<float*>(base);
     base += ws_attn_o(d, B, splits);
     a.part_lse = reinterpret_cast<float*>(base);
-    if (bf16) a.part_exp = reinterpret_cast<float*>(base + align_up((size_t)B * splits * d->num_heads * 4));
+    if (bf16) {
+      const size_t lse = align_up((size_t)B * splits * d->num_heads * 4);
+      a.part_exp = reinterpret_cast<float*>(base + lse);
+      a.part_first = reinterpret_cast<int32_t*>(base + 2 * lse);
+      // automatic plan, packed grid, more than one query: the kernel sizes the
+      // splits from the lengths, with at most one non-empty split per compute
+      // unit (and never more than the slots the workspace holds)
+      if (split_rows == 0 && B >= 2 && B <= 4096) {
+        const int64_t slots = (int64_t)B * splits, cus = device_cus();
+        a.auto_slots = (int32_t)(slots < cus ? slots : cus);
+      }
+    }
   }
   a.B = B;
   a.H = d->num_heads;

@@ -70,7 +70,7 @@ constexpr int kQReg = kW / 16 - kQLds;        // k-blocks of the query kept in V
 constexpr int kPRow = 80;                     // bytes per head row of P in LDS (64 + 16 pad)
 constexpr int kPBuf = kH * kPRow;             // one P buffer; two alternate by tile parity
 constexpr size_t kSmemBytes =
-    kBufs * kTileBytes + (kMaxSplitTiles + 8) * 4 + kH * 4 + 2 * kPBuf + kLoads * kThreads * 4 +
+    kBufs * kTileBytes + (kMaxSplitTiles + 12) * 4 + kH * 4 + 2 * kPBuf + kLoads * kThreads * 4 +
     kQLds * kThreads * 16;
 constexpr float kRestartLog2 = 32.0f;         // restart when the max grows by > 2^32
 constexpr int kMaxRestarts = 16;              // after that, one last pass that does not vote
@@ -89,8 +89,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   MLA_LDS char* tiles = (MLA_LDS char*)smem;
   MLA_LDS int* tile_base = (MLA_LDS int*)(smem + kBufs * kTileBytes);
-  MLA_LDS int* votes = tile_base + kMaxSplitTiles;         // [2][4] restart votes, by tile parity
-  MLA_LDS float* l_heads = (MLA_LDS float*)(votes + 8);    // [128] softmax denominators
+  MLA_LDS int* votes = tile_base + kMaxSplitTiles;         // [2] restart votes (a byte per wave), by tile parity; [8] the slot
+  MLA_LDS float* l_heads = (MLA_LDS float*)(votes + 12);   // [128] softmax denominators
   MLA_LDS char* p_lds = (MLA_LDS char*)(l_heads + kH);     // [2][128 heads][kPRow] bf16 P, slot order
   MLA_LDS uint32_t* goff_lds = (MLA_LDS uint32_t*)(p_lds + 2 * kPBuf);  // [kLoads][256]
   // [4 waves][kQLds][64 lanes] query fragments, in the order the lanes read them
@@ -101,40 +101,97 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   const int lane = tid & 63;
   int split = blockIdx.x;
   int b = blockIdx.y;
+  int rows = a.split_rows;  // rows per split
+  int slot = b * a.num_splits + split;  // partial slot of this (query, split)
   if (a.num_splits > 1 && a.B <= kMaxPacked) {
     // Packed plan: the non-empty (query, split) pairs, query-major, go to the
     // first workgroups in dispatch order, so a ragged batch's work starts at
     // once on every compute unit and the empty workgroups leave.  Query b has
-    // ceil(len_b / split_rows) non-empty splits; an exclusive scan over the
-    // queries finds this workgroup's pair.
+    // ceil(len_b / rows) non-empty splits; an exclusive scan over the queries
+    // finds this workgroup's pair, whose index is also its partial slot.
     const int w = blockIdx.y * gridDim.x + blockIdx.x;
     MLA_LDS int* scan = (MLA_LDS int*)p_lds;  // [4] wave totals, [2] the pair; free until the loop
-    int cnts[kMaxPacked / kThreads];  // all lengths read up front: one latency, not one per chunk
+    const int nchunks = (a.B + kThreads - 1) / kThreads;
+    int lens[kMaxPacked / kThreads];  // all lengths read up front: one latency, not one per chunk
 #pragma unroll
     for (int i = 0; i < kMaxPacked / kThreads; ++i) {
       const int q = i * kThreads + tid;
-      int lq = q < a.B ? a.seq_lens[q] : 0;
-      lq = lq < a.max_len ? lq : a.max_len;
-      cnts[i] = lq > 0 ? (lq + a.split_rows - 1) / a.split_rows : 0;
+      const int lq = q < a.B ? a.seq_lens[q] : 0;
+      lens[i] = lq < a.max_len ? lq : a.max_len;
     }
+    auto pairs_of = [&](int r) -> int {  // this thread's non-empty splits at r rows
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxPacked / kThreads; ++i)
+        n += (i < nchunks && lens[i] > 0) ? (lens[i] + r - 1) / r : 0;
+      return n;
+    };
+    // block-wide sum; each call k uses its own LDS slots, so no barrier is
+    // needed after it
+    int nsum = 0;
+    auto block_sum = [&](float v0, int v1, float* s0) -> int {
+      for (int o = 32; o > 0; o >>= 1) {
+        v0 += __shfl_xor(v0, o, 64);
+        v1 += __shfl_xor(v1, o, 64);
+      }
+      MLA_LDS int* r = scan + 16 + 8 * nsum++;
+      if (lane == 0) {
+        ((MLA_LDS float*)r)[wave] = v0;
+        r[4 + wave] = v1;
+      }
+      __syncthreads();
+      const MLA_LDS float* rf = (const MLA_LDS float*)r;
+      *s0 = (rf[0] + rf[1]) + (rf[2] + rf[3]);
+      return r[4] + r[5] + r[6] + r[7];
+    };
+    float tot = 0.f;
+    if (a.auto_slots > 0) {
+#pragma unroll
+      for (int i = 0; i < kMaxPacked / kThreads; ++i) tot += i < nchunks ? (float)lens[i] : 0.f;
+    }
+    // the host plan's number of non-empty splits (and the total rows)
+    int total = block_sum(tot, pairs_of(rows), &tot);
+    if (a.auto_slots > 0) {
+      // Rows per split from the lengths themselves: the smallest multiple of
+      // 64 (at least 128) found by a few refinements of total / slots whose
+      // non-empty splits fit auto_slots workgroups (about one per compute
+      // unit), so a ragged batch is not split for its longest sequence.  If
+      // no refinement fits, the host's plan (sized for the longest) stays.
+      const int cap = kMaxSplitTiles * kTile;
+      auto round64 = [&](float r) -> int {
+        const float c = (float)cap;
+        r = r < c ? r : c;
+        int ri = ((int)ceilf(r) + 63) / 64 * 64;
+        ri = ri < 128 ? 128 : ri;
+        return ri < cap ? ri : cap;
+      };
+      int r = round64(tot / (float)a.auto_slots);
+      float unused;
+      int n = r == rows ? total : block_sum(0.f, pairs_of(r), &unused);
+      for (int it = 0; it < 3 && n > a.auto_slots && r < cap; ++it) {
+        r = round64((float)r * (float)n / (float)a.auto_slots);
+        n = block_sum(0.f, pairs_of(r), &unused);
+      }
+      if (n <= a.auto_slots) {
+        rows = r;
+        total = n;
+      }
+    }
+    if (a.auto_slots > 0 && w == 0 && tid == 0) a.part_first[a.B] = rows;  // for the merge
+    int cnts[kMaxPacked / kThreads];
+#pragma unroll
+    for (int i = 0; i < kMaxPacked / kThreads; ++i) cnts[i] = lens[i] > 0 ? (lens[i] + rows - 1) / rows : 0;
     // Workgroups go to the XCDs round robin (w % 8 on this chip).  The
     // workgroups w < total take the pairs: XCD x's n_x = ceil((total - x) / 8)
     // of them take one contiguous run of pairs, so the splits of a query share
     // an XCD's L2 and its query is read from memory once per XCD, not per split.
-    int tsum = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxPacked / kThreads; ++i) tsum += cnts[i];
-    for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
-    if (lane == 0) scan[6 + wave] = tsum;
-    __syncthreads();
-    const int total = scan[6] + scan[7] + scan[8] + scan[9];
     if (w >= total) return;  // no work for this workgroup (uniform)
     int p = w / kXcds;
     for (int x = 0; x < w % kXcds; ++x) p += (total - x + kXcds - 1) / kXcds;
     int carry = 0;
 #pragma unroll
     for (int i = 0; i < kMaxPacked / kThreads; ++i) {
-      if (i * kThreads >= a.B) break;  // uniform
+      if (i >= nchunks) break;  // uniform
       const int q = i * kThreads + tid;
       const int cnt = cnts[i];
       int x = cnt;  // inclusive scan inside the wave
@@ -151,28 +208,39 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       if (p >= excl && p < excl + cnt) {
         scan[4] = q;
         scan[5] = p - excl;
+        scan[10] = excl;
       }
       carry += scan[0] + scan[1] + scan[2] + scan[3];
       __syncthreads();  // the totals are read before the next chunk rewrites them
     }
     b = scan[4];
     split = scan[5];
+    // a device plan packs the slots by pair; the host plan keeps b * S + split
+    slot = a.auto_slots > 0 ? p : b * a.num_splits + split;
+    if (a.auto_slots > 0 && split == 0 && tid == 0) a.part_first[b] = scan[10];
   }
+  // uniform across the workgroup (read from LDS above): keep them scalar.  The
+  // partial slot is only needed after the tile loop: it waits in LDS.
+  b = __builtin_amdgcn_readfirstlane(b);
+  split = __builtin_amdgcn_readfirstlane(split);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  if (tid == 0) votes[8] = slot;
   const int hf = lane >> 5;          // which half of the wave
   const int l32 = lane & 31;
   const int head = wave * 32 + l32;  // this lane's head in the S^T layout
 
   int len = a.seq_lens[b];
   len = len < a.max_len ? len : a.max_len;
-  const int row_begin = split * a.split_rows;
-  int row_end = row_begin + a.split_rows;
+  const int row_begin = split * rows;
+  int row_end = row_begin + rows;
   row_end = row_end < len ? row_end : len;
 
   // Outputs of this (sequence, split): with one partition v_combine and lse
-  // directly, otherwise the fp16 partial [128 heads][512], its exponent and lse.
-  const size_t bs = (size_t)b * a.num_splits + split;
+  // directly, otherwise the fp16 partial [128 heads][512] in its slot, its
+  // exponent and lse.
+  const size_t bs0 = (size_t)__builtin_amdgcn_readfirstlane(slot);
   float* out_lse = a.num_splits == 1 ? (a.lse ? a.lse + (size_t)b * kH + head : nullptr)
-                                     : a.part_lse + bs * kH + head;
+                                     : a.part_lse + bs0 * kH + head;
 
   if (row_begin >= row_end) {  // nothing to attend in this partition
     if (a.num_splits == 1) {
@@ -180,7 +248,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       for (int c = hf * 4; c < kC; c += 8)
         *reinterpret_cast<f32x4_t*>(out_o + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
     } else if (hf == 0) {
-      a.part_exp[bs * kH + head] = 0.f;
+      a.part_exp[bs0 * kH + head] = 0.f;
     }
     if (out_lse && hf == 0) *out_lse = -INFINITY;
     return;
@@ -375,9 +443,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     const char* nsrc = src2;
     const int raw3 = tile_base[it + 3 < ntiles ? it + 3 : 0];
     // the restart votes of tile it - 1, read now, used in the softmax slices
-    typedef int i32x4_t __attribute__((ext_vector_type(4)));
-    i32x4_t vv{0, 0, 0, 0};
-    if (kMode > 0) vv = *(const MLA_LDS i32x4_t*)(votes + ((it - 1) & 1) * 4);
+    // one byte per wave in the word of tile it - 1's parity
+    uint32_t vv = 0;
+    if (kMode > 0) vv = votes[(it - 1) & 1];
     uint32_t qa[4];
     kbases(tile, qa);
     uint32_t va[4];
@@ -391,9 +459,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     auto pread = [&](int x, int kb) {
       return *(const MLA_LDS bf16x8_t*)(p_lds + pbuf + x * (32 * kPRow) + kb * 32);
     };
-    bf16x8_t kf[3];
+    bf16x8_t kf[2];
 #pragma unroll
-    for (int kb = 0; kb < 3; ++kb) kf[kb] = *kaddr(qa, kb);
+    for (int kb = 0; kb < 2; ++kb) kf[kb] = *kaddr(qa, kb);
     bf16x8_t pf[2];  // P fragments (k-block, head block) in MFMA order, two in flight
     if (kMode > 0) {
       pf[0] = pread(0, 0);
@@ -426,8 +494,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       if (n == 0)
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(kf[0]), "v"(qn));
       else
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[n % 3]), "v"(qn));
-      if (n + 3 < kW / 16) kf[n % 3] = *kaddr(qa, n + 3);
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[n % 2]), "v"(qn));
+      if (n + 2 < kW / 16) kf[n % 2] = *kaddr(qa, n + 2);
       if (n >= 24 && n < 24 + 2 * kQLds && (n & 1) == 0) qp[(n - 24) >> 1] = qsrc[((n - 24) >> 1) * 64];
       if (kMode == 0 && n < 32) pv_step(n);  // the V^T reads only
       if (kMode > 0 && (n & 1) && n < 32) pv_step(n >> 1);
@@ -485,7 +553,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
           float lo, hi;
           wave_halves(e, &lo, &hi);
           e = fmaxf(lo, hi);
-          vote = __builtin_amdgcn_readfirstlane(vv.x | vv.y | vv.z | vv.w);
+          vote = __builtin_amdgcn_readfirstlane((int)vv);
           keep = keep && vote == 0;
           if (keep) m_seen = fmaxf(m_seen, e + m_ref);
         }
@@ -610,7 +678,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     pending = softmax(s, 0);
     bool restart = false;
     for (int it = 1;; ++it) {
-      if (lane == 0) votes[((it - 1) & 1) * 4 + wave] = __ballot(pending) != 0;
+      if (lane == 0)
+        ((MLA_LDS uint8_t*)(votes + ((it - 1) & 1)))[wave] = __ballot(pending) != 0 ? 1 : 0;
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's copies of tile it
       zero_tail(it);
       __syncthreads();
@@ -645,6 +714,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   const float l = l_lo + l_hi;
   if (hf == 0) l_heads[head] = l;
   __syncthreads();
+  const size_t bs = (size_t)__builtin_amdgcn_readfirstlane(votes[8]);  // the partial slot
   if (a.num_splits == 1) {
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
@@ -770,14 +840,21 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   const int b = blockIdx.y;
   const int h = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  // splits past ceil(len / split_rows) are empty: with a packed plan no
-  // workgroup wrote them, so they are not read
+  // Query b's ceil(len / rows) partials sit in consecutive slots from
+  // part_first[b] (rows, chosen by the split kernel, in part_first[B]); no
+  // workgroup wrote the slots of empty splits, so they are not read.
   int len = a.seq_lens[b];
   len = len < a.max_len ? len : a.max_len;
-  int S = len > 0 ? (len + a.split_rows - 1) / a.split_rows : 0;
-  S = S < a.num_splits ? S : a.num_splits;
-  const float* lse_s = a.part_lse + (size_t)b * a.num_splits * kH + h;  // stride kH over s
-  const float* exp_s = a.part_exp + (size_t)b * a.num_splits * kH + h;
+  // (with the host's plan: split_rows, and slot b * num_splits + split)
+  int rows = a.split_rows, first_raw = b * a.num_splits;
+  if (a.auto_slots > 0) {
+    rows = a.part_first[a.B];
+    first_raw = a.part_first[b];  // both loads in flight together
+  }
+  const int S = len > 0 ? (len + rows - 1) / rows : 0;
+  const size_t first = S > 0 ? (size_t)first_raw : 0;
+  const float* lse_s = a.part_lse + first * kH + h;  // stride kH over s
+  const float* exp_s = a.part_exp + first * kH + h;
 
   float m = -INFINITY;
   bool nan_lse = false;  // a bad table entry: NaN through the merge, as above
@@ -801,7 +878,7 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   const float inv = 1.0f / wsum;
 
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-  const _Float16* src = a.part_oh + ((size_t)b * a.num_splits * kH + h) * kC + lane * 8;
+  const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
   const size_t sstride = (size_t)kH * kC;
   f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 64) {

@@ -89,11 +89,16 @@ struct AttnArgs {
   float* v_combine;         // [B, H, C]
   float* lse;               // [B, H] or null
   float* part_o;            // [B, S, H, C] fp32 partials (fp32 kernel, S > 1)
-  _Float16* part_oh;        // [B, S, H, C] fp16 partials * 2^-part_exp (MFMA kernel, S > 1)
-  float* part_exp;          // [B, S, H]    the exponent e of each fp16 partial
+  _Float16* part_oh;        // [B*S slots, H, C] fp16 partials * 2^-part_exp (MFMA kernel, S > 1)
+  float* part_exp;          // [B*S slots, H]    the exponent e of each fp16 partial
   float* part_lse;          // [B, S, H]   (S > 1)
+  // MFMA kernel, S > 1: partials are kept in slots; part_first[b] is query b's
+  // first slot and part_first[B] the rows per split the split kernel used
+  int32_t* part_first;      // [B + 1]
   int32_t B, H, C, R, block, max_blocks, num_blocks, num_seqs;
   int32_t max_len, split_rows, num_splits;
+  int32_t auto_slots;       // > 0: the split kernel sizes the splits from the lengths,
+                            // at most auto_slots non-empty splits in all (MFMA kernel)
   float scale_log2;         // softmax_scale * log2(e)
 };
 
