@@ -103,10 +103,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   int b = blockIdx.y;
   int rows = a.split_rows;  // rows per split
   int slot = b * a.num_splits + split;  // partial slot of this (query, split)
-  if (a.num_splits > 1 && a.B <= kMaxPacked) {
+  if (a.num_splits > 1 && a.B > 1 && a.B <= kMaxPacked) {
     // Packed plan: the non-empty (query, split) pairs, query-major, go to the
     // first workgroups in dispatch order, so a ragged batch's work starts at
-    // once on every compute unit and the empty workgroups leave.  Query b has
+    // once on every compute unit and the empty workgroups leave (a single
+    // query keeps the direct mapping: its splits are all non-empty, or empty
+    // at the end only).  Query b has
     // ceil(len_b / rows) non-empty splits; an exclusive scan over the queries
     // finds this workgroup's pair, whose index is also its partial slot.
     const int w = blockIdx.y * gridDim.x + blockIdx.x;
@@ -715,21 +717,40 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   if (hf == 0) l_heads[head] = l;
   __syncthreads();
   const size_t bs = (size_t)__builtin_amdgcn_readfirstlane(votes[8]);  // the partial slot
+  // The outputs leave through LDS, one head block at a time: each wave
+  // transposes its 128 columns of 32 heads in its own part of the tile
+  // buffers (free since the barrier above; LDS operations of one wave run in
+  // order, so the area is reused from block to block without a barrier), so
+  // that every store instruction writes whole 128-byte lines of one head's
+  // consecutive columns.  Straight from the accumulator layout a store would
+  // put 16 or 32 bytes into each of 32 rows, and a lone workgroup's stores
+  // would then take longer than several of its tiles.  16-byte chunks are
+  // XOR-swizzled by head, so neither side has more bank conflicts than its
+  // width requires.
+  MLA_LDS char* stage = tiles + wave * 16384;
   if (a.num_splits == 1) {
+    // fp32 v_combine: head r's 128 columns are 32 chunks of 4 floats (chunk c
+    // at slot c ^ r); read back as 2 heads x 512 bytes per instruction
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       const float inv_l = bad ? NAN : 1.0f / l_heads[hb * 32 + l32];
-      float* dst = a.v_combine + (size_t)b * kH * kC + (size_t)(hb * 32 + l32) * kC + wave * 128;
 #pragma unroll
       for (int cbl = 0; cbl < 4; ++cbl) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = cbl * 32 + q4 * 8 + hf * 4;
+          const int chunk = cbl * 8 + q4 * 2 + hf;  // columns 4 * chunk .. + 3
           const f32x16_t& ob = o[cbl * 4 + hb];
           f32x4_t v{ob[4 * q4 + 0] * inv_l, ob[4 * q4 + 1] * inv_l, ob[4 * q4 + 2] * inv_l,
                     ob[4 * q4 + 3] * inv_l};
-          *reinterpret_cast<f32x4_t*>(dst + col) = v;
+          *(MLA_LDS f32x4_t*)(stage + l32 * 512 + ((chunk ^ l32) << 4)) = v;
         }
+      }
+      float* dst = a.v_combine + ((size_t)b * kH + hb * 32) * kC + wave * 128 + l32 * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 2 * i + hf;
+        const f32x4_t v = *(const MLA_LDS f32x4_t*)(stage + r * 512 + ((l32 ^ r) << 4));
+        *reinterpret_cast<f32x4_t*>(dst + (size_t)r * kC) = v;
       }
     }
   } else {
@@ -761,20 +782,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       const int e = (amax >= 32768.f && amax <= 3.0e38f) ? lg - 14 : 0;
       const float scale = __uint_as_float((uint32_t)(127 - e) << 23);
       const float inv_l = bad ? NAN : scale / l_heads[h];
-      _Float16* dst = a.part_oh + (bs * kH + h) * kC + wave * 128;
+      // head r's 128 columns are 16 chunks of 8 halves (chunk c at slot
+      // c ^ (r & 15)), each written as two 4-half pieces by the lane pair
+      // hf = 0, 1; read back as 4 heads x 256 bytes per instruction
 #pragma unroll
       for (int cbl = 0; cbl < 4; ++cbl) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = cbl * 32 + q4 * 8 + hf * 4;
+          const int chunk = cbl * 4 + q4;  // columns 8 * chunk .. + 7
           const f32x16_t& ob = o[cbl * 4 + hb];
           typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
           const f16x4_t v{(_Float16)(ob[4 * q4 + 0] * inv_l), (_Float16)(ob[4 * q4 + 1] * inv_l),
                           (_Float16)(ob[4 * q4 + 2] * inv_l), (_Float16)(ob[4 * q4 + 3] * inv_l)};
-          *reinterpret_cast<f16x4_t*>(dst + col) = v;
+          *(MLA_LDS f16x4_t*)(stage + l32 * 256 + ((chunk ^ (l32 & 15)) << 4) + hf * 8) = v;
         }
       }
       if (wave == 0 && hf == 0) a.part_exp[bs * kH + h] = (float)e;
+      _Float16* dst = a.part_oh + (bs * kH + hb * 32) * kC + wave * 128 + (lane & 15) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t v = *(const MLA_LDS u32x4_t*)(stage + r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+        *reinterpret_cast<u32x4_t*>(dst + (size_t)r * kC) = v;
+      }
     }
   }
   if (out_lse && hf == 0) *out_lse = bad ? NAN : (m_ref + log2f(l)) * kLn2;
