@@ -218,7 +218,11 @@ int mla_absorb_q(const mla_dims* dims, int32_t batch, const float* q_in,
  *                values above it are clamped to it on the device
  *   softmax_scale  multiplies the fp32 scores
  *   split_rows   rows per split-K partition (multiple of 64; at most 32768
- *                on a bf16 cache), 0 = automatic
+ *                on a bf16 cache), 0 = automatic: on a bf16 cache with 2 to
+ *                4096 queries the split kernel sizes the splits from the
+ *                lengths on the device (about one non-empty split per compute
+ *                unit, within the host plan's workspace), else the host plan
+ *                over batch * max_seq_len rows
  *   v_combine    device float [batch, H, C], written
  *   lse          device float [batch, H] or NULL: natural-log sum of exp of
  *                the scaled scores
@@ -248,6 +252,55 @@ int mla_decode_attn(const mla_dims* dims, int32_t batch, const void* q_abs,
 int mla_out_proj(const mla_dims* dims, int32_t batch, const float* v_combine,
                  const mla_weight* kv_b, const mla_weight* o_proj, float* out,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* The weights of one MLA attention layer for mla_decode_layer. */
+typedef struct mla_layer {
+  const mla_weight* kv_a;       /* as in mla_cache_append (ignored if hidden == 0) */
+  const mla_weight* kv_a_norm;  /* as in mla_cache_append */
+  const mla_weight* q_a;        /* as in mla_absorb_q, or NULL */
+  const mla_weight* q_a_norm;   /* with q_a */
+  const mla_weight* q_b;        /* with q_a */
+  const mla_weight* kv_b;       /* as in mla_absorb_q and mla_out_proj */
+  const mla_weight* o_proj;     /* as in mla_out_proj, or NULL */
+  const mla_rope* rope;         /* shared by the k_pe and q_pe rotations */
+} mla_layer;
+
+/* mla_decode_layer -- the whole decode step of one layer in one call, the
+ * forward the pages encode as a single command buffer (moeflux
+ * mla_attn_forward.rs, mla_attn_layer_forward_gpu: kv append, Q chain,
+ * absorb, SDPA over the latent cache, per-head W_UV, o_proj, one commit;
+ * turbospark deepseek2/attn.rs, encode_mla_attention_block).  Its results are
+ * those of mla_cache_append, mla_absorb_q, mla_decode_attn and mla_out_proj
+ * called in that order on `stream` with the same arguments:
+ *   x          as mla_cache_append's x; with q_a it is also mla_absorb_q's
+ *              q_in (the hidden state)
+ *   q_in       mla_absorb_q's q_in when layer->q_a is NULL (per-head q
+ *              [batch, H, N+R]); ignored otherwise
+ *   seq_lens   lengths after this step's append (positions[b] + 1 for a
+ *              sequence decoding at positions[b])
+ *   q_abs      device [batch, H, W] of cache_dtype, written (the latent query)
+ *   v_combine, lse, out   written as by mla_decode_attn and mla_out_proj
+ *   ws         device workspace of mla_layer_workspace_bytes() bytes
+ * All kernels go on the one stream, with no host synchronisation, so the call
+ * can be captured into a HIP graph.  With 4-bit kv_a and q_a of one type
+ * (hidden > 0, q_a given) the front runs fused: one fp16 pack of x, kv_a and
+ * q_a in one launch, the append and the q-latent RMSNorm in one launch; and
+ * when W_UV runs on the MFMA path with more than one split the attention
+ * merge also writes W_UV's packed input.  On the 4-bit DeepSeek-V3 layer that
+ * is 9 kernels: pack, kv_a + q_a, append + norm, q_b, absorb, attention,
+ * merge, W_UV, o_proj.  Each fused launch does the same arithmetic as the
+ * separate calls.
+ * Errors: those of the four calls, all checked before anything is enqueued. */
+int mla_decode_layer(const mla_dims* dims, int32_t batch, const float* x, const float* q_in,
+                     const mla_layer* layer, const int32_t* positions, const mla_cache* cache,
+                     const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                     int32_t split_rows, void* q_abs, float* v_combine, float* lse, float* out,
+                     int32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of mla_decode_layer for this geometry, batch, max_seq_len
+ * and split_rows (0 = automatic).  Returns 0 for invalid dims. */
+size_t mla_layer_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
+                                 int32_t split_rows);
 
 /* mla_decode_attn_noalloc -- mla_decode_attn for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
@@ -346,9 +399,10 @@ int mla_attn_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
  * rows, at least 128) whose non-empty workgroups fit one per compute unit of
  * the current device.  Pass *rows_per_split as split_rows to mla_decode_attn
  * or mla_attn_tokens (and to mla_workspace_bytes).  A ragged batch then runs
- * as one wave of workgroups of nearly equal size; the automatic plan sizes
- * every split for the longest sequence.  Falls back to the automatic plan of
- * the longest length when no split fits.  The flash-decoding split itself is
+ * as one wave of workgroups of nearly equal size (the automatic plan of a
+ * bf16 cache does the same on the device; the f32 kernel's sizes every split
+ * for the longest sequence).  Falls back to the automatic plan of the longest
+ * length when no split fits.  The flash-decoding split itself is
  * the long-context step of the pages' MLA decode (turbospark deepseek2
  * attn.rs; moeflux mla_attn_forward.rs, SDPA over the latent cache).
  * Errors: NULL, DIMS (a negative length), UNSUPPORTED. */

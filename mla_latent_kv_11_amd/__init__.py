@@ -30,7 +30,8 @@ MLA_DEV_POS_RANGE, MLA_DEV_BAD_BLOCK, MLA_DEV_BAD_SEQ = 1, 2, 4
 EXPORTED = ("mla_yarn_tables", "mla_cache_append", "mla_absorb_q", "mla_decode_attn",
             "mla_out_proj", "mla_cache_append_tokens", "mla_attn_tokens",
             "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan",
-            "mla_attn_plan_lens", "mla_status_str", "mla_decode_attn_noalloc")
+            "mla_attn_plan_lens", "mla_status_str", "mla_decode_attn_noalloc",
+            "mla_decode_layer", "mla_layer_workspace_bytes")
 MLA_NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
@@ -61,6 +62,13 @@ class CRope(ctypes.Structure):
 class CCache(ctypes.Structure):
     _fields_ = [("pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+class CLayer(ctypes.Structure):
+    _fields_ = [("kv_a", ctypes.POINTER(CWeight)), ("kv_a_norm", ctypes.POINTER(CWeight)),
+                ("q_a", ctypes.POINTER(CWeight)), ("q_a_norm", ctypes.POINTER(CWeight)),
+                ("q_b", ctypes.POINTER(CWeight)), ("kv_b", ctypes.POINTER(CWeight)),
+                ("o_proj", ctypes.POINTER(CWeight)), ("rope", ctypes.POINTER(CRope))]
 
 
 class CYarn(ctypes.Structure):
@@ -115,6 +123,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_attn_plan_lens": ([PD, I32, P, ctypes.POINTER(I32), ctypes.POINTER(I32)],
                                ctypes.c_int),
         "mla_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "mla_decode_layer": ([PD, I32, P, P, ctypes.POINTER(CLayer), P, PC, P, I32,
+                              ctypes.c_float, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "mla_layer_workspace_bytes": ([PD, I32, I32, I32], SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -348,3 +359,37 @@ def out_proj(dims: Dims, v_combine, kv_b: Weight, out, o_proj: Optional[Weight] 
                           ws.numel() * ws.element_size() if ws is not None else 0,
                           _stream(stream))
     _check(st, "mla_out_proj")
+
+
+def layer_workspace_bytes(dims: Dims, batch: int, max_seq_len: int, split_rows: int = 0) -> int:
+    return int(load_library().mla_layer_workspace_bytes(ctypes.byref(dims.c()), batch,
+                                                        max_seq_len, split_rows))
+
+
+def decode_layer(dims: Dims, x, positions, pool, table, seq_lens, max_seq_len: int,
+                 softmax_scale: float, q_abs, v_combine, out, *, kv_a: Optional[Weight],
+                 kv_a_norm: Weight, kv_b: Weight, inv_freq, rope_mscale: float,
+                 q_a: Optional[Weight] = None, q_a_norm: Optional[Weight] = None,
+                 q_b: Optional[Weight] = None, o_proj: Optional[Weight] = None, q_in=None,
+                 lse=None, split_rows: int = 0, dev_status=None, ws=None, stream=None) -> None:
+    """The whole decode step in one call (mla_decode_layer): the results of
+    cache_append, absorb_q, decode_attn and out_proj in that order."""
+    lib = load_library()
+    rope = CRope(_ptr(inv_freq), float(rope_mscale))
+    cw = {k: (w.c() if w is not None else None)
+          for k, w in (("kv_a", kv_a), ("kv_a_norm", kv_a_norm), ("q_a", q_a),
+                       ("q_a_norm", q_a_norm), ("q_b", q_b), ("kv_b", kv_b), ("o_proj", o_proj))}
+    null = ctypes.POINTER(CWeight)()
+    layer = CLayer(*[ctypes.pointer(cw[k]) if cw[k] is not None else null
+                     for k in ("kv_a", "kv_a_norm", "q_a", "q_a_norm", "q_b", "kv_b", "o_proj")],
+                   ctypes.pointer(rope))
+    cache = _cache(pool, table)
+    B = int(positions.shape[0])
+    st = lib.mla_decode_layer(ctypes.byref(dims.c()), B, _ptr(x), _ptr(q_in), ctypes.byref(layer),
+                              _ptr(positions), ctypes.byref(cache), _ptr(seq_lens),
+                              int(max_seq_len), float(softmax_scale), int(split_rows),
+                              _ptr(q_abs), _ptr(v_combine), _ptr(lse), _ptr(out),
+                              _ptr(dev_status), _ptr(ws),
+                              ws.numel() * ws.element_size() if ws is not None else 0,
+                              _stream(stream))
+    _check(st, "mla_decode_layer")

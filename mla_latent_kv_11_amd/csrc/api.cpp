@@ -158,9 +158,16 @@ size_t ws_attn(const mla_dims* d, int32_t B, int32_t splits) {
   if (d->cache_dtype != MLA_BF16) return ws_attn_o(d, B, splits) + lse;
   return ws_attn_o(d, B, splits) + 2 * lse + align_up(((size_t)B + 1) * 4);
 }
+// mla_decode_layer: the regions of the four calls side by side (append,
+// absorb, attention, out), each a multiple of kAlign.
+size_t ws_layer(const mla_dims* d, int32_t B, int32_t splits);
 size_t ws_out(const mla_dims* d, int32_t B) {
   const size_t vc = align_up(packed_bytes(d->num_heads, B, d->kv_lora));
   return vc + (d->hidden > 0 ? align_up((size_t)((B + 31) / 32) * 32 * d->num_heads * d->v_head * 4) : 0);
+}
+
+size_t ws_layer(const mla_dims* d, int32_t B, int32_t splits) {
+  return ws_append(d, B) + ws_absorb(d, B) + ws_attn(d, B, splits) + ws_out(d, B);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -298,12 +305,41 @@ int mla_attn_plan_lens(const mla_dims* d, int32_t B, const int32_t* host_lens,
   return plan(d, B, max_len, (int32_t)(lo * 64), rows_per_split, num_splits);
 }
 
-// token_seq null: token b owns table row b (num_seqs = B).
+// Arguments of the append kernels for pre-norm rows given as S partial sums.
+static AppendArgs append_args(const mla_dims* d, int32_t B, const float* kv_pre, int kv_splits,
+                              const mla_weight* kv_a_norm, const mla_rope* rope,
+                              const int32_t* positions, const int32_t* token_seq, int32_t num_seqs,
+                              const mla_cache* cache, int32_t* dev_status) {
+  AppendArgs a{};
+  a.kv_pre = kv_pre;
+  a.kv_splits = kv_splits;
+  a.kv_split_stride = (int64_t)B * (d->kv_lora + d->qk_rope);
+  a.gamma = view(kv_a_norm);
+  a.inv_freq = rope->inv_freq;
+  a.rope_mscale = rope->mscale;
+  a.positions = positions;
+  a.pool = cache->pool;
+  a.table = cache->block_table;
+  a.q_seq = token_seq;
+  a.num_seqs = num_seqs;
+  a.dev_status = dev_status;
+  a.B = B;
+  a.C = d->kv_lora;
+  a.R = d->qk_rope;
+  a.block = d->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  a.num_blocks = cache->num_blocks;
+  a.cache_dtype = d->cache_dtype;
+  a.eps = d->rms_eps;
+  return a;
+}
+
+// token_seq null: token b owns table row b (num_seqs = B).  dry: validate only.
 static int cache_append_impl(const mla_dims* d, int32_t B, const float* x, const mla_weight* kv_a,
                              const mla_weight* kv_a_norm, const mla_rope* rope,
                              const int32_t* positions, const int32_t* token_seq, int32_t num_seqs,
                              const mla_cache* cache, int32_t* dev_status, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             size_t ws_bytes, void* stream, bool dry) {
   int st = dims_status(d);
   if (st) return st;
   if (B < 0) return MLA_ERR_DIMS;
@@ -317,7 +353,7 @@ static int cache_append_impl(const mla_dims* d, int32_t B, const float* x, const
   if (d->hidden > 0 && (st = check_weight(kv_a, W, d->hidden, true))) return st;
   const size_t need = ws_append(d, B);
   if (need && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
-  if (B == 0) return MLA_OK;
+  if (dry || B == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const float* kv_pre = x;
@@ -344,27 +380,8 @@ static int cache_append_impl(const mla_dims* d, int32_t B, const float* x, const
     if ((st = hip_status(launch_gemm_nt(g, gemm_max_splits(d->hidden), &kv_splits, s)))) return st;
     kv_pre = g.y;
   }
-  AppendArgs a{};
-  a.kv_pre = kv_pre;
-  a.kv_splits = kv_splits;
-  a.kv_split_stride = (int64_t)B * W;
-  a.gamma = view(kv_a_norm);
-  a.inv_freq = rope->inv_freq;
-  a.rope_mscale = rope->mscale;
-  a.positions = positions;
-  a.pool = cache->pool;
-  a.table = cache->block_table;
-  a.q_seq = token_seq;
-  a.num_seqs = num_seqs;
-  a.dev_status = dev_status;
-  a.B = B;
-  a.C = d->kv_lora;
-  a.R = d->qk_rope;
-  a.block = d->block_size;
-  a.max_blocks = cache->max_blocks_per_seq;
-  a.num_blocks = cache->num_blocks;
-  a.cache_dtype = d->cache_dtype;
-  a.eps = d->rms_eps;
+  const AppendArgs a = append_args(d, B, kv_pre, kv_splits, kv_a_norm, rope, positions, token_seq,
+                                   num_seqs, cache, dev_status);
   return hip_status(launch_append_rows(a, s));
 }
 
@@ -373,7 +390,7 @@ int mla_cache_append(const mla_dims* d, int32_t B, const float* x, const mla_wei
                      const mla_cache* cache, int32_t* dev_status, void* ws, size_t ws_bytes,
                      void* stream) {
   return cache_append_impl(d, B, x, kv_a, kv_a_norm, rope, positions, nullptr, B, cache,
-                           dev_status, ws, ws_bytes, stream);
+                           dev_status, ws, ws_bytes, stream, false);
 }
 
 int mla_cache_append_tokens(const mla_dims* d, int32_t n_tokens, const float* x,
@@ -383,13 +400,71 @@ int mla_cache_append_tokens(const mla_dims* d, int32_t n_tokens, const float* x,
                             int32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
   if (!token_seq) return MLA_ERR_NULL;
   return cache_append_impl(d, n_tokens, x, kv_a, kv_a_norm, rope, positions, token_seq, num_seqs,
-                           cache, dev_status, ws, ws_bytes, stream);
+                           cache, dev_status, ws, ws_bytes, stream, false);
 }
 
-int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weight* q_a,
-                 const mla_weight* q_a_norm, const mla_weight* q_b, const mla_weight* kv_b,
-                 const mla_rope* rope, const int32_t* positions, void* q_abs, void* ws,
-                 size_t ws_bytes, void* stream) {
+static AbsorbArgs absorb_args(const mla_dims* d, int32_t B, const float* q, const mla_weight* kv_b,
+                              const mla_rope* rope, const int32_t* positions, void* q_abs) {
+  AbsorbArgs a{};
+  a.q = q;
+  a.kv_b = view(kv_b);
+  a.inv_freq = rope->inv_freq;
+  a.rope_mscale = rope->mscale;
+  a.positions = positions;
+  a.q_abs = q_abs;
+  a.B = B;
+  a.H = d->num_heads;
+  a.N = d->qk_nope;
+  a.R = d->qk_rope;
+  a.V = d->v_head;
+  a.C = d->kv_lora;
+  a.cache_dtype = d->cache_dtype;
+  return a;
+}
+
+// Workspace regions of the q chain (mla_absorb_q): x packed, q_a partial sums,
+// q latent packed, q fp32.
+struct AbsorbWs {
+  _Float16* x_pk;
+  float* q_part;
+  _Float16* q_lat_pk;
+  float* q_full;
+};
+static AbsorbWs absorb_ws(const mla_dims* d, int32_t B, void* ws) {
+  char* base = static_cast<char*>(ws);
+  AbsorbWs r{};
+  r.x_pk = reinterpret_cast<_Float16*>(base);
+  base += align_up(packed_bytes(1, B, d->hidden));
+  r.q_part = reinterpret_cast<float*>(base);
+  base += ws_q_part(d, B);
+  r.q_lat_pk = reinterpret_cast<_Float16*>(base);
+  base += align_up(packed_bytes(1, B, d->q_lora));
+  r.q_full = reinterpret_cast<float*>(base);
+  return r;
+}
+
+// q_b of the q chain: q latent (packed on the MFMA path, else the normalised
+// fp32 partials in place) -> q fp32 [B, H, N+R].
+static GemmArgs q_b_gemm(const mla_dims* d, int32_t B, const mla_weight* q_b, const AbsorbWs& r) {
+  GemmArgs g2{};
+  g2.w = view(q_b);
+  g2.x = r.q_part;  // normalised in place on the fp32 path
+  g2.x_b = d->q_lora;
+  g2.y = r.q_full;
+  g2.y_b = (int64_t)d->num_heads * (d->qk_nope + d->qk_rope);
+  g2.O = d->num_heads * (d->qk_nope + d->qk_rope);
+  g2.K = d->q_lora;
+  g2.B = B;
+  g2.Z = 1;
+  if (gemm_mfma_ok(g2)) g2.xp = r.q_lat_pk;
+  return g2;
+}
+
+// dry: validate only.
+static int absorb_impl(const mla_dims* d, int32_t B, const float* q_in, const mla_weight* q_a,
+                       const mla_weight* q_a_norm, const mla_weight* q_b, const mla_weight* kv_b,
+                       const mla_rope* rope, const int32_t* positions, void* q_abs, void* ws,
+                       size_t ws_bytes, void* stream, bool dry) {
   int st = dims_status(d);
   if (st) return st;
   if (B < 0) return MLA_ERR_DIMS;
@@ -407,78 +482,60 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
   } else if (q_b) {
     return MLA_ERR_DIMS;  // q_b without q_a
   }
-  if (B == 0) return MLA_OK;
+  if (dry || B == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const float* q = q_in;
   if (q_a) {
-    char* base = static_cast<char*>(ws);
-    _Float16* x_pk = reinterpret_cast<_Float16*>(base);
-    base += align_up(packed_bytes(1, B, d->hidden));
-    float* q_part = reinterpret_cast<float*>(base);
-    base += ws_q_part(d, B);
-    _Float16* q_lat_pk = reinterpret_cast<_Float16*>(base);
-    base += align_up(packed_bytes(1, B, d->q_lora));
-    float* q_full = reinterpret_cast<float*>(base);
+    const AbsorbWs r = absorb_ws(d, B, ws);
     GemmArgs g{};
     g.w = view(q_a);
     g.x = q_in;
     g.x_b = d->hidden;
-    g.y = q_part;
+    g.y = r.q_part;
     g.y_b = d->q_lora;
     g.y_s = (int64_t)B * d->q_lora;
     g.O = d->q_lora;
     g.K = d->hidden;
     g.B = B;
     g.Z = 1;
-    GemmArgs g2{};
-    g2.w = view(q_b);
-    g2.x = q_part;  // normalised in place on the fp32 path
-    g2.x_b = d->q_lora;
-    g2.y = q_full;
-    g2.y_b = (int64_t)H * (N + R);
-    g2.O = H * (N + R);
-    g2.K = d->q_lora;
-    g2.B = B;
-    g2.Z = 1;
-    if (gemm_mfma_ok(g2)) g2.xp = q_lat_pk;
+    const GemmArgs g2 = q_b_gemm(d, B, q_b, r);
     if (gemm_mfma_ok(g)) {
-      g.xp = x_pk;
-      if ((st = hip_status(launch_pack_f16(q_in, d->hidden, 0, 1, B, d->hidden, x_pk, s))))
+      g.xp = r.x_pk;
+      if ((st = hip_status(launch_pack_f16(q_in, d->hidden, 0, 1, B, d->hidden, r.x_pk, s))))
         return st;
     }
     int splits = 1;
     if ((st = hip_status(launch_gemm_nt(g, gemm_max_splits(d->hidden), &splits, s)))) return st;
-    if ((st = hip_status(launch_rmsnorm_rows(q_part, splits, g.y_s, B, d->q_lora, d->q_lora,
+    if ((st = hip_status(launch_rmsnorm_rows(r.q_part, splits, g.y_s, B, d->q_lora, d->q_lora,
                                              view(q_a_norm), d->rms_eps,
-                                             g2.xp ? nullptr : q_part,
-                                             g2.xp ? q_lat_pk : nullptr, s))))
+                                             g2.xp ? nullptr : r.q_part,
+                                             g2.xp ? r.q_lat_pk : nullptr, s))))
       return st;
     if ((st = hip_status(launch_gemm_nt(g2, 1, &splits, s)))) return st;
-    q = q_full;
+    q = r.q_full;
   }
-  AbsorbArgs a{};
-  a.q = q;
-  a.kv_b = view(kv_b);
-  a.inv_freq = rope->inv_freq;
-  a.rope_mscale = rope->mscale;
-  a.positions = positions;
-  a.q_abs = q_abs;
-  a.B = B;
-  a.H = H;
-  a.N = N;
-  a.R = R;
-  a.V = V;
-  a.C = C;
-  a.cache_dtype = d->cache_dtype;
-  return hip_status(launch_absorb(a, s));
+  return hip_status(launch_absorb(absorb_args(d, B, q, kv_b, rope, positions, q_abs), s));
 }
 
-// token_seq null: query b reads table row b (num_seqs = B).
+int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weight* q_a,
+                 const mla_weight* q_a_norm, const mla_weight* q_b, const mla_weight* kv_b,
+                 const mla_rope* rope, const int32_t* positions, void* q_abs, void* ws,
+                 size_t ws_bytes, void* stream) {
+  return absorb_impl(d, B, q_in, q_a, q_a_norm, q_b, kv_b, rope, positions, q_abs, ws, ws_bytes,
+                     stream, false);
+}
+
+// token_seq null: query b reads table row b (num_seqs = B).  dry: validate
+// only.  vc_pk: where the merge of the MFMA kernel's split partials also
+// writes v_combine in the packed fp16 layout of W_UV's input (*vc_written
+// says whether it did: only with more than one split on a bf16 cache).
 static int attn_impl(const mla_dims* d, int32_t B, const void* q_abs, const mla_cache* cache,
                      const int32_t* token_seq, int32_t num_seqs, const int32_t* seq_lens,
                      int32_t max_len, float softmax_scale, int32_t split_rows, float* v_combine,
-                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+                     float* lse, void* ws, size_t ws_bytes, void* stream, bool dry,
+                     _Float16* vc_pk = nullptr, bool* vc_written = nullptr) {
+  if (vc_written) *vc_written = false;
   int st = dims_status(d);
   if (st) return st;
   if (B < 0 || max_len < 0) return MLA_ERR_DIMS;
@@ -500,7 +557,7 @@ static int attn_impl(const mla_dims* d, int32_t B, const void* q_abs, const mla_
   if ((st = plan(d, B, max_len, split_rows, &rows, &splits))) return st;
   const size_t need = ws_attn(d, B, splits);
   if (need && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
-  if (B == 0) return MLA_OK;
+  if (dry || B == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   AttnArgs a{};
@@ -529,6 +586,8 @@ static int attn_impl(const mla_dims* d, int32_t B, const void* q_abs, const mla_
         const int64_t slots = (int64_t)B * splits, cus = device_cus();
         a.auto_slots = (int32_t)(slots < cus ? slots : cus);
       }
+      a.vc_pk = vc_pk;
+      if (vc_written) *vc_written = vc_pk != nullptr;
     }
   }
   a.B = B;
@@ -553,7 +612,7 @@ int mla_decode_attn(const mla_dims* d, int32_t B, const void* q_abs, const mla_c
                     int32_t split_rows, float* v_combine, float* lse, void* ws, size_t ws_bytes,
                     void* stream) {
   return attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
-                   v_combine, lse, ws, ws_bytes, stream);
+                   v_combine, lse, ws, ws_bytes, stream, false);
 }
 
 int mla_decode_attn_noalloc(const mla_dims* d, int32_t B, const void* q_abs,
@@ -569,7 +628,7 @@ int mla_decode_attn_noalloc(const mla_dims* d, int32_t B, const void* q_abs,
   void* ws = nullptr;
   if (splits > 1 && !(ws = scratch_ptr())) return MLA_ERR_HIP;
   return attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
-                   v_combine, lse, ws, ws ? kScratchBytes : 0, stream);
+                   v_combine, lse, ws, ws ? kScratchBytes : 0, stream, false);
 }
 
 int mla_attn_tokens(const mla_dims* d, int32_t n_tokens, const void* q_abs,
@@ -579,27 +638,17 @@ int mla_attn_tokens(const mla_dims* d, int32_t n_tokens, const void* q_abs,
                     void* stream) {
   if (!token_seq) return MLA_ERR_NULL;
   return attn_impl(d, n_tokens, q_abs, cache, token_seq, num_seqs, seq_lens, max_len,
-                   softmax_scale, split_rows, v_combine, lse, ws, ws_bytes, stream);
+                   softmax_scale, split_rows, v_combine, lse, ws, ws_bytes, stream, false);
 }
 
-int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla_weight* kv_b,
-                 const mla_weight* o_proj, float* out, void* ws, size_t ws_bytes, void* stream) {
-  int st = dims_status(d);
-  if (st) return st;
-  if (B < 0) return MLA_ERR_DIMS;
+// W_UV (per head, z = head) and the optional o_proj of mla_out_proj over the
+// workspace at base (may be null when nothing runs on the MFMA path): v_combine
+// packed at the start, then the per-head outputs.
+static void out_gemms(const mla_dims* d, int32_t B, const float* v_combine, const mla_weight* kv_b,
+                      const mla_weight* o_proj, float* out, char* base, GemmArgs* pg, GemmArgs* pg2) {
   const int H = d->num_heads, N = d->qk_nope, V = d->v_head, C = d->kv_lora;
-  if (!v_combine || !out) return MLA_ERR_NULL;
-  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true, true))) return st;
-  if (o_proj) {
-    if (d->hidden < 1) return MLA_ERR_DIMS;
-    if ((st = check_weight(o_proj, d->hidden, (int64_t)H * V, true))) return st;
-    if (!ws || ws_bytes < ws_out(d, B)) return MLA_ERR_WORKSPACE;
-  }
-  if (B == 0) return MLA_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* base = static_cast<char*>(ws);
   _Float16* vc_pk = reinterpret_cast<_Float16*>(base);
-  void* heads = base + align_up(packed_bytes(H, B, C));
+  void* heads = base ? base + align_up(packed_bytes(H, B, C)) : nullptr;
   GemmArgs g{};
   g.w = view(kv_b);
   g.w_row0 = N;
@@ -633,16 +682,172 @@ int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla
       g.yp_K = (int64_t)H * V;
     }
   }
-  if (gemm_mfma_ok(g)) {
+  if (gemm_mfma_ok(g)) g.xp = vc_pk;
+  *pg = g;
+  *pg2 = g2;
+}
+
+// dry: validate only.  vc_ready: the packed v_combine is already at the start
+// of the workspace (written by the attention merge).
+static int out_proj_impl(const mla_dims* d, int32_t B, const float* v_combine,
+                         const mla_weight* kv_b, const mla_weight* o_proj, float* out, void* ws,
+                         size_t ws_bytes, void* stream, bool dry, bool vc_ready) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (B < 0) return MLA_ERR_DIMS;
+  const int H = d->num_heads, N = d->qk_nope, V = d->v_head, C = d->kv_lora;
+  if (!v_combine || !out) return MLA_ERR_NULL;
+  if ((st = check_weight(kv_b, (int64_t)H * (N + V), C, true, true))) return st;
+  if (o_proj) {
+    if (d->hidden < 1) return MLA_ERR_DIMS;
+    if ((st = check_weight(o_proj, d->hidden, (int64_t)H * V, true))) return st;
     if (!ws || ws_bytes < ws_out(d, B)) return MLA_ERR_WORKSPACE;
-    g.xp = vc_pk;
-    if ((st = hip_status(launch_pack_f16(v_combine, (int64_t)H * C, C, H, B, C, vc_pk, s))))
+  }
+  if (B == 0) return MLA_OK;
+  GemmArgs g, g2;
+  out_gemms(d, B, v_combine, kv_b, o_proj, out, static_cast<char*>(ws), &g, &g2);
+  const bool mfma = gemm_mfma_ok(g);
+  if (mfma && (!ws || ws_bytes < ws_out(d, B))) return MLA_ERR_WORKSPACE;
+  if (dry) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mfma && !vc_ready) {
+    if ((st = hip_status(launch_pack_f16(v_combine, (int64_t)H * C, C, H, B, C,
+                                         const_cast<_Float16*>(g.xp), s))))
       return st;
   }
   int splits = 1;
   if ((st = hip_status(launch_gemm_nt(g, 1, &splits, s)))) return st;
   if (o_proj) st = hip_status(launch_gemm_nt(g2, 1, &splits, s));
   return st;
+}
+
+int mla_out_proj(const mla_dims* d, int32_t B, const float* v_combine, const mla_weight* kv_b,
+                 const mla_weight* o_proj, float* out, void* ws, size_t ws_bytes, void* stream) {
+  return out_proj_impl(d, B, v_combine, kv_b, o_proj, out, ws, ws_bytes, stream, false, false);
+}
+
+// Front of mla_decode_layer when both projections of x run on the MFMA path
+// with one weight type: x is packed once, kv_a and q_a run in one launch, the
+// append and the q-latent RMSNorm in one launch, then q_b and the absorb as in
+// mla_absorb_q.  Every launch computes what the separate calls compute, in the
+// same arithmetic.  Returns kNotFused, having launched nothing, when the shapes
+// do not allow it.  ws_a / ws_b: the append and absorb regions.
+constexpr int kNotFused = 1;
+static int layer_front_fused(const mla_dims* d, int32_t B, const float* x, const mla_layer* w,
+                             const int32_t* positions, const mla_cache* cache,
+                             int32_t* dev_status, void* q_abs, char* ws_a, char* ws_b,
+                             hipStream_t s) {
+  if (d->hidden <= 0 || !w->q_a || B <= 0) return kNotFused;
+  const int W = d->kv_lora + d->qk_rope;
+  _Float16* x_pk = reinterpret_cast<_Float16*>(ws_a);
+  float* kv_part = reinterpret_cast<float*>(ws_a + align_up(packed_bytes(1, B, d->hidden)));
+  const AbsorbWs r = absorb_ws(d, B, ws_b);
+  GemmArgs ga{};  // kv_a, as in mla_cache_append
+  ga.w = view(w->kv_a);
+  ga.x = x;
+  ga.xp = x_pk;
+  ga.x_b = d->hidden;
+  ga.y = kv_part;
+  ga.y_b = W;
+  ga.y_s = (int64_t)B * W;
+  ga.O = W;
+  ga.K = d->hidden;
+  ga.B = B;
+  ga.Z = 1;
+  GemmArgs gq{};  // q_a, as in mla_absorb_q
+  gq.w = view(w->q_a);
+  gq.x = x;
+  gq.xp = x_pk;
+  gq.x_b = d->hidden;
+  gq.y = r.q_part;
+  gq.y_b = d->q_lora;
+  gq.y_s = (int64_t)B * d->q_lora;
+  gq.O = d->q_lora;
+  gq.K = d->hidden;
+  gq.B = B;
+  gq.Z = 1;
+  const GemmArgs g2 = q_b_gemm(d, B, w->q_b, r);
+  AppendArgs a = append_args(d, B, kv_part, 1, w->kv_a_norm, w->rope, positions, nullptr, B, cache,
+                             dev_status);
+  QNormArgs qn{};
+  qn.part = r.q_part;
+  qn.S = 1;
+  qn.split_stride = gq.y_s;
+  qn.n = d->q_lora;
+  qn.stride = d->q_lora;
+  qn.gamma = view(w->q_a_norm);
+  qn.eps = d->rms_eps;
+  qn.yp = g2.xp ? r.q_lat_pk : nullptr;
+  if (!gemm_pair_ok(ga, gq) || !g2.xp || !append_qnorm_ok(a, qn)) return kNotFused;
+  int st;
+  if ((st = hip_status(launch_pack_f16(x, d->hidden, 0, 1, B, d->hidden, x_pk, s)))) return st;
+  int splits = 1;
+  if ((st = hip_status(launch_gemm_pair(ga, gq, gemm_max_splits(d->hidden), &splits, s)))) return st;
+  a.kv_splits = splits;
+  qn.S = splits;
+  if ((st = hip_status(launch_append_qnorm(a, qn, s)))) return st;
+  if ((st = hip_status(launch_gemm_nt(g2, 1, &splits, s)))) return st;
+  return hip_status(launch_absorb(absorb_args(d, B, r.q_full, w->kv_b, w->rope, positions, q_abs), s));
+}
+
+size_t mla_layer_workspace_bytes(const mla_dims* d, int32_t B, int32_t max_len, int32_t split_rows) {
+  if (!dims_ok(d) || B < 0) return 0;
+  int32_t rows = 0, splits = 1;
+  if (plan(d, B, max_len, split_rows, &rows, &splits) != MLA_OK) return 0;
+  return ws_layer(d, B, splits) + kAlign;
+}
+
+int mla_decode_layer(const mla_dims* d, int32_t B, const float* x, const float* q_in,
+                     const mla_layer* w, const int32_t* positions, const mla_cache* cache,
+                     const int32_t* seq_lens, int32_t max_len, float softmax_scale,
+                     int32_t split_rows, void* q_abs, float* v_combine, float* lse, float* out,
+                     int32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
+  int st = dims_status(d);
+  if (st) return st;
+  if (!w) return MLA_ERR_NULL;
+  if (B < 0 || max_len < 0) return MLA_ERR_DIMS;
+  int32_t rows = 0, splits = 1;
+  if ((st = plan(d, B, max_len, split_rows, &rows, &splits))) return st;
+  const size_t wa = ws_append(d, B), wb = ws_absorb(d, B), wc = ws_attn(d, B, splits);
+  const size_t wo = ws_out(d, B);
+  if (wa + wb + wc + wo > 0 && (!ws || ws_bytes < wa + wb + wc + wo)) return MLA_ERR_WORKSPACE;
+  char* ws_a = static_cast<char*>(ws);
+  char* ws_b = ws_a ? ws_a + wa : nullptr;
+  char* ws_c = ws_a ? ws_b + wb : nullptr;
+  char* ws_o = ws_a ? ws_c + wc : nullptr;
+  const float* qx = w->q_a ? x : q_in;
+  // every step's arguments are checked before anything is enqueued
+  if ((st = cache_append_impl(d, B, x, w->kv_a, w->kv_a_norm, w->rope, positions, nullptr, B, cache,
+                              dev_status, ws_a, wa, stream, true)))
+    return st;
+  if ((st = absorb_impl(d, B, qx, w->q_a, w->q_a_norm, w->q_b, w->kv_b, w->rope, positions, q_abs,
+                        ws_b, wb, stream, true)))
+    return st;
+  if ((st = attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
+                      v_combine, lse, ws_c, wc, stream, true)))
+    return st;
+  if ((st = out_proj_impl(d, B, v_combine, w->kv_b, w->o_proj, out, ws_o, wo, stream, true, false)))
+    return st;
+  if (B == 0) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = layer_front_fused(d, B, x, w, positions, cache, dev_status, q_abs, ws_a, ws_b, s);
+  if (st == kNotFused) {
+    st = cache_append_impl(d, B, x, w->kv_a, w->kv_a_norm, w->rope, positions, nullptr, B, cache,
+                           dev_status, ws_a, wa, stream, false);
+    if (!st)
+      st = absorb_impl(d, B, qx, w->q_a, w->q_a_norm, w->q_b, w->kv_b, w->rope, positions, q_abs,
+                       ws_b, wb, stream, false);
+  }
+  if (st) return st;
+  // the merge writes W_UV's packed input itself when W_UV runs on the MFMA path
+  GemmArgs g, g2;
+  out_gemms(d, B, v_combine, w->kv_b, w->o_proj, out, ws_o, &g, &g2);
+  _Float16* vc_pk = gemm_mfma_ok(g) ? const_cast<_Float16*>(g.xp) : nullptr;
+  bool packed = false;
+  if ((st = attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
+                      v_combine, lse, ws_c, wc, stream, false, vc_pk, &packed)))
+    return st;
+  return out_proj_impl(d, B, v_combine, w->kv_b, w->o_proj, out, ws_o, wo, stream, false, packed);
 }
 
 }  // extern "C"

@@ -897,9 +897,19 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   m = wave_max(m);
   if (__ballot(nan_lse) != 0) m = NAN;
   float* dst = a.v_combine + ((size_t)b * kH + h) * kC + lane * 8;
+  // the packed fp16 copy: this lane's 8 columns are one 16-byte chunk, in
+  // the pair order c0 c4 c1 c5 c2 c6 c3 c7
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  auto put_packed = [&](f32x4_t lo4, f32x4_t hi4) {
+    if (!a.vc_pk) return;
+    const f16x8_t hv = {(_Float16)lo4[0], (_Float16)hi4[0], (_Float16)lo4[1], (_Float16)hi4[1],
+                        (_Float16)lo4[2], (_Float16)hi4[2], (_Float16)lo4[3], (_Float16)hi4[3]};
+    *reinterpret_cast<f16x8_t*>(a.vc_pk + packed_index(h, b, lane * 8, a.B, kC)) = hv;
+  };
   if (m == -INFINITY) {  // empty sequence
     *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    put_packed(f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f});
     if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = -INFINITY;
     return;
   }
@@ -908,7 +918,6 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   wsum = wave_sum(wsum);
   const float inv = 1.0f / wsum;
 
-  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
   const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
   const size_t sstride = (size_t)kH * kC;
   f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
@@ -943,8 +952,11 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
       }
     }
   }
-  *reinterpret_cast<f32x4_t*>(dst) = lo * inv;
-  *reinterpret_cast<f32x4_t*>(dst + 4) = hi * inv;
+  lo = lo * inv;
+  hi = hi * inv;
+  *reinterpret_cast<f32x4_t*>(dst) = lo;
+  *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
+  put_packed(lo, hi);
   if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = m + logf(wsum);
 }
 

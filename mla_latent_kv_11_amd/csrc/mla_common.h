@@ -95,6 +95,10 @@ struct AttnArgs {
   // MFMA kernel, S > 1: partials are kept in slots; part_first[b] is query b's
   // first slot and part_first[B] the rows per split the split kernel used
   int32_t* part_first;      // [B + 1]
+  // or null: the merge of the MFMA kernel's partials also writes v_combine as
+  // packed fp16 [H][B][C] (packed_index with z = head), the input layout of the
+  // per-head W_UV product on the 4-bit path
+  _Float16* vc_pk;
   int32_t B, H, C, R, block, max_blocks, num_blocks, num_seqs;
   int32_t max_len, split_rows, num_splits;
   int32_t auto_slots;       // > 0: the split kernel sizes the splits from the lengths,
@@ -177,6 +181,31 @@ struct AppendArgs {
   float eps;
 };
 hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s);
+
+// RMSNorm of a q latent from its split partial sums, into the packed layout.
+struct QNormArgs {
+  const float* part;        // [S][B, n] fp32 partial sums
+  int32_t S;
+  int64_t split_stride;
+  int32_t n;
+  int64_t stride;           // between tokens inside a split
+  WeightView gamma;         // 1 x n
+  float eps;
+  _Float16* yp;             // packed [B][n]
+};
+// The append (token count a.B) and the q-latent norm of the same tokens in
+// one launch; hipErrorInvalidValue (nothing launched) when either part does
+// not fit its vector kernel.
+hipError_t launch_append_qnorm(const AppendArgs& a, const QNormArgs& q, hipStream_t s);
+bool append_qnorm_ok(const AppendArgs& a, const QNormArgs& q);
+// y_a = x W_a^T and y_b = x W_b^T in one launch over the same packed x, with
+// the K splits of the pair's combined tile count (*splits, for both);
+// hipErrorInvalidValue (nothing launched) unless both are 4-bit weights on the
+// MFMA path with the same depth and tokens, Z = 1, fp32 outputs and the same
+// K-split decision as their own launches would take.
+hipError_t launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, int max_splits, int* splits,
+                            hipStream_t s);
+bool gemm_pair_ok(const GemmArgs& a, const GemmArgs& b);
 
 struct AbsorbArgs {
   const float* q;           // [B, H, N+R]

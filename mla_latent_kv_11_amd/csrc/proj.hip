@@ -149,10 +149,12 @@ __device__ __forceinline__ f16x8_t dequant8_q8(uint32_t lo, uint32_t hi, f16x2_t
   return __builtin_bit_cast(f16x8_t, uint4{r[0], r[1], r[2], r[3]});
 }
 
+// Row tile bx (32 output rows) of y = x W^T for the token tile blockIdx.y and
+// the (z, K split) pair blockIdx.z.
 template <int U, bool kQ8>
-__device__ __forceinline__ void gemm_mfma_body(const GemmArgs& a, int nw, int S, float* red) {
+__device__ __forceinline__ void gemm_mfma_body(const GemmArgs& a, int bx, int nw, int S, float* red) {
   const int zz = blockIdx.z / S, s = blockIdx.z - zz * S;
-  const int o0 = blockIdx.x * 32, b0 = blockIdx.y * 32;
+  const int o0 = bx * 32, b0 = blockIdx.y * 32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int units = a.K >> 7;
   const int ubeg = (s * nw + wave) * U;
@@ -262,13 +264,25 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmArgs& a, int nw, int S,
 template <int U>
 __global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q4_mfma_kernel(GemmArgs a, int nw, int S) {
   extern __shared__ float red[];  // [nw][16][64]
-  gemm_mfma_body<U, false>(a, nw, S, red);
+  gemm_mfma_body<U, false>(a, blockIdx.x, nw, S, red);
 }
 
 template <int U>
 __global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_q8_mfma_kernel(GemmArgs a, int nw, int S) {
   extern __shared__ float red[];  // [nw][16][64]
-  gemm_mfma_body<U, true>(a, nw, S, red);
+  gemm_mfma_body<U, true>(a, blockIdx.x, nw, S, red);
+}
+
+// Two products of the same packed activations in one launch: the first
+// tiles_a row tiles are a's, the rest b's (same depth, tokens and K splits;
+// each workgroup's arithmetic is that of its own single launch).
+template <int U, bool kQ8>
+__global__ void __launch_bounds__(64 * kQ4MaxWaves) gemm_pair_mfma_kernel(GemmArgs a, GemmArgs b,
+                                                                          int tiles_a, int nw, int S) {
+  extern __shared__ float red[];  // [nw][16][64]
+  const int bx = blockIdx.x;
+  if (bx < tiles_a) gemm_mfma_body<U, kQ8>(a, bx, nw, S, red);
+  else gemm_mfma_body<U, kQ8>(b, bx - tiles_a, nw, S, red);
 }
 
 // fp32 x[z*x_z + b*x_b + k] -> packed fp16; one thread writes one 16-byte chunk
@@ -416,13 +430,10 @@ __device__ __forceinline__ void gamma8(const WeightView& g, int k0, float gm[8])
 // RMSNorm of the summed split partials of one token per block, straight into
 // the packed fp16 layout: thread t owns k = 8t .. 8t + 7, one 16-byte packed
 // chunk.  Block = n/8 threads rounded up to whole waves; n % 8 == 0.
-__global__ void __launch_bounds__(1024) rmsnorm_pack_kernel(const float* part, int32_t S,
-                                                            int64_t split_stride, int32_t B,
-                                                            int32_t n, int64_t stride,
-                                                            WeightView gamma, float eps,
-                                                            _Float16* yp) {
-  __shared__ float red[16];
-  const int64_t b = blockIdx.x;
+__device__ __forceinline__ void rmsnorm_pack_row(const float* part, int32_t S, int64_t split_stride,
+                                                 int32_t B, int32_t n, int64_t stride,
+                                                 WeightView gamma, float eps, _Float16* yp,
+                                                 int64_t b, float* red) {
   const int k0 = 8 * threadIdx.x;
   const bool on = k0 < n;
   float v[8];
@@ -441,6 +452,15 @@ __global__ void __launch_bounds__(1024) rmsnorm_pack_kernel(const float* part, i
   const f16x8_t h = {(_Float16)o[0], (_Float16)o[4], (_Float16)o[1], (_Float16)o[5],
                      (_Float16)o[2], (_Float16)o[6], (_Float16)o[3], (_Float16)o[7]};
   *reinterpret_cast<uint4*>(yp + packed_index(0, b, k0, B, n)) = __builtin_bit_cast(uint4, h);
+}
+
+__global__ void __launch_bounds__(1024) rmsnorm_pack_kernel(const float* part, int32_t S,
+                                                            int64_t split_stride, int32_t B,
+                                                            int32_t n, int64_t stride,
+                                                            WeightView gamma, float eps,
+                                                            _Float16* yp) {
+  __shared__ float red[16];
+  rmsnorm_pack_row(part, S, split_stride, B, n, stride, gamma, eps, yp, blockIdx.x, red);
 }
 
 // (x, y) -> mscale * (x cos a - y sin a, x sin a + y cos a), a = pos * inv_freq.
@@ -502,9 +522,7 @@ __global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
 // values 8t .. 8t + 7 (RMSNorm), the next R/8 own k_pe values (4 RoPE pairs
 // each); every thread stores 8 cache elements at once.  C % 8 == R % 8 == 0.
 template <typename T>
-__global__ void __launch_bounds__(256) append_rows_vec_kernel(AppendArgs a) {
-  __shared__ float red[4];
-  const int b = blockIdx.x;
+__device__ __forceinline__ void append_row_vec(const AppendArgs& a, int b, float* red) {
   const int W = a.C + a.R;
   const int pos = a.positions[b];
   if (pos < 0 || (int64_t)pos >= (int64_t)a.max_blocks * a.block) {
@@ -554,6 +572,25 @@ __global__ void __launch_bounds__(256) append_rows_vec_kernel(AppendArgs a) {
       u[i] = (uint32_t)f32_to_bf16(o[2 * i]) | ((uint32_t)f32_to_bf16(o[2 * i + 1]) << 16);
     *reinterpret_cast<uint4*>(dst) = uint4{u[0], u[1], u[2], u[3]};
   }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) append_rows_vec_kernel(AppendArgs a) {
+  __shared__ float red[4];
+  append_row_vec<T>(a, blockIdx.x, red);
+}
+
+// The cache append of a step and the RMSNorm of its q latent in one launch:
+// workgroups b < B append token b's row, the next B normalise token b - B's
+// q latent into the packed layout.  The block has the larger of the two
+// thread counts; the surplus threads of the other part only join its sums.
+template <typename T>
+__global__ void __launch_bounds__(1024) append_qnorm_kernel(AppendArgs a, QNormArgs q) {
+  __shared__ float red[16];
+  const int b = blockIdx.x;
+  if (b < a.B) append_row_vec<T>(a, b, red);
+  else rmsnorm_pack_row(q.part, q.S, q.split_stride, a.B, q.n, q.stride, q.gamma, q.eps, q.yp,
+                        b - a.B, red);
 }
 
 // grid (H, ceil(C/128)); thread = one latent column c of head h.  Each W_UK
@@ -772,27 +809,93 @@ int gemm_max_splits(int64_t K) {
   return (int)(s < 1 ? 1 : (s > kMaxKSplits ? kMaxKSplits : s));
 }
 
+namespace {
+// Shape of an MFMA-path launch over `units` 128-k units and `tiles` output
+// tiles: U units per wave, nw waves, S K splits.  With few tiles K is spread
+// over workgroups (the consumer adds the S partial sums).
+void q4_shape(int units, int64_t tiles, int max_splits, bool packed_out, int* U, int* nw, int* S) {
+  *U = 1;
+  *S = 1;
+  if (max_splits > kMaxKSplits) max_splits = kMaxKSplits;
+  if (tiles >= 128 || max_splits <= 1 || packed_out) {
+    while ((units + *U - 1) / *U > kQ4MaxWaves) *U *= 2;
+    *nw = (units + *U - 1) / *U;
+  } else {
+    *nw = units < 8 ? units : 8;
+    *S = (units + *nw - 1) / *nw;
+    while (*S > max_splits) {
+      *U *= 2;
+      *S = (units + *nw * *U - 1) / (*nw * *U);
+    }
+  }
+}
+
+hipError_t launch_pair(const GemmArgs& a, const GemmArgs& b, int tiles_a, int tiles, int U, int nw,
+                       int S, hipStream_t s) {
+  constexpr bool kQ8 = false;  // kv_a and q_a take the 4-bit format only
+  dim3 grid(tiles, (a.B + 31) / 32, S);
+  const size_t lds = (size_t)nw * 16 * 64 * sizeof(float);
+  const dim3 blk(nw * 64);
+  switch (U) {
+    case 1: hipLaunchKernelGGL((gemm_pair_mfma_kernel<1, kQ8>), grid, blk, lds, s, a, b, tiles_a, nw, S); break;
+    case 2: hipLaunchKernelGGL((gemm_pair_mfma_kernel<2, kQ8>), grid, blk, lds, s, a, b, tiles_a, nw, S); break;
+    case 4: hipLaunchKernelGGL((gemm_pair_mfma_kernel<4, kQ8>), grid, blk, lds, s, a, b, tiles_a, nw, S); break;
+    case 8: hipLaunchKernelGGL((gemm_pair_mfma_kernel<8, kQ8>), grid, blk, lds, s, a, b, tiles_a, nw, S); break;
+    default: hipLaunchKernelGGL((gemm_pair_mfma_kernel<16, kQ8>), grid, blk, lds, s, a, b, tiles_a, nw, S); break;
+  }
+  return hipGetLastError();
+}
+
+bool append_vec_ok(const AppendArgs& a) {
+  const int W = a.C + a.R;
+  const size_t elem = a.cache_dtype == MLA_F32 ? 4 : 2;
+  return a.C % 8 == 0 && a.R % 8 == 0 && W <= 2048 &&
+         (reinterpret_cast<uintptr_t>(a.kv_pre) & 15) == 0 && a.kv_split_stride % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(a.pool) & 15) == 0 && ((size_t)W * elem) % 16 == 0 &&
+         (reinterpret_cast<uintptr_t>(a.gamma.data) & 15) == 0;
+}
+
+bool qnorm_pack_ok(const float* part, int32_t S, int64_t split_stride, int32_t n, int64_t stride,
+                   WeightView gamma, _Float16* yp) {
+  return yp && n % 128 == 0 && n <= 8192 && S >= 1 && S <= kMaxKSplits &&
+         (reinterpret_cast<uintptr_t>(part) & 15) == 0 && stride % 4 == 0 &&
+         split_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(gamma.data) & 15) == 0;
+}
+}  // namespace
+
+namespace {
+int64_t q4_tiles(const GemmArgs& a) { return (int64_t)((a.O + 31) / 32) * a.Z * ((a.B + 31) / 32); }
+}  // namespace
+
+// The pair also requires that both products would take the same K-split
+// decision on their own, so each gets the shape (and the sums) of its own
+// single launch.
+bool gemm_pair_ok(const GemmArgs& a, const GemmArgs& b) {
+  return a.O > 0 && b.O > 0 && a.B > 0 && a.Z == 1 && b.Z == 1 && a.K == b.K && a.B == b.B &&
+         gemm_mfma_ok(a) && gemm_mfma_ok(b) && a.w.dtype == MLA_Q4G64 && b.w.dtype == MLA_Q4G64 &&
+         a.xp && a.xp == b.xp &&
+         !a.yp && !b.yp && a.y && b.y && (q4_tiles(a) >= 128) == (q4_tiles(b) >= 128);
+}
+
+hipError_t launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, int max_splits, int* splits,
+                            hipStream_t s) {
+  *splits = 1;
+  if (!gemm_pair_ok(a, b)) return hipErrorInvalidValue;
+  const int tiles_a = (a.O + 31) / 32, tiles = tiles_a + (b.O + 31) / 32;
+  int U, nw, S;
+  q4_shape(a.K / 128, q4_tiles(a), max_splits, false, &U, &nw, &S);
+  *splits = S;
+  return launch_pair(a, b, tiles_a, tiles, U, nw, S, s);
+}
+
 hipError_t launch_gemm_nt(const GemmArgs& a, int max_splits, int* splits, hipStream_t s) {
   *splits = 1;
   if (a.O <= 0 || a.B <= 0 || a.Z <= 0) return hipSuccess;
   if (a.yp && (a.yp_K % 128) != 0) return hipErrorInvalidValue;
   if (gemm_mfma_ok(a)) {
     if (!a.xp) return hipErrorInvalidValue;
-    const int units = a.K / 128;
-    const int64_t tiles = (int64_t)((a.O + 31) / 32) * a.Z * ((a.B + 31) / 32);
-    int U = 1, nw, S = 1;
-    if (max_splits > kMaxKSplits) max_splits = kMaxKSplits;
-    if (tiles >= 128 || max_splits <= 1 || a.yp) {
-      while ((units + U - 1) / U > kQ4MaxWaves) U *= 2;
-      nw = (units + U - 1) / U;
-    } else {  // few row tiles: spread K over workgroups, the consumer adds the splits
-      nw = units < 8 ? units : 8;
-      S = (units + nw - 1) / nw;
-      while (S > max_splits) {
-        U *= 2;
-        S = (units + nw * U - 1) / (nw * U);
-      }
-    }
+    int U, nw, S;
+    q4_shape(a.K / 128, q4_tiles(a), max_splits, a.yp != nullptr, &U, &nw, &S);
     *splits = S;
     return launch_q4(a, U, nw, S, s);
   }
@@ -820,9 +923,7 @@ hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_strid
                                _Float16* yp, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (S < 1 || S > kMaxKSplits || (yp && n % 128 != 0)) return hipErrorInvalidValue;
-  const bool aligned = (reinterpret_cast<uintptr_t>(part) & 15) == 0 && stride % 4 == 0 &&
-                       split_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(gamma.data) & 15) == 0;
-  if (yp && aligned && n <= 8192) {
+  if (qnorm_pack_ok(part, S, split_stride, n, stride, gamma, yp)) {
     const int threads = ((n / 8) + 63) / 64 * 64;
     hipLaunchKernelGGL(rmsnorm_pack_kernel, dim3(B), dim3(threads), 0, s, part, S, split_stride,
                        B, n, stride, gamma, eps, yp);
@@ -833,15 +934,26 @@ hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_strid
   return hipGetLastError();
 }
 
+bool append_qnorm_ok(const AppendArgs& a, const QNormArgs& q) {
+  return append_vec_ok(a) && qnorm_pack_ok(q.part, q.S, q.split_stride, q.n, q.stride, q.gamma, q.yp);
+}
+
+hipError_t launch_append_qnorm(const AppendArgs& a, const QNormArgs& q, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  if (!append_qnorm_ok(a, q)) return hipErrorInvalidValue;
+  const int ta = ((a.C + a.R) / 8 + 63) / 64 * 64, tq = (q.n / 8 + 63) / 64 * 64;
+  const int threads = ta > tq ? ta : tq;
+  if (a.cache_dtype == MLA_F32)
+    hipLaunchKernelGGL(append_qnorm_kernel<float>, dim3(2 * a.B), dim3(threads), 0, s, a, q);
+  else
+    hipLaunchKernelGGL(append_qnorm_kernel<uint16_t>, dim3(2 * a.B), dim3(threads), 0, s, a, q);
+  return hipGetLastError();
+}
+
 hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   const int W = a.C + a.R;
-  const size_t elem = a.cache_dtype == MLA_F32 ? 4 : 2;
-  const bool vec = a.C % 8 == 0 && a.R % 8 == 0 && W <= 2048 &&
-                   (reinterpret_cast<uintptr_t>(a.kv_pre) & 15) == 0 &&
-                   a.kv_split_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(a.pool) & 15) == 0 &&
-                   ((size_t)W * elem) % 16 == 0 && (reinterpret_cast<uintptr_t>(a.gamma.data) & 15) == 0;
-  if (vec) {
+  if (append_vec_ok(a)) {
     const int threads = ((W / 8) + 63) / 64 * 64;
     if (a.cache_dtype == MLA_F32)
       hipLaunchKernelGGL(append_rows_vec_kernel<float>, dim3(a.B), dim3(threads), 0, s, a);

@@ -123,6 +123,23 @@ def run_step(case: Case, ns, split_rows: int = 0, ws=None, stream=None) -> None:
         mla.out_proj(ns.dims, ns.v_combine, ns.kv_b, ns.out, ns.o_proj, ws, stream)
 
 
+def layer_workspace(ns, split_rows: int = 0, device="cuda") -> torch.Tensor:
+    n = mla.layer_workspace_bytes(ns.dims, int(ns.lens.shape[0]), ns.max_len, split_rows)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def run_layer(case: Case, ns, split_rows: int = 0, ws=None, stream=None) -> None:
+    """The staged case's step as one decode_layer call (a case with an append
+    and a query to absorb: configurations 1, 2, 3 and 5)."""
+    ws = layer_workspace(ns, split_rows) if ws is None else ws
+    mla.decode_layer(ns.dims, ns.x, ns.positions, ns.pool, ns.table, ns.lens, ns.max_len,
+                     ns.softmax_scale, ns.q_abs, ns.v_combine, ns.out, kv_a=ns.kv_a,
+                     kv_a_norm=ns.kv_a_norm, kv_b=ns.kv_b, inv_freq=ns.inv_freq,
+                     rope_mscale=ns.rope_mscale, q_a=ns.q_a, q_a_norm=ns.q_a_norm, q_b=ns.q_b,
+                     o_proj=ns.o_proj, q_in=ns.q, lse=ns.lse, split_rows=split_rows,
+                     dev_status=ns.status, ws=ws, stream=stream)
+
+
 class GraphStep:
     """One decode step as the library calls it, replayable as one HIP graph:
 

@@ -283,3 +283,40 @@ def test_one_hip_runtime_in_the_process():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_layer_validation_before_launch(lib):
+    """mla_decode_layer checks the arguments of all four steps before it
+    enqueues anything: an error in the last step (out_proj) is reported as
+    that step reports it, with no launch (there is no device here)."""
+    d = mla.Dims(16, 32, 16, 32, 64, hidden=256, q_lora=0, block_size=64, cache_dtype=mla.MLA_F32)
+    rope = mla.CRope(0x100, 1.0)
+    kva, norm = _w(mla.MLA_F32, 80, 256), _w(mla.MLA_F32, 1, 64)
+    kvb, wo = _w(mla.MLA_F32, 16 * 64, 64), _w(mla.MLA_F32, 256, 16 * 32)
+    cache = mla.CCache(0x2000, 0x3000, 4, 2)
+    null = ctypes.POINTER(mla.CWeight)()
+
+    def layer(o_proj=wo, kv_b=kvb, q_in=0x700, ws=0x9000, ws_bytes=None, B=2, x=0x600):
+        L = mla.CLayer(ctypes.pointer(kva), ctypes.pointer(norm), null, null, null,
+                       ctypes.pointer(kv_b) if kv_b is not None else null,
+                       ctypes.pointer(o_proj) if o_proj is not None else null,
+                       ctypes.pointer(rope))
+        need = lib.mla_layer_workspace_bytes(ctypes.byref(d.c()), B, 100, 0)
+        return lib.mla_decode_layer(ctypes.byref(d.c()), B, x, q_in, ctypes.byref(L), 0x800,
+                                    ctypes.byref(cache), 0x4000, 100, 0.1, 0, 0xa000, 0x5000,
+                                    None, 0xb000, None, ws, need if ws_bytes is None else ws_bytes,
+                                    None)
+    assert lib.mla_decode_layer(ctypes.byref(d.c()), 2, 0x600, 0x700, None, 0x800,
+                                ctypes.byref(cache), 0x4000, 100, 0.1, 0, 0xa000, 0x5000, None,
+                                0xb000, None, 0x9000, 1 << 20, None) == mla.MLA_ERR_NULL
+    assert layer(kv_b=None) == mla.MLA_ERR_NULL
+    assert layer(q_in=None) == mla.MLA_ERR_NULL          # no q_a: the query is given
+    assert layer(x=None) == mla.MLA_ERR_NULL
+    assert layer(o_proj=_w(mla.MLA_F32, 256, 16 * 32 + 1)) == mla.MLA_ERR_DIMS
+    assert layer(ws_bytes=64) == mla.MLA_ERR_WORKSPACE
+    assert layer(ws=None) == mla.MLA_ERR_WORKSPACE
+    assert layer(B=0) == mla.MLA_OK
+    # the layer's workspace holds every call's regions side by side
+    for B, L in ((1, 128), (32, 16384)):
+        assert (lib.mla_layer_workspace_bytes(ctypes.byref(d.c()), B, L, 0)
+                >= lib.mla_workspace_bytes(ctypes.byref(d.c()), B, L, 0))
