@@ -4,11 +4,13 @@
 A step is one pass of the whole decode path over one batch: kv_a projection +
 latent RMSNorm + YaRN RoPE + paged append, the q chain + absorb, decode
 attention over the paged latent cache, the W_UV expansion and o_proj.  The
-append and the absorb are independent and run on two streams, and the whole
-step is replayed as one HIP graph (``--eager``: every call launched on one
-stream).  The attention call is then timed where the step runs it (HIP events
-around decode_attn inside eager steps, between append/absorb and out_proj), and
-also back to back (a replayed graph of 20 calls; ``--eager``: one by one).  The
+step is one mla_decode_layer call (9 kernels on one stream), replayed as one
+HIP graph (``--eager``: the call launched every step); the same step as the
+four separate calls (append and absorb on two streams, one graph) is timed
+beside it.  The attention call is then timed where the step runs it (HIP events
+around decode_attn inside eager steps of the four calls, between
+append/absorb and out_proj), and also back to back (a replayed graph of 20
+calls; ``--eager``: one by one).  The
 workload is the full per-layer configuration: batch 32, 16384 cached rows per
 sequence (append at 16383), DeepSeek-V3 shapes (128 heads, latent 512, rope
 64), hidden 7168, q_lora 1536, 4-bit affine (group 64) projections, bf16
@@ -130,6 +132,7 @@ def time_attn_only(cfg, torch, D, S, mla, iters=50, warm=50, oracle=True, lens_p
         for _ in range(warm):
             call()
         torch.cuda.synchronize()
+        settle(call, torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(iters):
@@ -371,25 +374,32 @@ def main():
     ns = D.stage(case)
     B = case.batch
     rows = int(case.lens.sum())
-    # One step = cache_append and absorb_q (two streams: independent), then
-    # decode_attn, then out_proj, replayed as one HIP graph (--eager: the calls
-    # launched one by one on one stream).
-    step = D.GraphStep(case, ns, two_streams=not args.eager)
-    for _ in range(args.warmup):
-        step.run(eager=True)
-    torch.cuda.synchronize()
-    if not args.eager:
-        step.capture()
+    # One step = one mla_decode_layer call (the fused front, attention with its
+    # merge, W_UV and o_proj: 9 kernels on one stream), replayed as one HIP
+    # graph (--eager: the call launched every step).
+    def timed_steps(step):
         for _ in range(args.warmup):
-            step.run()
-    torch.cuda.synchronize()
-    settle_ms, settle_steps = settle(lambda: step.run(eager=args.eager), torch)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step.run(eager=args.eager)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+            step.run(eager=True)
+        torch.cuda.synchronize()
+        if not args.eager:
+            step.capture()
+            for _ in range(args.warmup):
+                step.run()
+        torch.cuda.synchronize()
+        settled = settle(lambda: step.run(eager=args.eager), torch)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step.run(eager=args.eager)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, settled
+
+    ms_step, (settle_ms, settle_steps) = timed_steps(D.LayerStep(case, ns))
+    assert int(ns.status.cpu()[0]) == 0
+    # The same step as the four calls: cache_append and absorb_q on two streams
+    # (independent), then decode_attn, then out_proj, replayed as one HIP graph
+    # (--eager: launched one by one on one stream).
+    step = D.GraphStep(case, ns, two_streams=not args.eager)
+    ms_step_calls, _ = timed_steps(step)
     assert int(ns.status.cpu()[0]) == 0
 
     # The attention call timed where the step runs it: eager steps (the same
@@ -454,8 +464,13 @@ def main():
             "workload": "MLA decode layer, batch 32, L=16384 (append at 16383), 128 heads, "
                         "kv_lora 512 + rope 64, hidden 7168, q_lora 1536, 4-bit g64 projections, "
                         "bf16 paged cache (64-row blocks)",
-            "launch": "eager, one stream" if args.eager else
-                      "one HIP graph per step; append | absorb on two streams",
+            "launch": "one mla_decode_layer call per step, eager" if args.eager else
+                      "one HIP graph per step holding one mla_decode_layer call (9 kernels, "
+                      "one stream)",
+            "ms_per_step_four_calls": round(ms_step_calls, 4),
+            "four_calls_launch": "eager, one stream" if args.eager else
+                                 "cache_append | absorb_q on two streams, decode_attn, "
+                                 "out_proj; one HIP graph per step",
             "global_batch": B, "seq_len": int(ns.max_len), "parallelism": "none (1 GPU)",
             "split_rows": r_split, "splits_per_seq": n_split,
             "precision": "attention: bf16 MFMA operands, fp32 accumulate, fp32 softmax; "

@@ -204,3 +204,30 @@ class GraphStep:
             self.post()
         else:
             self.graph.replay()
+
+
+class LayerStep:
+    """One decode step as one decode_layer call (on the 4-bit layer: 9 kernels
+    on one stream), replayable as one HIP graph.  Library calls only."""
+
+    def __init__(self, case: Case, ns, split_rows: int = 0):
+        self.case, self.ns, self.split_rows = case, ns, split_rows
+        self.ws = layer_workspace(ns, split_rows)
+        self.graph = None
+
+    def call(self):
+        run_layer(self.case, self.ns, self.split_rows, self.ws)
+
+    def capture(self):
+        """Record the call (run it eagerly at least once before)."""
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.call()
+        torch.cuda.synchronize()
+
+    def run(self, eager=False):
+        if eager:
+            self.call()
+        else:
+            self.graph.replay()
