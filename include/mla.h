@@ -100,6 +100,13 @@ typedef struct mla_dims {
  *     [rows, cols/64]; w = scale * nibble + bias.  Products with a Q4G64
  *     weight whose depth is a multiple of 128 run on fp16 MFMA: w and the
  *     activations are rounded to fp16 (11-bit significands), sums are fp32.
+ *     The hidden state and the normalised q latent are first scaled per
+ *     token by a power of two that brings their largest magnitude into
+ *     [2^14, 2^15) (undone exactly on the fp32 results), as is each token's
+ *     q_nope per head before the W_UK product, so no value overflows fp16 or
+ *     falls into its subnormals.  v_combine and the per-head W_UV outputs
+ *     enter W_UV and o_proj unscaled: they are bounded by the cache latents
+ *     (|c| <= sqrt(C) max|kv_a_norm gamma|) times the weights.
  *   MLA_Q8_0: data = bytes, [rows][cols/32] blocks of 34: a little-endian
  *     binary16 scale d, then 32 signed bytes q; element = d * q (turbospark
  *     deepseek2/attn.rs, validate_q8_0_matrix: kv_b read in place; the byte
@@ -229,8 +236,9 @@ int mla_absorb_q(const mla_dims* dims, int32_t batch, const float* q_in,
  * bf16 caches run on the MFMA kernel (H = 128, C = 512, R = 64, block_size a
  * multiple of 32); f32 caches on a VALU kernel of any shape.  With more than
  * one split the bf16 kernel keeps each split's normalised partial in fp16
- * times a power-of-two scale per head (2^-11 relative rounding before the
- * fp32 merge); the f32 kernel keeps fp32 partials.
+ * times a power-of-two scale per head that brings the head's largest
+ * magnitude into [2^14, 2^15) (2^-11 relative rounding before the fp32
+ * merge, at any magnitude); the f32 kernel keeps fp32 partials.
  * Errors: NULL, DIMS (max_seq_len < 0, split_rows), UNSUPPORTED, CAPACITY
  * (max_seq_len > max_blocks_per_seq * block_size), WORKSPACE. */
 int mla_decode_attn(const mla_dims* dims, int32_t batch, const void* q_abs,

@@ -125,15 +125,18 @@ int plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t req, int32_t
 
 // Workspace regions of the projection calls (each 256-byte aligned); "packed"
 // is the fp16 activation layout of the 4-bit MFMA path (packed_index):
-//   append : x packed [B][hidden]; kv_a partial sums [S][B][W] fp32
+//   append : x packed [B][hidden]; kv_a partial sums [S][B][W] fp32; the
+//            packed tokens' exponents [B] int32
 //   absorb : x packed [B][hidden]; q_a partial sums [S][B][q_lora] fp32;
-//            normalised q latent packed [B][q_lora]; q [B][H][N+R] fp32
+//            normalised q latent packed [B][q_lora]; q [B][H][N+R] fp32; the
+//            exponents of the packed x and q latent, [B] int32 each
 //   out    : v_combine packed [H][B][C]; per-head W_UV outputs [B][H*V]
 //            (packed fp16 for a 4-bit o_proj, else fp32)
 size_t ws_append(const mla_dims* d, int32_t B) {
   if (d->hidden <= 0) return 0;
   return align_up(packed_bytes(1, B, d->hidden)) +
-         align_up((size_t)gemm_max_splits(d->hidden) * B * (d->kv_lora + d->qk_rope) * 4);
+         align_up((size_t)gemm_max_splits(d->hidden) * B * (d->kv_lora + d->qk_rope) * 4) +
+         align_up((size_t)B * 4);
 }
 size_t ws_q_part(const mla_dims* d, int32_t B) {
   return align_up((size_t)gemm_max_splits(d->hidden) * B * d->q_lora * 4);
@@ -142,7 +145,8 @@ size_t ws_absorb(const mla_dims* d, int32_t B) {
   if (d->q_lora <= 0) return 0;
   return align_up(packed_bytes(1, B, d->hidden)) + ws_q_part(d, B) +
          align_up(packed_bytes(1, B, d->q_lora)) +
-         align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4);
+         align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4) +
+         2 * align_up((size_t)B * 4);
 }
 // Split partials: fp16 values plus a power-of-two exponent per (sequence,
 // split, head) for a bf16 cache, fp32 values for an fp32 cache; and the lse.
@@ -373,8 +377,12 @@ static int cache_append_impl(const mla_dims* d, int32_t B, const float* x, const
     g.Z = 1;
     if (gemm_mfma_ok(g)) {
       g.xp = reinterpret_cast<_Float16*>(base);
-      if ((st = hip_status(launch_pack_f16(x, d->hidden, 0, 1, B, d->hidden,
-                                           reinterpret_cast<_Float16*>(base), s))))
+      int32_t* x_exp = reinterpret_cast<int32_t*>(
+          base + align_up(packed_bytes(1, B, d->hidden)) +
+          align_up((size_t)gemm_max_splits(d->hidden) * B * W * 4));
+      g.x_exp = x_exp;
+      if ((st = hip_status(launch_pack_scaled(x, d->hidden, B, d->hidden,
+                                              reinterpret_cast<_Float16*>(base), x_exp, s))))
         return st;
     }
     if ((st = hip_status(launch_gemm_nt(g, gemm_max_splits(d->hidden), &kv_splits, s)))) return st;
@@ -429,6 +437,8 @@ struct AbsorbWs {
   float* q_part;
   _Float16* q_lat_pk;
   float* q_full;
+  int32_t* x_exp;
+  int32_t* q_lat_exp;
 };
 static AbsorbWs absorb_ws(const mla_dims* d, int32_t B, void* ws) {
   char* base = static_cast<char*>(ws);
@@ -440,6 +450,9 @@ static AbsorbWs absorb_ws(const mla_dims* d, int32_t B, void* ws) {
   r.q_lat_pk = reinterpret_cast<_Float16*>(base);
   base += align_up(packed_bytes(1, B, d->q_lora));
   r.q_full = reinterpret_cast<float*>(base);
+  base += align_up((size_t)B * d->num_heads * (d->qk_nope + d->qk_rope) * 4);
+  r.x_exp = reinterpret_cast<int32_t*>(base);
+  r.q_lat_exp = reinterpret_cast<int32_t*>(base + align_up((size_t)B * 4));
   return r;
 }
 
@@ -456,7 +469,10 @@ static GemmArgs q_b_gemm(const mla_dims* d, int32_t B, const mla_weight* q_b, co
   g2.K = d->q_lora;
   g2.B = B;
   g2.Z = 1;
-  if (gemm_mfma_ok(g2)) g2.xp = r.q_lat_pk;
+  if (gemm_mfma_ok(g2)) {
+    g2.xp = r.q_lat_pk;
+    g2.x_exp = r.q_lat_exp;
+  }
   return g2;
 }
 
@@ -502,7 +518,8 @@ static int absorb_impl(const mla_dims* d, int32_t B, const float* q_in, const ml
     const GemmArgs g2 = q_b_gemm(d, B, q_b, r);
     if (gemm_mfma_ok(g)) {
       g.xp = r.x_pk;
-      if ((st = hip_status(launch_pack_f16(q_in, d->hidden, 0, 1, B, d->hidden, r.x_pk, s))))
+      g.x_exp = r.x_exp;
+      if ((st = hip_status(launch_pack_scaled(q_in, d->hidden, B, d->hidden, r.x_pk, r.x_exp, s))))
         return st;
     }
     int splits = 1;
@@ -510,7 +527,8 @@ static int absorb_impl(const mla_dims* d, int32_t B, const float* q_in, const ml
     if ((st = hip_status(launch_rmsnorm_rows(r.q_part, splits, g.y_s, B, d->q_lora, d->q_lora,
                                              view(q_a_norm), d->rms_eps,
                                              g2.xp ? nullptr : r.q_part,
-                                             g2.xp ? r.q_lat_pk : nullptr, s))))
+                                             g2.xp ? r.q_lat_pk : nullptr,
+                                             g2.xp ? r.q_lat_exp : nullptr, s))))
       return st;
     if ((st = hip_status(launch_gemm_nt(g2, 1, &splits, s)))) return st;
     q = r.q_full;
@@ -741,11 +759,15 @@ static int layer_front_fused(const mla_dims* d, int32_t B, const float* x, const
   const int W = d->kv_lora + d->qk_rope;
   _Float16* x_pk = reinterpret_cast<_Float16*>(ws_a);
   float* kv_part = reinterpret_cast<float*>(ws_a + align_up(packed_bytes(1, B, d->hidden)));
+  int32_t* x_exp = reinterpret_cast<int32_t*>(
+      ws_a + align_up(packed_bytes(1, B, d->hidden)) +
+      align_up((size_t)gemm_max_splits(d->hidden) * B * W * 4));
   const AbsorbWs r = absorb_ws(d, B, ws_b);
   GemmArgs ga{};  // kv_a, as in mla_cache_append
   ga.w = view(w->kv_a);
   ga.x = x;
   ga.xp = x_pk;
+  ga.x_exp = x_exp;
   ga.x_b = d->hidden;
   ga.y = kv_part;
   ga.y_b = W;
@@ -758,6 +780,7 @@ static int layer_front_fused(const mla_dims* d, int32_t B, const float* x, const
   gq.w = view(w->q_a);
   gq.x = x;
   gq.xp = x_pk;
+  gq.x_exp = x_exp;
   gq.x_b = d->hidden;
   gq.y = r.q_part;
   gq.y_b = d->q_lora;
@@ -778,9 +801,10 @@ static int layer_front_fused(const mla_dims* d, int32_t B, const float* x, const
   qn.gamma = view(w->q_a_norm);
   qn.eps = d->rms_eps;
   qn.yp = g2.xp ? r.q_lat_pk : nullptr;
+  qn.yexp = r.q_lat_exp;
   if (!gemm_pair_ok(ga, gq) || !g2.xp || !append_qnorm_ok(a, qn)) return kNotFused;
   int st;
-  if ((st = hip_status(launch_pack_f16(x, d->hidden, 0, 1, B, d->hidden, x_pk, s)))) return st;
+  if ((st = hip_status(launch_pack_scaled(x, d->hidden, B, d->hidden, x_pk, x_exp, s)))) return st;
   int splits = 1;
   if ((st = hip_status(launch_gemm_pair(ga, gq, gemm_max_splits(d->hidden), &splits, s)))) return st;
   a.kv_splits = splits;

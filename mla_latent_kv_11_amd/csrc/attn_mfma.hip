@@ -680,8 +680,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     pending = softmax(s, 0);
     bool restart = false;
     for (int it = 1;; ++it) {
-      if (lane == 0)
-        ((MLA_LDS uint8_t*)(votes + ((it - 1) & 1)))[wave] = __ballot(pending) != 0 ? 1 : 0;
+      // the ballot runs in every lane (inside the branch it would see lane 0 only)
+      const bool wave_vote = __ballot(pending) != 0;
+      if (lane == 0) ((MLA_LDS uint8_t*)(votes + ((it - 1) & 1)))[wave] = wave_vote ? 1 : 0;
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's copies of tile it
       zero_tail(it);
       __syncthreads();
@@ -754,10 +755,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       }
     }
   } else {
-    // fp16 partial: O / l * 2^-e with e >= 0 the smallest exponent that keeps
-    // the head's largest magnitude under 2^15 (0 unless |V| is huge); the
-    // largest |O| / l of each head over the four waves meets in LDS (the P
-    // area, free after the barrier above).
+    // fp16 partial: O / l * 2^-e with e the exponent that brings the head's
+    // largest magnitude into [2^14, 2^15) (f16_range_exp), so that neither a
+    // huge |V| overflows binary16 nor a tiny one falls into its subnormals;
+    // the largest |O| / l of each head over the four waves meets in LDS (the
+    // P area, free after the barrier above).
     MLA_LDS float* amax_lds = (MLA_LDS float*)p_lds;  // [4 waves][128 heads]
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
@@ -777,10 +779,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       const int h = hb * 32 + l32;
       const float amax = fmaxf(fmaxf(amax_lds[h], amax_lds[kH + h]),
                                fmaxf(amax_lds[2 * kH + h], amax_lds[3 * kH + h]));
-      // floor(log2 amax) from the exponent bits; e keeps amax * 2^-e below 2^15
-      const int lg = (int)((__float_as_uint(amax) >> 23) & 255u) - 127;
-      const int e = (amax >= 32768.f && amax <= 3.0e38f) ? lg - 14 : 0;
-      const float scale = __uint_as_float((uint32_t)(127 - e) << 23);
+      const int e = f16_range_exp(amax);
+      const float scale = pow2f(-e);
       const float inv_l = bad ? NAN : scale / l_heads[h];
       // head r's 128 columns are 16 chunks of 8 halves (chunk c at slot
       // c ^ (r & 15)), each written as two 4-half pieces by the lane pair

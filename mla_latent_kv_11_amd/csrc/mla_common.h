@@ -70,6 +70,19 @@ __device__ __forceinline__ void wave_halves(float x, float* lo, float* hi) {
   *hi = __uint_as_float(r[1]);
 }
 
+// Exponent e that brings a block's largest magnitude amax into [2^14, 2^15)
+// once the block is multiplied by 2^-e, so that binary16 holds it with full
+// 11-bit significands and no overflow; clamped to [-100, 113] so that 2^-e
+// and 2^e are normal floats.  0 for amax zero, infinite or NaN (those values
+// pass through unscaled).  A power-of-two scale is exact in both directions.
+__device__ __forceinline__ int f16_range_exp(float amax) {
+  if (!(amax > 0.f) || !(amax <= 3.4028235e38f)) return 0;
+  const int e = (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 14;
+  return e < -100 ? -100 : (e > 113 ? 113 : e);
+}
+// 2^k for k in [-126, 127], from the exponent bits.
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
@@ -127,6 +140,9 @@ struct GemmArgs {
   _Float16* yp;
   int64_t y_b, y_z, y_s, yp_K;
   int32_t O, K, B, Z;
+  // with xp: token b's packed activations hold x * 2^-x_exp[b] (or null: x);
+  // the results are multiplied back by 2^x_exp[b]
+  const int32_t* x_exp;
 };
 
 // Packed fp16 activations of a logical [Z][B][K] matrix (K % 128 == 0), laid
@@ -157,13 +173,19 @@ hipError_t launch_gemm_nt(const GemmArgs& a, int max_splits, int* splits, hipStr
 // Packs fp32 x[z*x_z + b*x_b + k] into packed fp16 (packed_index) for the MFMA path.
 hipError_t launch_pack_f16(const float* x, int64_t x_b, int64_t x_z, int32_t Z, int32_t B,
                            int32_t K, _Float16* xp, hipStream_t s);
+// Packs fp32 x[b*x_b + k] (Z = 1) with a power-of-two scale per token: token
+// b's values times 2^-x_exp[b] (f16_range_exp of its largest magnitude), so
+// no value overflows binary16; the consuming GEMM gets x_exp.
+hipError_t launch_pack_scaled(const float* x, int64_t x_b, int32_t B, int32_t K, _Float16* xp,
+                              int32_t* x_exp, hipStream_t s);
 
 // RMSNorm of rows b < B of the sum of S split partials part[s*split_stride +
 // b*stride + i], i < n, with gamma (1 x n weight of F32/BF16), written to
-// y[b*stride + i] (fp32; may alias part) or packed fp16 yp (n % 128 == 0).
+// y[b*stride + i] (fp32; may alias part) or packed fp16 yp (n % 128 == 0),
+// row b times 2^-yexp[b] (f16_range_exp of its largest magnitude).
 hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_stride, int32_t B,
                                int32_t n, int64_t stride, WeightView gamma, float eps, float* y,
-                               _Float16* yp, hipStream_t s);
+                               _Float16* yp, int32_t* yexp, hipStream_t s);
 
 struct AppendArgs {
   const float* kv_pre;      // [S][B, W] fp32 partial sums of the pre-norm row
@@ -191,7 +213,8 @@ struct QNormArgs {
   int64_t stride;           // between tokens inside a split
   WeightView gamma;         // 1 x n
   float eps;
-  _Float16* yp;             // packed [B][n]
+  _Float16* yp;             // packed [B][n], token b times 2^-yexp[b]
+  int32_t* yexp;            // [B]
 };
 // The append (token count a.B) and the q-latent norm of the same tokens in
 // one launch; hipErrorInvalidValue (nothing launched) when either part does

@@ -254,6 +254,7 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmArgs& a, int bx, int nw
     const int o = o0 + (ln & 31);
     const int t = b0 + (j >> 2) * 8 + (ln >> 5) * 4 + (j & 3);
     if (o >= a.O || t >= a.B) continue;
+    if (a.x_exp) v = ldexpf(v, a.x_exp[t]);
     if (a.yp)
       a.yp[packed_index(0, t, (int64_t)zz * a.y_z + o, a.B, a.yp_K)] = (_Float16)v;
     else
@@ -344,6 +345,65 @@ __device__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Largest value over the threads of a block; every thread gets it.
+__device__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) t = fmaxf(t, red[i]);
+  __syncthreads();
+  return t;
+}
+
+// fp32 x[b*x_b + k] -> packed fp16 with a power-of-two scale per token: one
+// workgroup per token slot of the padded tiles finds the token's largest
+// magnitude, then writes its 16-byte chunks (8 values each) times 2^-e; token
+// slots past B are zero.  x is read twice (the second time from cache).
+__global__ void __launch_bounds__(256) pack_scaled_kernel(const float* x, int64_t x_b, int32_t B,
+                                                          int32_t K, bool vec, _Float16* xp,
+                                                          int32_t* x_exp) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const float* row = x + (int64_t)(b < B ? b : 0) * x_b;
+  auto load8 = [&](int k, float v[8]) {
+    if (vec) {
+      const float4 v0 = reinterpret_cast<const float4*>(row + k)[0];
+      const float4 v1 = reinterpret_cast<const float4*>(row + k)[1];
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = row[k + i];
+    }
+  };
+  float m = 0.f;
+  if (b < B) {
+    for (int c = threadIdx.x; c < K / 8; c += 256) {
+      float v[8];
+      load8(8 * c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+  }
+  const int e = f16_range_exp(block_max(m, red));  // uniform: b is
+  if (b < B && threadIdx.x == 0) x_exp[b] = e;
+  const float sc = pow2f(-e);
+  for (int c = threadIdx.x; c < K / 8; c += 256) {
+    uint4 o = uint4{0u, 0u, 0u, 0u};
+    if (b < B) {
+      float v[8];
+      load8(8 * c, v);
+      const f16x8_t h = {(_Float16)(v[0] * sc), (_Float16)(v[4] * sc), (_Float16)(v[1] * sc),
+                         (_Float16)(v[5] * sc), (_Float16)(v[2] * sc), (_Float16)(v[6] * sc),
+                         (_Float16)(v[3] * sc), (_Float16)(v[7] * sc)};
+      o = __builtin_bit_cast(uint4, h);
+    }
+    *reinterpret_cast<uint4*>(xp + packed_index(0, b, 8 * c, B, K)) = o;
+  }
+}
+
 __device__ __forceinline__ float gamma_at(const WeightView& g, int i) {
   return g.dtype == MLA_F32 ? static_cast<const float*>(g.data)[i]
                             : bf16_to_f32(static_cast<const uint16_t*>(g.data)[i]);
@@ -353,27 +413,37 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* part, in
                                                            int64_t split_stride, int32_t B,
                                                            int32_t n, int64_t stride,
                                                            WeightView gamma, float eps, float* y,
-                                                           _Float16* yp) {
+                                                           _Float16* yp, int32_t* yexp) {
   __shared__ float red[4];
   const int64_t b = blockIdx.x;
   constexpr int kPer = 8;  // values per thread kept in registers (n <= 2048)
   float v[kPer];
-  float ss = 0.f;
+  float ss = 0.f, mg = 0.f;  // mg: largest |value * gamma| (the output's, before 1 / rms)
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = threadIdx.x + 256 * r;
     v[r] = i < n ? sum_splits(part + b * stride + i, S, split_stride) : 0.f;
     ss = fmaf(v[r], v[r], ss);
+    if (i < n) mg = fmaxf(mg, fabsf(v[r] * gamma_at(gamma, i)));
   }
   for (int i = threadIdx.x + 256 * kPer; i < n; i += 256) {
     const float t = sum_splits(part + b * stride + i, S, split_stride);
     ss = fmaf(t, t, ss);
+    mg = fmaxf(mg, fabsf(t * gamma_at(gamma, i)));
   }
   const float tot = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+  // packed output: scaled into binary16's range (the scale's rounding margin
+  // is far inside it: the largest scaled value stays below 2^15 (1 + 2^-20))
+  int e = 0;
+  if (yp) {
+    e = f16_range_exp(block_max(mg, red) * inv);
+    if (yexp && threadIdx.x == 0) yexp[b] = e;
+  }
+  const float sc = pow2f(-e);
   auto put = [&](int i, float t) {
     const float o = t * inv * gamma_at(gamma, i);
-    if (yp) yp[packed_index(0, b, i, B, n)] = (_Float16)o;
+    if (yp) yp[packed_index(0, b, i, B, n)] = (_Float16)(o * sc);
     else y[b * stride + i] = o;
   };
 #pragma unroll
@@ -433,22 +503,32 @@ __device__ __forceinline__ void gamma8(const WeightView& g, int k0, float gm[8])
 __device__ __forceinline__ void rmsnorm_pack_row(const float* part, int32_t S, int64_t split_stride,
                                                  int32_t B, int32_t n, int64_t stride,
                                                  WeightView gamma, float eps, _Float16* yp,
-                                                 int64_t b, float* red) {
+                                                 int32_t* yexp, int64_t b, float* red) {
   const int k0 = 8 * threadIdx.x;
   const bool on = k0 < n;
-  float v[8];
+  float v[8] = {};
   if (on) sum_splits8(part + b * stride + k0, S, split_stride, v);
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss = on ? fmaf(v[i], v[i], ss) : ss;
   const float tot = block_sum(ss, red);
-  if (!on) return;
   const float inv = 1.0f / sqrtf(tot / (float)n + eps);
-  float gm[8];
-  gamma8(gamma, k0, gm);
+  float gm[8] = {};
+  if (on) gamma8(gamma, k0, gm);
   float o[8];
+  float mx = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = v[i] * inv * gm[i];
+  for (int i = 0; i < 8; ++i) {
+    o[i] = on ? v[i] * inv * gm[i] : 0.f;
+    mx = fmaxf(mx, fabsf(o[i]));
+  }
+  // the row scaled into binary16's range by a power of two
+  const int e = f16_range_exp(block_max(mx, red));
+  if (!on) return;
+  if (yexp && threadIdx.x == 0) yexp[b] = e;
+  const float sc = pow2f(-e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] *= sc;
   const f16x8_t h = {(_Float16)o[0], (_Float16)o[4], (_Float16)o[1], (_Float16)o[5],
                      (_Float16)o[2], (_Float16)o[6], (_Float16)o[3], (_Float16)o[7]};
   *reinterpret_cast<uint4*>(yp + packed_index(0, b, k0, B, n)) = __builtin_bit_cast(uint4, h);
@@ -458,9 +538,9 @@ __global__ void __launch_bounds__(1024) rmsnorm_pack_kernel(const float* part, i
                                                             int64_t split_stride, int32_t B,
                                                             int32_t n, int64_t stride,
                                                             WeightView gamma, float eps,
-                                                            _Float16* yp) {
+                                                            _Float16* yp, int32_t* yexp) {
   __shared__ float red[16];
-  rmsnorm_pack_row(part, S, split_stride, B, n, stride, gamma, eps, yp, blockIdx.x, red);
+  rmsnorm_pack_row(part, S, split_stride, B, n, stride, gamma, eps, yp, yexp, blockIdx.x, red);
 }
 
 // (x, y) -> mscale * (x cos a - y sin a, x sin a + y cos a), a = pos * inv_freq.
@@ -590,7 +670,7 @@ __global__ void __launch_bounds__(1024) append_qnorm_kernel(AppendArgs a, QNormA
   const int b = blockIdx.x;
   if (b < a.B) append_row_vec<T>(a, b, red);
   else rmsnorm_pack_row(q.part, q.S, q.split_stride, a.B, q.n, q.stride, q.gamma, q.eps, q.yp,
-                        b - a.B, red);
+                        q.yexp, b - a.B, red);
 }
 
 // grid (H, ceil(C/128)); thread = one latent column c of head h.  Each W_UK
@@ -683,6 +763,21 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
   const int tok = b0 + l32;
   const bool tok_ok = tok < a.B;
   const float* qp = a.q + ((size_t)(tok_ok ? tok : 0) * a.H + h) * QW;
+  // q_nope of (token, head) enters the MFMAs times 2^-qe, its largest
+  // magnitude brought into binary16's range; the results are multiplied back
+  int qe = 0;
+  if (wave_on) {
+    float m = 0.f;
+    if (tok_ok)
+      for (int n = 4 * hh; n < a.N; n += 8) {
+        const float4 v = *reinterpret_cast<const float4*>(qp + n);
+        m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+      }
+    float lo, hi;
+    wave_halves(m, &lo, &hi);
+    qe = f16_range_exp(fmaxf(lo, hi));
+  }
+  const float qsc = pow2f(-qe);
   const int64_t row0 = (int64_t)h * (a.N + a.V);
   const int64_t cols8 = a.kv_b.cols >> 3, cols64 = a.kv_b.cols >> 6;
   // staging role: rows 2np, 2np+1 (np = thread % 64), columns 32 cq .. 32 cq + 31
@@ -743,8 +838,9 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
         if (tok_ok) {
           const float4 x0 = *reinterpret_cast<const float4*>(qp + n0 + nb);
           const float4 x1 = *reinterpret_cast<const float4*>(qp + n0 + nb + 4);
-          qa = f16x8_t{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
-                       (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+          qa = f16x8_t{(_Float16)(x0.x * qsc), (_Float16)(x0.y * qsc), (_Float16)(x0.z * qsc),
+                       (_Float16)(x0.w * qsc), (_Float16)(x1.x * qsc), (_Float16)(x1.y * qsc),
+                       (_Float16)(x1.z * qsc), (_Float16)(x1.w * qsc)};
         }
         const f16x8_t wb = *reinterpret_cast<const f16x8_t*>(&wt[(c0 + l32) * kAbsPitch + nb]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, wb, acc, 0, 0, 0);
@@ -757,7 +853,8 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int t = b0 + (j >> 2) * 8 + hh * 4 + (j & 3);
-    if (t < a.B) Elem<T>::store(out, ((size_t)t * a.H + h) * W + c, acc[j]);
+    const int et = __shfl(qe, t - b0, 64);  // token t's exponent, from lane t - b0
+    if (t < a.B) Elem<T>::store(out, ((size_t)t * a.H + h) * W + c, ldexpf(acc[j], et));
   }
 }
 
@@ -918,19 +1015,31 @@ hipError_t launch_pack_f16(const float* x, int64_t x_b, int64_t x_z, int32_t Z, 
   return hipGetLastError();
 }
 
+hipError_t launch_pack_scaled(const float* x, int64_t x_b, int32_t B, int32_t K, _Float16* xp,
+                              int32_t* x_exp, hipStream_t s) {
+  if (B <= 0 || K <= 0) return hipSuccess;
+  if (K % 128 != 0 || !x_exp) return hipErrorInvalidValue;
+  const bool vec = x_b % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  const int64_t slots = (int64_t)(B + 31) / 32 * 32;
+  if (slots > (1ll << 31) - 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_scaled_kernel, dim3((unsigned)slots), dim3(256), 0, s, x, x_b, B, K, vec,
+                     xp, x_exp);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm_rows(const float* part, int32_t S, int64_t split_stride, int32_t B,
                                int32_t n, int64_t stride, WeightView gamma, float eps, float* y,
-                               _Float16* yp, hipStream_t s) {
+                               _Float16* yp, int32_t* yexp, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (S < 1 || S > kMaxKSplits || (yp && n % 128 != 0)) return hipErrorInvalidValue;
   if (qnorm_pack_ok(part, S, split_stride, n, stride, gamma, yp)) {
     const int threads = ((n / 8) + 63) / 64 * 64;
     hipLaunchKernelGGL(rmsnorm_pack_kernel, dim3(B), dim3(threads), 0, s, part, S, split_stride,
-                       B, n, stride, gamma, eps, yp);
+                       B, n, stride, gamma, eps, yp, yexp);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, part, S, split_stride, B, n,
-                     stride, gamma, eps, y, yp);
+                     stride, gamma, eps, y, yp, yexp);
   return hipGetLastError();
 }
 

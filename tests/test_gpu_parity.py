@@ -213,6 +213,31 @@ def test_attn_growing_scores_restart_path():
         attn_check(vc, lse, rvc, rlse, f"split={split}")
 
 
+@pytest.mark.parametrize("head", [5, 37, 127])
+def test_attn_restart_needed_by_one_head(head):
+    # One row's k_pe times 300 and the rope part of q kept in a single head
+    # (not the first of its wave): only that head's maximum leaves the
+    # reference's range, so the restart vote must count every lane of the
+    # wave, not its first.
+    case = S.make_case(4, lens=[300, 1000], seed=21)
+    pool = S.bf16_bits_to_f32(case.pool)
+    for b, r in ((0, 299), (1, 517)):
+        pool[case.table[b][r // 64], r % 64, 512:] *= 300.0
+    case.pool = S.to_bf16_bits(pool)
+    q = S.bf16_bits_to_f32(case.q_abs)
+    keep = q[:, head, 512:].copy()
+    q[:, :, 512:] = 0.0
+    q[:, head, 512:] = np.abs(keep) * np.sign(
+        S.bf16_bits_to_f32(case.pool)[case.table[0][299 // 64], 299 % 64, 512:])
+    case.q_abs = S.to_bf16_bits(q)
+    ns = D.stage(case)
+    rvc, rlse = oracle_attn(case)
+    assert rlse[0, head] > rlse[0].max(initial=0, where=np.arange(128) != head) + 100
+    for split in (0, 64, 2048):
+        vc, lse = attn_only(case, ns, split)
+        attn_check(vc, lse, rvc, rlse, f"head {head} split={split}")
+
+
 @pytest.mark.parametrize("split", [0, 64])
 def test_attn_first_tile_without_finite_scores(split):
     """Rows 0..31 of sequence 0 score -inf for every head (a -inf in a rope
@@ -273,6 +298,27 @@ def test_attn_split_partials_beyond_fp16_range():
         vc, lse = attn_only(case, ns, split)
         assert np.isfinite(vc).all()
         close_bf16(vc * 2.0 ** -17, rvc * 2.0 ** -17, f"v_combine / 2^17 split={split}")
+        attn_tight(vc, lse, rvc, rlse, f"split={split}")
+
+
+def test_attn_split_partials_far_below_fp16_normals():
+    # Latent values scaled by 2^-20 and the latent part of q by 2^20 (exact in
+    # bf16): the scores are unchanged and v_combine scales by 2^-20, below the
+    # smallest binary16 normal (2^-14) the split partials are stored in, so the
+    # per-head exponent must lift them into range (fp16 subnormals would keep
+    # 4 or fewer significant bits and miss the tight check).
+    case = S.make_case(4, lens=[300, 200], seed=16)
+    pool = S.bf16_bits_to_f32(case.pool)
+    pool[..., :512] *= 2.0 ** -20
+    case.pool = S.to_bf16_bits(pool)
+    q = S.bf16_bits_to_f32(case.q_abs)
+    q[..., :512] *= 2.0 ** 20
+    case.q_abs = S.to_bf16_bits(q)
+    ns = D.stage(case)
+    rvc, rlse = oracle_attn(case)
+    for split in (0, 64):
+        vc, lse = attn_only(case, ns, split)
+        close_bf16(vc * 2.0 ** 20, rvc * 2.0 ** 20, f"v_combine * 2^20 split={split}")
         attn_tight(vc, lse, rvc, rlse, f"split={split}")
 
 
@@ -376,6 +422,59 @@ def test_absorb_q(cfg, kw):
         # stored bf16 values sit within one step of the exact product
         ok = np.abs(got - res["q_abs64"]) <= 2.0 ** -7 * np.abs(res["q_abs64"]) + 1e-3
         assert ok.mean() > 0.999
+
+
+def test_chain_hidden_state_beyond_fp16_range():
+    # One token's hidden state holds values far past binary16's range (1.5e5,
+    # -8e4) and another's lies far below its normals (x 2^-20).  The 4-bit
+    # projections pack x per token by a power of two (and the q latent and
+    # the absorbed q_nope rows likewise), so nothing overflows or underflows:
+    # the appended rows, q_abs and the layer match the oracle at the bar.
+    case = S.make_case(5, batch=3, lens=[300, 1100, 64])
+    x = case.x.copy()
+    x[0, 17], x[0, 4000] = 1.5e5, -8.0e4
+    x[1] *= 2.0 ** -20
+    case.x = x
+    ns = D.stage(case)
+    D.run_step(case, ns)
+    sync()
+    res = O.decode_step(case)
+    assert int(host(ns.status)[0]) == 0
+    # per token, relative to the token's own scale as well (the 2^-20 token's
+    # rows are far below the absolute part of the bar): fp16 subnormals would
+    # leave ~3% errors there, the scaled pack leaves the bf16 rounding
+    bs = case.dims.block_size
+    got_pool, ref_pool = O.widen(host(ns.pool), O.BF16), O.widen(res["pool"], O.BF16)
+    got_q = O.widen(host(ns.q_abs), O.BF16)
+    for b, (pos, blk) in enumerate(zip(case.positions, case.table)):
+        r = got_pool[blk[pos // bs], pos % bs]
+        ref = ref_pool[blk[pos // bs], pos % bs]
+        close_bf16(r, ref, f"appended row of sequence {b}")
+        assert np.max(np.abs(r - ref)) <= 1e-2 * np.max(np.abs(ref)), f"row {b} relative"
+        dq = np.max(np.abs(got_q[b] - res["q_abs64"][b]))
+        assert dq <= 1e-2 * np.max(np.abs(res["q_abs64"][b])), f"q_abs of token {b} relative"
+    close_bf16(got_q, res["q_abs64"], "q_abs")
+    close_bf16(host(ns.v_combine), res["v_combine"], "v_combine")
+    close_bf16(host(ns.out), res["out"].reshape(case.batch, -1), "out")
+
+
+def test_absorb_q_latent_beyond_fp16_range():
+    # q_a_norm's gamma times 2^20 (exact in bf16): the normalised q latent and
+    # q itself reach ~1e6, past binary16's range, on the way to q_b and the
+    # absorb MFMAs.  q_abs scales by 2^20 exactly, so the bar applies to
+    # q_abs / 2^20 as it does at the unscaled size.
+    case = S.make_case(5, batch=2, lens=[300, 1100])
+    case.q_a_norm = S.to_bf16_bits(S.bf16_bits_to_f32(case.q_a_norm) * 2.0 ** 20)
+    ns = D.stage(case)
+    ws = D.workspace(ns)
+    mla.absorb_q(ns.dims, ns.x, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
+                 ns.q_a, ns.q_a_norm, ns.q_b, ws)
+    sync()
+    res = oracle_for(case)
+    got = O.widen(host(ns.q_abs), case.dims.cache_dtype)
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(res["q_abs64"])) > 65504.0
+    close_bf16(got * 2.0 ** -20, res["q_abs64"] * 2.0 ** -20, "q_abs / 2^20")
 
 
 @pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(lens=[50, 10], batch=2)),
