@@ -347,6 +347,9 @@ def main():
     ap.add_argument("--attn-only", action="store_true",
                     help="only the attention call on the other full-size workloads (one JSON "
                          "object of them; not the benchmark line)")
+    ap.add_argument("--attn-cfg", type=int, choices=(2, 3, 4), default=None,
+                    help="with --attn-only: just this workload (2: 1 x 4096, 3: 64 ragged "
+                         "paged sequences, 4: 4 x 131072), e.g. for counter passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -366,8 +369,10 @@ def main():
     if args.attn_only:
         extra = {}
         for cfg, name in ((2, "b1_L4096"), (3, "b64_L1024-8192_paged"), (4, "b4_L131072")):
+            if args.attn_cfg not in (None, cfg):
+                continue
             extra[name] = time_attn_only(cfg, torch, D, S, mla, oracle=not args.no_cpu,
-                                         lens_plan=(cfg == 3))
+                                         lens_plan=(cfg == 3 and args.attn_cfg is None))
         print(json.dumps({"attn_only": extra}), flush=True)
         return
     case = S.make_case(5)

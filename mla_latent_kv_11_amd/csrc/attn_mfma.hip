@@ -784,7 +784,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       const float inv_l = bad ? NAN : scale / l_heads[h];
       // head r's 128 columns are 16 chunks of 8 halves (chunk c at slot
       // c ^ (r & 15)), each written as two 4-half pieces by the lane pair
-      // hf = 0, 1; read back as 4 heads x 256 bytes per instruction
+      // hf = 0, 1 (in swapped order for r >= 16, so that rows r and r + 16
+      // fall in different banks); read back as 4 heads x 256 bytes per
+      // instruction
 #pragma unroll
       for (int cbl = 0; cbl < 4; ++cbl) {
 #pragma unroll
@@ -794,7 +796,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
           typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
           const f16x4_t v{(_Float16)(ob[4 * q4 + 0] * inv_l), (_Float16)(ob[4 * q4 + 1] * inv_l),
                           (_Float16)(ob[4 * q4 + 2] * inv_l), (_Float16)(ob[4 * q4 + 3] * inv_l)};
-          *(MLA_LDS f16x4_t*)(stage + l32 * 256 + ((chunk ^ (l32 & 15)) << 4) + hf * 8) = v;
+          *(MLA_LDS f16x4_t*)(stage + l32 * 256 + ((chunk ^ (l32 & 15)) << 4) +
+                              ((hf ^ (l32 >> 4)) << 3)) = v;
         }
       }
       if (wave == 0 && hf == 0) a.part_exp[bs * kH + h] = (float)e;
@@ -803,7 +806,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       for (int i = 0; i < 8; ++i) {
         const int r = 4 * i + (lane >> 4);
         typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-        const u32x4_t v = *(const MLA_LDS u32x4_t*)(stage + r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+        u32x4_t v = *(const MLA_LDS u32x4_t*)(stage + r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+        if (i >= 4) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);  // rows 16..31: halves swapped
         *reinterpret_cast<u32x4_t*>(dst + (size_t)r * kC) = v;
       }
     }
@@ -886,10 +890,25 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   const size_t first = S > 0 ? (size_t)first_raw : 0;
   const float* lse_s = a.part_lse + first * kH + h;  // stride kH over s
   const float* exp_s = a.part_exp + first * kH + h;
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
+  const size_t sstride = (size_t)kH * kC;
 
-  float m = -INFINITY;
-  bool nan_lse = false;  // a bad table entry: NaN through the merge, as above
-  for (int s = lane; s < S; s += 64) {
+  // One memory round trip for everything that needs only the slot range: the
+  // first eight partial rows (the last one repeated past the end; slot 0 for
+  // an empty query, never used) and this lane's split lse and exponent.
+  f16x8_t v0[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int sj = j < S ? j : (S > 0 ? S - 1 : 0);  // uniform
+    v0[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * sstride);
+  }
+  const float ls0 = lane < S ? lse_s[(size_t)lane * kH] : -INFINITY;
+  const float ex0 = lane < S ? exp_s[(size_t)lane * kH] : 0.f;
+
+  float m = ls0;
+  bool nan_lse = ls0 != ls0;  // a bad table entry: NaN through the merge, as above
+  for (int s = 64 + lane; s < S; s += 64) {
     const float l = lse_s[(size_t)s * kH];
     m = fmaxf(m, l);
     nan_lse |= l != l;
@@ -899,7 +918,6 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
   float* dst = a.v_combine + ((size_t)b * kH + h) * kC + lane * 8;
   // the packed fp16 copy: this lane's 8 columns are one 16-byte chunk, in
   // the pair order c0 c4 c1 c5 c2 c6 c3 c7
-  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
   auto put_packed = [&](f32x4_t lo4, f32x4_t hi4) {
     if (!a.vc_pk) return;
     const f16x8_t hv = {(_Float16)lo4[0], (_Float16)hi4[0], (_Float16)lo4[1], (_Float16)hi4[1],
@@ -913,34 +931,34 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
     if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = -INFINITY;
     return;
   }
-  float wsum = 0.f;
-  for (int s = lane; s < S; s += 64) wsum += expf(lse_s[(size_t)s * kH] - m);
+  float wsum = expf(ls0 - m);  // 0 for lanes past the splits (ls0 = -inf)
+  for (int s = 64 + lane; s < S; s += 64) wsum += expf(lse_s[(size_t)s * kH] - m);
   wsum = wave_sum(wsum);
   const float inv = 1.0f / wsum;
 
-  const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
-  const size_t sstride = (size_t)kH * kC;
   f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 64) {
     // this lane's split s0 + lane: its weight, 0 for an empty split (whose
     // partial is never written and is not read)
     float w = 0.f;
     if (s0 + lane < S) {
-      const float ls = lse_s[(size_t)(s0 + lane) * kH];
-      if (ls != -INFINITY) w = ldexpf(expf(ls - m), (int)exp_s[(size_t)(s0 + lane) * kH]);
+      const float ls = s0 == 0 ? ls0 : lse_s[(size_t)(s0 + lane) * kH];
+      const float ex = s0 == 0 ? ex0 : exp_s[(size_t)(s0 + lane) * kH];
+      if (ls != -INFINITY) w = ldexpf(expf(ls - m), (int)ex);
     }
     const int n = S - s0 < 64 ? S - s0 : 64;
     for (int j0 = 0; j0 < n; j0 += 8) {
       // eight loads in flight, no branches: a split past the end re-reads
       // the last row and an empty split's unwritten row is read too, and
-      // both are dropped by a select (not multiplied by 0, which keeps NaN)
+      // both are dropped by a select (not multiplied by 0, which keeps NaN);
+      // the first eight rows were read with the lse
       f16x8_t v[8];
       float wj[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int sj = j0 + j < n ? j0 + j : n - 1;  // uniform
         wj[j] = j0 + j < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sj)) : 0.f;
-        v[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)(s0 + sj) * sstride);
+        v[j] = s0 + j0 == 0 ? v0[j] : *reinterpret_cast<const f16x8_t*>(src + (size_t)(s0 + sj) * sstride);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
