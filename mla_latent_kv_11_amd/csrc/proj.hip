@@ -378,9 +378,22 @@ __global__ void __launch_bounds__(256) pack_scaled_kernel(const float* x, int64_
       for (int i = 0; i < 8; ++i) v[i] = row[k + i];
     }
   };
+  // the first kKeep chunks of each thread stay in registers between the two
+  // passes (K <= 16384 at 256 threads); deeper rows read the rest twice
+  constexpr int kKeep = 8;
+  float keep[kKeep][8] = {};
   float m = 0.f;
   if (b < B) {
-    for (int c = threadIdx.x; c < K / 8; c += 256) {
+#pragma unroll
+    for (int j = 0; j < kKeep; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      if (c < K / 8) {
+        load8(8 * c, keep[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(keep[j][i]));
+      }
+    }
+    for (int c = threadIdx.x + 256 * kKeep; c < K / 8; c += 256) {
       float v[8];
       load8(8 * c, v);
 #pragma unroll
@@ -390,19 +403,28 @@ __global__ void __launch_bounds__(256) pack_scaled_kernel(const float* x, int64_
   const int e = f16_range_exp(block_max(m, red));  // uniform: b is
   if (b < B && threadIdx.x == 0) x_exp[b] = e;
   const float sc = pow2f(-e);
-  for (int c = threadIdx.x; c < K / 8; c += 256) {
+  auto put = [&](int c, const float* v) {
     uint4 o = uint4{0u, 0u, 0u, 0u};
     if (b < B) {
-      float v[8];
-      load8(8 * c, v);
       const f16x8_t h = {(_Float16)(v[0] * sc), (_Float16)(v[4] * sc), (_Float16)(v[1] * sc),
                          (_Float16)(v[5] * sc), (_Float16)(v[2] * sc), (_Float16)(v[6] * sc),
                          (_Float16)(v[3] * sc), (_Float16)(v[7] * sc)};
       o = __builtin_bit_cast(uint4, h);
     }
     *reinterpret_cast<uint4*>(xp + packed_index(0, b, 8 * c, B, K)) = o;
+  };
+#pragma unroll
+  for (int j = 0; j < kKeep; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < K / 8) put(c, keep[j]);
+  }
+  for (int c = threadIdx.x + 256 * kKeep; c < K / 8; c += 256) {
+    float v[8] = {};
+    if (b < B) load8(8 * c, v);
+    put(c, v);
   }
 }
+
 
 __device__ __forceinline__ float gamma_at(const WeightView& g, int i) {
   return g.dtype == MLA_F32 ? static_cast<const float*>(g.data)[i]
@@ -764,20 +786,31 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
   const bool tok_ok = tok < a.B;
   const float* qp = a.q + ((size_t)(tok_ok ? tok : 0) * a.H + h) * QW;
   // q_nope of (token, head) enters the MFMAs times 2^-qe, its largest
-  // magnitude brought into binary16's range; the results are multiplied back
+  // magnitude brought into binary16's range; the results are multiplied back.
+  // The lane's operands of the first 128 n are read here, before the W_UK
+  // slice's loads, so both latencies overlap; the scale is formed after them.
+  float4 q0[16];  // n = 64 hh + 8 st + (0..3 | 4..7), st < 8
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    q0[i] = wave_on && tok_ok ? *reinterpret_cast<const float4*>(qp + 64 * hh + 4 * i)
+                              : float4{0.f, 0.f, 0.f, 0.f};
   int qe = 0;
-  if (wave_on) {
+  float qsc = 1.f;
+  auto range_scale = [&]() {
     float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      m = fmaxf(fmaxf(m, fmaxf(fabsf(q0[i].x), fabsf(q0[i].y))), fmaxf(fabsf(q0[i].z), fabsf(q0[i].w)));
     if (tok_ok)
-      for (int n = 4 * hh; n < a.N; n += 8) {
+      for (int n = kAbsN + 4 * hh; n < a.N; n += 8) {  // the rest of a deeper q_nope
         const float4 v = *reinterpret_cast<const float4*>(qp + n);
         m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
       }
     float lo, hi;
     wave_halves(m, &lo, &hi);
     qe = f16_range_exp(fmaxf(lo, hi));
-  }
-  const float qsc = pow2f(-qe);
+    qsc = pow2f(-qe);
+  };
   const int64_t row0 = (int64_t)h * (a.N + a.V);
   const int64_t cols8 = a.kv_b.cols >> 3, cols64 = a.kv_b.cols >> 6;
   // staging role: rows 2np, 2np+1 (np = thread % 64), columns 32 cq .. 32 cq + 31
@@ -829,6 +862,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
             __builtin_bit_cast(uint32_t, pr);
       }
     }
+    if (n0 == 0 && wave_on) range_scale();
     __syncthreads();
     if (wave_on) {
 #pragma unroll
@@ -836,8 +870,8 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
         const int nb = 64 * hh + 8 * st;
         f16x8_t qa = f16x8_t{};
         if (tok_ok) {
-          const float4 x0 = *reinterpret_cast<const float4*>(qp + n0 + nb);
-          const float4 x1 = *reinterpret_cast<const float4*>(qp + n0 + nb + 4);
+          const float4 x0 = n0 == 0 ? q0[2 * st] : *reinterpret_cast<const float4*>(qp + n0 + nb);
+          const float4 x1 = n0 == 0 ? q0[2 * st + 1] : *reinterpret_cast<const float4*>(qp + n0 + nb + 4);
           qa = f16x8_t{(_Float16)(x0.x * qsc), (_Float16)(x0.y * qsc), (_Float16)(x0.z * qsc),
                        (_Float16)(x0.w * qsc), (_Float16)(x1.x * qsc), (_Float16)(x1.y * qsc),
                        (_Float16)(x1.z * qsc), (_Float16)(x1.w * qsc)};
