@@ -13,8 +13,10 @@ append/absorb and out_proj), and also back to back (a replayed graph of 20
 calls; ``--eager``: one by one).  The
 workload is the full per-layer configuration: batch 32, 16384 cached rows per
 sequence (append at 16383), DeepSeek-V3 shapes (128 heads, latent 512, rope
-64), hidden 7168, q_lora 1536, 4-bit affine (group 64) projections, bf16
-cache.  Inputs are synthetic (seeded) and resident in HBM before timing.
+64), hidden 7168, q_lora 1536, 4-bit affine (group 64) projections (repacked
+once, before timing, into the library's tiled layout; ``--row-major-weights``:
+as given), bf16 cache.  Inputs are synthetic (seeded) and resident in HBM
+before timing.
 
 Prints one JSON line.  ``roofline`` describes the attention call (its split
 kernel plus the split-K combine kernel), timed with HIP events on the stream
@@ -29,6 +31,7 @@ timed on the same inputs.
 from __future__ import annotations
 
 import argparse
+import copy
 import hashlib
 import json
 import os
@@ -242,7 +245,7 @@ def time_tokens(torch, D, S, mla, iters=10):
     for name, prior, chunk in (("decode_b32_t4_L16384", [16380] * 32, 4),
                                ("prefill_b4_t512_L8192", [8192] * 4, 512)):
         case = S.make_chunk_case(5, prior, chunk)
-        ns = D.stage(case)
+        ns = D.stage(case, tiled=True)
         step = D.GraphStep(case, ns)
         for _ in range(3):
             step.run(eager=True)
@@ -347,6 +350,8 @@ def main():
     ap.add_argument("--attn-only", action="store_true",
                     help="only the attention call on the other full-size workloads (one JSON "
                          "object of them; not the benchmark line)")
+    ap.add_argument("--row-major-weights", action="store_true",
+                    help="time the step on the 4-bit weights as given (no tiled repack)")
     ap.add_argument("--attn-cfg", type=int, choices=(2, 3, 4), default=None,
                     help="with --attn-only: just this workload (2: 1 x 4096, 3: 64 ragged "
                          "paged sequences, 4: 4 x 131072), e.g. for counter passes")
@@ -376,7 +381,14 @@ def main():
         print(json.dumps({"attn_only": extra}), flush=True)
         return
     case = S.make_case(5)
-    ns = D.stage(case)
+    # The 4-bit weights are repacked once, before timing, into the tiled
+    # format the MFMA products read in whole lines (mla_repack_q4g64), as a
+    # server would at load time; the row-major step is timed beside it.
+    ns_rm = D.stage(case)
+    ns = ns_rm
+    if not args.row_major_weights:
+        ns = copy.copy(ns_rm)
+        D.tile_weights(ns)
     B = case.batch
     rows = int(case.lens.sum())
     # One step = one mla_decode_layer call (the fused front, attention with its
@@ -400,6 +412,9 @@ def main():
 
     ms_step, (settle_ms, settle_steps) = timed_steps(D.LayerStep(case, ns))
     assert int(ns.status.cpu()[0]) == 0
+    ms_step_rm = None
+    if ns is not ns_rm:
+        ms_step_rm, _ = timed_steps(D.LayerStep(case, ns_rm))
     # The same step as the four calls: cache_append and absorb_q on two streams
     # (independent), then decode_attn, then out_proj, replayed as one HIP graph
     # (--eager: launched one by one on one stream).
@@ -472,6 +487,10 @@ def main():
             "launch": "one mla_decode_layer call per step, eager" if args.eager else
                       "one HIP graph per step holding one mla_decode_layer call (9 kernels, "
                       "one stream)",
+            "weights": "4-bit g64 as given (row-major)" if ns is ns_rm else
+                       "4-bit g64 repacked once before timing into the tiled layout "
+                       "(mla_repack_q4g64, MLA_Q4G64_T; same values, same results)",
+            "ms_per_step_row_major_weights": None if ms_step_rm is None else round(ms_step_rm, 4),
             "ms_per_step_four_calls": round(ms_step_calls, 4),
             "four_calls_launch": "eager, one stream" if args.eager else
                                  "cache_append | absorb_q on two streams, decode_attn, "

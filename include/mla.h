@@ -68,7 +68,8 @@ enum {
   MLA_F32 = 0,   /* IEEE float32 */
   MLA_BF16 = 1,  /* bfloat16 bit patterns (uint16) */
   MLA_Q4G64 = 2, /* 4-bit affine, group 64 along the input dim (weights only) */
-  MLA_Q8_0 = 3   /* 8-bit blocks of 32 with a binary16 scale (kv_b only) */
+  MLA_Q8_0 = 3,  /* 8-bit blocks of 32 with a binary16 scale (kv_b only) */
+  MLA_Q4G64_T = 4 /* MLA_Q4G64 repacked in MFMA fragment order (mla_repack_q4g64) */
 };
 
 /* ---- device status flags OR-ed by mla_cache_append (dev_status) ---- */
@@ -107,6 +108,16 @@ typedef struct mla_dims {
  *     falls into its subnormals.  v_combine and the per-head W_UV outputs
  *     enter W_UV and o_proj unscaled: they are bounded by the cache latents
  *     (|c| <= sqrt(C) max|kv_a_norm gamma|) times the weights.
+ *   MLA_Q4G64_T: the same values as MLA_Q4G64, repacked by mla_repack_q4g64
+ *     (rows a multiple of 32, cols of 128) so that the 4-bit MFMA products
+ *     read them in whole lines: for row tile t = r/32 and unit u = k/128, a
+ *     2048-byte block at (t * cols/128 + u) * 2048 holds two 1 KB parts; lane
+ *     L = r%32 + 32*h (h = (k%128)/64) owns 16 bytes at part*1024 + 16*L,
+ *     part = (k%64)/32, with the row-major format's nibble order inside (the
+ *     32 elements 64h + 32*part .. +31 of the unit, low nibble first).
+ *     scales and biases: bf16 at (t * cols/128 + u) * 64 + L (group 2u + h of
+ *     row r).  Accepted wherever MLA_Q4G64 is; it changes the reads, not the
+ *     arithmetic (results equal bit for bit).
  *   MLA_Q8_0: data = bytes, [rows][cols/32] blocks of 34: a little-endian
  *     binary16 scale d, then 32 signed bytes q; element = d * q (turbospark
  *     deepseek2/attn.rs, validate_q8_0_matrix: kv_b read in place; the byte
@@ -309,6 +320,22 @@ int mla_decode_layer(const mla_dims* dims, int32_t batch, const float* x, const 
  * and split_rows (0 = automatic).  Returns 0 for invalid dims. */
 size_t mla_layer_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
                                  int32_t split_rows);
+
+/* mla_repack_q4g64 -- a MLA_Q4G64 weight repacked into MLA_Q4G64_T (see
+ * mla_weight), once, for the faster 4-bit products: the 4-bit MFMA kernels
+ * read a row-major weight in 16 bytes per row for 32 rows per load
+ * instruction, the repacked one in 1 KB contiguous per instruction (o_proj
+ * at batch 32: the whole out_proj call 29.7 against 39.3 us with the weights
+ * in the last-level cache, 50.8 against 63.8 us from HBM).  The tiled format
+ * is this library's; the sources' 4-bit format (gpu_matvec.rs MatvecSpec) is
+ * the row-major MLA_Q4G64, which stays the input.
+ *   src       a MLA_Q4G64 weight, rows a multiple of 32, cols of 128
+ *   data      device, rows * cols / 2 bytes, written
+ *   scales, biases  device bf16 [rows * cols / 64] each, written
+ * The caller then passes {MLA_Q4G64_T, rows, cols, data, scales, biases}.
+ * Errors: NULL, DTYPE (src not MLA_Q4G64), DIMS (rows, cols). */
+int mla_repack_q4g64(const mla_weight* src, void* data, uint16_t* scales, uint16_t* biases,
+                     void* stream);
 
 /* mla_decode_attn_noalloc -- mla_decode_attn for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

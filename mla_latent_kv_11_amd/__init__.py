@@ -24,14 +24,14 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK = 0
 MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_DTYPE, MLA_ERR_UNSUPPORTED = -1, -2, -3, -4
 MLA_ERR_CAPACITY, MLA_ERR_WORKSPACE, MLA_ERR_HIP = -5, -6, -7
-MLA_F32, MLA_BF16, MLA_Q4G64, MLA_Q8_0 = 0, 1, 2, 3
+MLA_F32, MLA_BF16, MLA_Q4G64, MLA_Q8_0, MLA_Q4G64_T = 0, 1, 2, 3, 4
 MLA_DEV_POS_RANGE, MLA_DEV_BAD_BLOCK, MLA_DEV_BAD_SEQ = 1, 2, 4
 
 EXPORTED = ("mla_yarn_tables", "mla_cache_append", "mla_absorb_q", "mla_decode_attn",
             "mla_out_proj", "mla_cache_append_tokens", "mla_attn_tokens",
             "mla_validate_q8_0_kv_b", "mla_workspace_bytes", "mla_attn_plan",
             "mla_attn_plan_lens", "mla_status_str", "mla_decode_attn_noalloc",
-            "mla_decode_layer", "mla_layer_workspace_bytes")
+            "mla_decode_layer", "mla_layer_workspace_bytes", "mla_repack_q4g64")
 MLA_NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
@@ -126,6 +126,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_decode_layer": ([PD, I32, P, P, ctypes.POINTER(CLayer), P, PC, P, I32,
                               ctypes.c_float, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "mla_layer_workspace_bytes": ([PD, I32, I32, I32], SZ),
+        "mla_repack_q4g64": ([PW, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -189,6 +190,22 @@ class Weight:
     def c(self) -> CWeight:
         return CWeight(self.dtype, self.rows, self.cols, _ptr(self.data), _ptr(self.scales),
                        _ptr(self.biases))
+
+
+def repack_q4g64(w: Weight, stream=None) -> Weight:
+    """The MLA_Q4G64 weight ``w`` repacked as MLA_Q4G64_T (mla_repack_q4g64):
+    the same values in the layout the 4-bit MFMA products read in whole lines.
+    The new buffers are torch tensors on ``w``'s device."""
+    import torch
+    if w.dtype != MLA_Q4G64:
+        raise MLAError("mla_repack_q4g64", MLA_ERR_DTYPE)
+    dev = w.data.device
+    data = torch.empty(w.rows * w.cols // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(w.rows * w.cols // 64, dtype=torch.int16, device=dev)
+    biases = torch.empty_like(scales)
+    _check(load_library().mla_repack_q4g64(ctypes.byref(w.c()), _ptr(data), _ptr(scales),
+                                           _ptr(biases), _stream(stream)), "mla_repack_q4g64")
+    return Weight(MLA_Q4G64_T, w.rows, w.cols, data, scales, biases)
 
 
 def _c_or_null(obj, ctype):

@@ -55,16 +55,19 @@ int dims_status(const mla_dims* d) {
 }
 
 // A weight must be non-null, of an accepted dtype, and exactly [rows, cols].
-// allow_q4: the 4-bit affine format; allow_q8: Q8_0 (kv_b only).
+// allow_q4: the 4-bit affine format, row-major or tiled; allow_q8: Q8_0
+// (kv_b only).
 int check_weight(const mla_weight* w, int64_t rows, int64_t cols, bool allow_q4,
                  bool allow_q8 = false) {
   if (!w || !w->data) return MLA_ERR_NULL;
-  if (w->dtype != MLA_F32 && w->dtype != MLA_BF16 && !(allow_q4 && w->dtype == MLA_Q4G64) &&
+  const bool q4 = w->dtype == MLA_Q4G64 || w->dtype == MLA_Q4G64_T;
+  if (w->dtype != MLA_F32 && w->dtype != MLA_BF16 && !(allow_q4 && q4) &&
       !(allow_q8 && w->dtype == MLA_Q8_0))
     return MLA_ERR_DTYPE;
   if (w->rows != rows || w->cols != cols) return MLA_ERR_DIMS;
-  if (w->dtype == MLA_Q4G64) {
+  if (q4) {
     if (cols % 64 != 0) return MLA_ERR_DIMS;
+    if (w->dtype == MLA_Q4G64_T && (cols % 128 != 0 || rows % 32 != 0)) return MLA_ERR_DIMS;
     if (!w->scales || !w->biases) return MLA_ERR_NULL;
   }
   if (w->dtype == MLA_Q8_0 && (cols % 32 != 0 || cols <= 0)) return MLA_ERR_DIMS;
@@ -208,6 +211,16 @@ int mla_validate_q8_0_kv_b(int32_t dtype, int64_t rows, int64_t cols, int64_t si
   if (rows > INT64_MAX / row_bytes) return MLA_ERR_DIMS;
   if (size_bytes != rows * row_bytes) return MLA_ERR_DIMS;
   return MLA_OK;
+}
+
+int mla_repack_q4g64(const mla_weight* src, void* data, uint16_t* scales, uint16_t* biases,
+                     void* stream) {
+  if (!src || !src->data || !src->scales || !src->biases || !data || !scales || !biases)
+    return MLA_ERR_NULL;
+  if (src->dtype != MLA_Q4G64) return MLA_ERR_DTYPE;
+  if (src->rows < 0 || src->cols < 0 || src->rows % 32 != 0 || src->cols % 128 != 0)
+    return MLA_ERR_DIMS;
+  return hip_status(launch_repack_q4(view(src), data, scales, biases, (hipStream_t)stream));
 }
 
 const char* mla_status_str(int st) {

@@ -55,6 +55,15 @@ __device__ __forceinline__ float weight_at(const WeightView& w, int64_t r, int64
     const uint16_t dbits = (uint16_t)(blk[0] | (blk[1] << 8));
     return (float)__builtin_bit_cast(_Float16, dbits) * (float)(int8_t)blk[2 + (k & 31)];
   }
+  if (w.dtype == MLA_Q4G64_T) {  // 2 KB block per (row tile, 128-k unit), lane order
+    const int64_t j = k & 63, L = (r & 31) + 32 * ((k >> 6) & 1);
+    const int64_t blk = (r >> 5) * (w.cols >> 7) + (k >> 7);
+    const uint32_t word = static_cast<const uint32_t*>(w.data)[blk * 512 + (j >> 5) * 256 + 4 * L +
+                                                                ((j & 31) >> 3)];
+    const float q = static_cast<float>((word >> (4 * (k & 7))) & 15u);
+    const int64_t g = blk * 64 + L;
+    return fmaf(bf16_to_f32(w.scales[g]), q, bf16_to_f32(w.biases[g]));
+  }
   const uint32_t word = static_cast<const uint32_t*>(w.data)[r * (w.cols >> 3) + (k >> 3)];
   const float q = static_cast<float>((word >> (4 * (k & 7))) & 15u);
   const int64_t g = r * (w.cols >> 6) + (k >> 6);
@@ -203,6 +212,9 @@ struct AppendArgs {
   float eps;
 };
 hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s);
+// MLA_Q4G64 [rows, cols] (rows % 32 == 0, cols % 128 == 0) -> MLA_Q4G64_T.
+hipError_t launch_repack_q4(const WeightView& src, void* data, uint16_t* scales, uint16_t* biases,
+                            hipStream_t s);
 
 // RMSNorm of a q latent from its split partial sums, into the packed layout.
 struct QNormArgs {

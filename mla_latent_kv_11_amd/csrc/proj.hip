@@ -168,8 +168,15 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmArgs& a, int bx, int nw
   const char* sbase = reinterpret_cast<const char*>(a.w.scales);
   const char* bbase = reinterpret_cast<const char*>(a.w.biases);
   const char* xbase = reinterpret_cast<const char*>(a.xp);
-  const uint32_t woff = wrow * (uint32_t)(a.w.cols >> 1) + 32u * hh;  // + 64 per unit
-  const uint32_t soff = wrow * (uint32_t)(a.w.cols >> 6) * 2u + 2u * hh;  // + 4 per unit
+  // Row-major 4-bit rows: the lane's 32 bytes of a unit at 64 B per unit along
+  // its row (a load instruction touches 32 rows).  MLA_Q4G64_T: a 2 KB block
+  // per (32-row tile, unit), lane (wrow % 32) + 32 hh at 16 B steps in each
+  // 1 KB half, so a load instruction reads 1 KB in one piece.
+  const bool tiled = a.w.dtype == MLA_Q4G64_T;
+  const uint32_t tblk = (wrow >> 5) * (uint32_t)(a.w.cols >> 7), tlane = (wrow & 31u) + 32u * hh;
+  const uint32_t woff = tiled ? tblk * 2048u + 16u * tlane : wrow * (uint32_t)(a.w.cols >> 1) + 32u * hh;
+  const uint32_t soff = tiled ? tblk * 128u + 2u * tlane : wrow * (uint32_t)(a.w.cols >> 6) * 2u + 2u * hh;
+  const uint32_t wstep = tiled ? 2048u : 64u, whalf = tiled ? 1024u : 16u, sstep = tiled ? 128u : 4u;
   const uint32_t xoff =
       (uint32_t)((zz * gridDim.y + blockIdx.y) * units) * 8192u + 16u * lane;  // + 8192 per unit
   // Q8_0: byte offset of the lane's first block (+ 136 per unit), and the
@@ -192,9 +199,9 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmArgs& a, int bx, int nw
         ub[slot].qx[j] = *reinterpret_cast<const uint16_t*>(wbase + ((qs & 2u) ? al + 32u : al + 30u));
       }
     } else {
-      const uint32_t wo = woff + 64u * ku, so = soff + 4u * ku;
+      const uint32_t wo = woff + wstep * ku, so = soff + sstep * ku;
       ub[slot].w[0] = *reinterpret_cast<const uint4*>(wbase + wo);
-      ub[slot].w[1] = *reinterpret_cast<const uint4*>(wbase + wo + 16u);
+      ub[slot].w[1] = *reinterpret_cast<const uint4*>(wbase + wo + whalf);
       ub[slot].sc = *reinterpret_cast<const uint16_t*>(sbase + so);
       ub[slot].bi = *reinterpret_cast<const uint16_t*>(bbase + so);
     }
@@ -813,6 +820,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
   };
   const int64_t row0 = (int64_t)h * (a.N + a.V);
   const int64_t cols8 = a.kv_b.cols >> 3, cols64 = a.kv_b.cols >> 6;
+  const bool tiled = a.kv_b.dtype == MLA_Q4G64_T;
   // staging role: rows 2np, 2np+1 (np = thread % 64), columns 32 cq .. 32 cq + 31
   const int np = threadIdx.x & 63, cq = threadIdx.x >> 6;
   const int cst = cw0 + 32 * cq;
@@ -846,10 +854,19 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int64_t row = row0 + n0 + 2 * np + r;
-        wv[r] = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(a.kv_b.data) +
-                                                row * cols8 + (cst >> 3));
-        sc[r] = bf16_to_f32(a.kv_b.scales[row * cols64 + (cst >> 6)]);
-        bi[r] = bf16_to_f32(a.kv_b.biases[row * cols64 + (cst >> 6)]);
+        int64_t wq, g;  // uint4 index of the 32 columns, index of their group's scale
+        if (tiled) {  // 2 KB block per (32-row tile, 128 columns); see the GEMM body
+          const int64_t blk = (row >> 5) * (a.kv_b.cols >> 7) + (cst >> 7);
+          const int64_t L = (row & 31) + 32 * ((cst >> 6) & 1);
+          wq = blk * 128 + ((cst >> 5) & 1) * 64 + L;
+          g = blk * 64 + L;
+        } else {
+          wq = (row * cols8 + (cst >> 3)) >> 2;
+          g = row * cols64 + (cst >> 6);
+        }
+        wv[r] = static_cast<const uint4*>(a.kv_b.data)[wq];
+        sc[r] = bf16_to_f32(a.kv_b.scales[g]);
+        bi[r] = bf16_to_f32(a.kv_b.biases[g]);
       }
       const uint32_t w0[4] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w};
       const uint32_t w1[4] = {wv[1].x, wv[1].y, wv[1].z, wv[1].w};
@@ -895,6 +912,37 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
 }  // namespace
 
 namespace {
+// One 2 KB block of MLA_Q4G64_T per workgroup of 64 threads: thread L copies
+// row 32 t + L % 32's two 16-byte pieces of columns 128 u + 64 (L / 32) ..
+// +63 and that group's scale and bias.
+__global__ void __launch_bounds__(64) repack_q4_kernel(WeightView w, uint8_t* od, uint16_t* osc,
+                                                        uint16_t* obi) {
+  const int64_t Un = w.cols >> 7, blk = blockIdx.x;
+  const int64_t t = blk / Un, u = blk - t * Un;
+  const int L = threadIdx.x;
+  const int64_t row = 32 * t + (L & 31), g = row * (w.cols >> 6) + 2 * u + (L >> 5);
+  const uint8_t* src = static_cast<const uint8_t*>(w.data) + row * (w.cols >> 1) + 64 * u + 32 * (L >> 5);
+  uint8_t* dst = od + blk * 2048 + 16 * L;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  *reinterpret_cast<uint4*>(dst + 1024) = *reinterpret_cast<const uint4*>(src + 16);
+  osc[blk * 64 + L] = w.scales[g];
+  obi[blk * 64 + L] = w.biases[g];
+}
+}  // namespace
+
+hipError_t launch_repack_q4(const WeightView& src, void* data, uint16_t* scales, uint16_t* biases,
+                            hipStream_t s) {
+  if (src.dtype != MLA_Q4G64 || src.rows % 32 != 0 || src.cols % 128 != 0)
+    return hipErrorInvalidValue;
+  const int64_t blocks = (src.rows / 32) * (src.cols / 128);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > (1ll << 31) - 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(repack_q4_kernel, dim3((unsigned)blocks), dim3(64), 0, s, src,
+                     static_cast<uint8_t*>(data), scales, biases);
+  return hipGetLastError();
+}
+
+namespace {
 constexpr int kMaxU = 16;
 
 hipError_t launch_q4(const GemmArgs& a, int U, int nw, int S, hipStream_t s) {
@@ -928,8 +976,9 @@ bool gemm_mfma_ok(const GemmArgs& a) {
   const int64_t xbytes = (int64_t)packed_bytes(a.Z, a.B, a.K);
   // Q8_0 blocks are read with aligned dword loads from a 4-byte aligned base
   if (q8 && (reinterpret_cast<uintptr_t>(a.w.data) & 3) != 0) return false;
-  return (a.w.dtype == MLA_Q4G64 || q8) && a.K > 0 && (a.K % 128) == 0 &&
-         (a.w.cols % (q8 ? 32 : 64)) == 0 &&
+  const bool tiled = a.w.dtype == MLA_Q4G64_T;
+  return (a.w.dtype == MLA_Q4G64 || tiled || q8) && a.K > 0 && (a.K % 128) == 0 &&
+         (a.w.cols % (q8 ? 32 : tiled ? 128 : 64)) == 0 && (!tiled || a.w.rows % 32 == 0) &&
          a.K <= a.w.cols && (a.K / 128) <= kQ4MaxWaves * kMaxU && wbytes < (1ll << 31) &&
          xbytes < (1ll << 31);
 }
@@ -1003,7 +1052,7 @@ int64_t q4_tiles(const GemmArgs& a) { return (int64_t)((a.O + 31) / 32) * a.Z * 
 // single launch.
 bool gemm_pair_ok(const GemmArgs& a, const GemmArgs& b) {
   return a.O > 0 && b.O > 0 && a.B > 0 && a.Z == 1 && b.Z == 1 && a.K == b.K && a.B == b.B &&
-         gemm_mfma_ok(a) && gemm_mfma_ok(b) && a.w.dtype == MLA_Q4G64 && b.w.dtype == MLA_Q4G64 &&
+         gemm_mfma_ok(a) && gemm_mfma_ok(b) && a.w.dtype != MLA_Q8_0 && b.w.dtype != MLA_Q8_0 &&
          a.xp && a.xp == b.xp &&
          !a.yp && !b.yp && a.y && b.y && (q4_tiles(a) >= 128) == (q4_tiles(b) >= 128);
 }
@@ -1114,7 +1163,9 @@ hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s) {
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   const bool q8_ok = a.kv_b.dtype == MLA_Q8_0 && (reinterpret_cast<uintptr_t>(a.kv_b.data) & 1) == 0;
-  if ((a.kv_b.dtype == MLA_Q4G64 || q8_ok) && a.N % kAbsN == 0 && a.C % 32 == 0) {
+  const bool q4 = a.kv_b.dtype == MLA_Q4G64 ||
+                  (a.kv_b.dtype == MLA_Q4G64_T && a.kv_b.rows % 32 == 0 && a.kv_b.cols % 128 == 0);
+  if ((q4 || q8_ok) && a.N % kAbsN == 0 && a.C % 32 == 0) {
     dim3 grid(a.H, (a.C + 127) / 128, (a.B + 31) / 32);
     const bool q8 = a.kv_b.dtype == MLA_Q8_0;
     if (a.cache_dtype == MLA_F32) {

@@ -40,8 +40,18 @@ def dims_of(case: Case) -> mla.Dims:
                     d.block_size, d.cache_dtype, d.rms_eps)
 
 
-def stage(case: Case, device="cuda") -> types.SimpleNamespace:
-    """Everything a decode step of ``case`` needs, resident in device memory."""
+def tile_weights(ns) -> None:
+    """Swap every 4-bit weight of ``ns`` whose shape allows it (rows a multiple
+    of 32, cols of 128) for its MLA_Q4G64_T repack."""
+    for name in ("kv_a", "q_a", "q_b", "kv_b", "o_proj"):
+        w = getattr(ns, name)
+        if w is not None and w.dtype == mla.MLA_Q4G64 and w.rows % 32 == 0 and w.cols % 128 == 0:
+            setattr(ns, name, mla.repack_q4g64(w))
+
+
+def stage(case: Case, device="cuda", tiled: bool = False) -> types.SimpleNamespace:
+    """Everything a decode step of ``case`` needs, resident in device memory
+    (``tiled``: the 4-bit weights repacked by the library, see tile_weights)."""
     d = case.dims
     H, N, R, V, C = d.num_heads, d.qk_nope, d.qk_rope, d.v_head, d.kv_lora
     ns = types.SimpleNamespace()
@@ -77,6 +87,8 @@ def stage(case: Case, device="cuda") -> types.SimpleNamespace:
     ns.inv_freq = torch.tensor(inv, dtype=torch.float32, device=device)
     ns.rope_mscale = rm
     ns.softmax_scale = float(case.softmax_scale) if case.softmax_scale is not None else sc
+    if tiled:
+        tile_weights(ns)
     return ns
 
 

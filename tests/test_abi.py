@@ -320,3 +320,35 @@ def test_layer_validation_before_launch(lib):
     for B, L in ((1, 128), (32, 16384)):
         assert (lib.mla_layer_workspace_bytes(ctypes.byref(d.c()), B, L, 0)
                 >= lib.mla_workspace_bytes(ctypes.byref(d.c()), B, L, 0))
+
+
+def test_tiled_4bit_validation(lib):
+    # mla_repack_q4g64 checks before any launch
+    src = _w(mla.MLA_Q4G64, 64, 256, sc=0x10, bi=0x20)
+
+    def repack(w=src, data=0x100, sc=0x200, bi=0x300):
+        return lib.mla_repack_q4g64(ctypes.byref(w) if w else None, data, sc, bi, None)
+    assert repack(w=None) == mla.MLA_ERR_NULL
+    assert repack(data=None) == mla.MLA_ERR_NULL
+    assert repack(bi=None) == mla.MLA_ERR_NULL
+    assert repack(w=_w(mla.MLA_Q4G64, 64, 256)) == mla.MLA_ERR_NULL      # no scales
+    assert repack(w=_w(mla.MLA_BF16, 64, 256, sc=0x10, bi=0x20)) == mla.MLA_ERR_DTYPE
+    assert repack(w=_w(mla.MLA_Q4G64_T, 64, 256, sc=0x10, bi=0x20)) == mla.MLA_ERR_DTYPE
+    assert repack(w=_w(mla.MLA_Q4G64, 48, 256, sc=0x10, bi=0x20)) == mla.MLA_ERR_DIMS   # rows
+    assert repack(w=_w(mla.MLA_Q4G64, 64, 192, sc=0x10, bi=0x20)) == mla.MLA_ERR_DIMS   # cols
+    # a tiled weight is taken where the 4-bit one is, with its own shape rules
+    d = mla.Dims(16, 32, 16, 32, 64, hidden=256, q_lora=0, cache_dtype=mla.MLA_F32)
+    rope = mla.CRope(0x100, 1.0)
+    cache = mla.CCache(0x200, 0x300, 2, 2)
+    norm = _w(mla.MLA_F32, 1, 64)
+
+    def app(dims, kv_a):
+        return lib.mla_cache_append(ctypes.byref(dims.c()), 1, 0x400, ctypes.byref(kv_a),
+                                    ctypes.byref(norm), ctypes.byref(rope), 0x500,
+                                    ctypes.byref(cache), None, 0x900, 1 << 20, None)
+    d3 = mla.Dims(16, 32, 32, 32, 64, hidden=256, q_lora=0, cache_dtype=mla.MLA_F32)  # W = 96
+    assert app(d3, _w(mla.MLA_Q4G64_T, 96, 256)) == mla.MLA_ERR_NULL       # no scales
+    assert app(d, _w(mla.MLA_Q4G64_T, 80, 256, sc=0x10, bi=0x20)) == mla.MLA_ERR_DIMS  # 80 rows
+    d4 = mla.Dims(16, 32, 32, 32, 64, hidden=192, q_lora=0, cache_dtype=mla.MLA_F32)
+    assert app(d4, _w(mla.MLA_Q4G64_T, 96, 192, sc=0x10, bi=0x20)) == mla.MLA_ERR_DIMS  # 192 cols
+    assert app(d, _w(mla.MLA_Q4G64_T, 1, 64, sc=0x10, bi=0x20)) == mla.MLA_ERR_DIMS
