@@ -23,13 +23,18 @@
 //
 // The tile loop is a software pipeline with one barrier per tile: after the
 // barrier that publishes tile i and the P of tile i - 1, one stream of MFMAs
-// runs the scores of tile i with half of the P*V of tile i - 1 between them,
-// then the other half of the P*V with tile i's softmax issued between those
-// MFMAs (it writes tile i's P into one of two P buffers, by tile parity); the
-// copies of tile i + 2 go out into the buffer tile i - 1 has left, the V^T
-// fragments of tile i are read as registers free up, and the wave waits for
-// its copies of tile i + 1 before the next barrier.  Tiles stream HBM -> LDS with 16-byte
+// runs the scores of tile i as one unbroken accumulate chain, then the P*V of
+// tile i - 1 with tile i's softmax cut into slices between those MFMAs (it
+// writes tile i's P into one of two P buffers, by tile parity); the copies of
+// tile i + 2 go out into the buffer tile i - 1 has left, the V^T fragments of
+// tile i are read as registers free up, and the wave waits for its copies of
+// tile i + 1 before the next barrier.  Tiles stream HBM -> LDS with 16-byte
 // direct-to-LDS loads, three buffers deep.
+// With one wave per SIMD nothing else hides a wave's own issue: an MFMA of 32
+// cycles covers about four VALU or LDS instructions issued behind it, more
+// stretch it, and P*V MFMAs placed inside the score chain cost more than
+// their own issue time.  Hence the chain is kept whole and the softmax is
+// spread over the 32 P*V MFMAs, a few instructions after each.
 // The LDS tile is 32 rows x 72 sixteen-byte granules with an XOR swizzle of the
 // granule index inside each aligned group of 8, chosen so that both the
 // row-wise K reads (16 rows, one granule each) and the transpose V reads (4
@@ -103,6 +108,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   int b = blockIdx.y;
   int rows = a.split_rows;  // rows per split
   int slot = b * a.num_splits + split;  // partial slot of this (query, split)
+  int len = -1;                         // this query's rows (the packed plan finds it)
   if (a.num_splits > 1 && a.B > 1 && a.B <= kMaxPacked) {
     // Packed plan: the non-empty (query, split) pairs, query-major, go to the
     // first workgroups in dispatch order, so a ragged batch's work starts at
@@ -211,12 +217,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         scan[4] = q;
         scan[5] = p - excl;
         scan[10] = excl;
+        scan[11] = lens[i];
       }
       carry += scan[0] + scan[1] + scan[2] + scan[3];
       __syncthreads();  // the totals are read before the next chunk rewrites them
     }
     b = scan[4];
     split = scan[5];
+    len = scan[11];
     // a device plan packs the slots by pair; the host plan keeps b * S + split
     slot = a.auto_slots > 0 ? p : b * a.num_splits + split;
     if (a.auto_slots > 0 && split == 0 && tid == 0) a.part_first[b] = scan[10];
@@ -231,8 +239,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int head = wave * 32 + l32;  // this lane's head in the S^T layout
 
-  int len = a.seq_lens[b];
-  len = len < a.max_len ? len : a.max_len;
+  if (len < 0) {
+    len = a.seq_lens[b];
+    len = len < a.max_len ? len : a.max_len;
+  }
+  len = __builtin_amdgcn_readfirstlane(len);
   const int row_begin = split * rows;
   int row_end = row_begin + rows;
   row_end = row_end < len ? row_end : len;
@@ -256,12 +267,62 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     return;
   }
   const int ntiles = (row_end - row_begin + kTile - 1) / kTile;
+  const char* pool = static_cast<const char*>(a.pool);
+  const uint32_t tiles_lds = (uint32_t)(uintptr_t)tiles;
+
+  // Byte offset, inside a tile of 32 consecutive rows, of granule copy k of
+  // this thread: LDS slot p = (k*4 + wave)*64 + lane holds granule
+  // (p % 72) ^ swizzle(row) of row p / 72.  Only this thread reads its entries.
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) {
+    const int p = (k * 4 + wave) * 64 + lane;
+    const int r = p / kGran;
+    const int x = p - r * kGran;
+    const int j = (r >> 1) & 7;
+    goff_lds[k * kThreads + tid] = (uint32_t)(r * (kW * 2) + (x ^ (((j & 1) << 2) | (j >> 1))) * 16);
+  }
+
+  // Physical first row of tile i from the block table; -1 marks a bad table
+  // entry (or a query whose sequence index is out of range).
+  const int sq = a.q_seq ? a.q_seq[b] : b;
+  const bool seq_ok = sq >= 0 && sq < a.num_seqs;
+  const int32_t* trow = a.table + (size_t)(seq_ok ? sq : 0) * a.max_blocks;
+  auto tile_blk = [&](int i) -> int { return seq_ok ? trow[(row_begin + i * kTile) / a.block] : -1; };
+  auto tile_row = [&](int i, int blk) -> int {
+    return blk >= 0 && blk < a.num_blocks ? blk * a.block + ((row_begin + i * kTile) % a.block) : -1;
+  };
+  // Source of tile i: the address of its first row (a bad table entry reads
+  // row 0 and makes the output NaN).  A tile never crosses a block, so all its
+  // 32 rows lie inside the pool even where the split ends first.
+  auto base_src = [&](int raw) -> const char* {
+    const int base = __builtin_amdgcn_readfirstlane(raw);
+    return pool + (size_t)(base < 0 ? 0 : base) * (kW * 2);
+  };
+  // Copy granule k of tile i: 16 bytes per lane straight into LDS at
+  // M0 + 16 * lane.  Issued from asm so that the compiler does not treat every
+  // later LDS read as aliasing the copy; the explicit vmcnt waits order them.
+  auto issue_load = [&](int i, int k, uint32_t off, const char* src) {
+    const uint32_t lds = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes + (k * 4 + wave) * 1024);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(src), "s"(lds)
+                 : "memory");
+  };
+  auto issue_tile_from = [&](int i, const char* src) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) issue_load(i, k, goff_lds[k * kThreads + tid], src);
+  };
+  // The table entries of tiles 0 and 1 are read before the query, and their
+  // copies go out right after the query's loads, so the three latencies
+  // (table, query, first tiles) overlap instead of following each other.
+  const int blk0 = tile_blk(0);
+  const int blk1 = ntiles > 1 ? tile_blk(1) : 0;
+  __builtin_amdgcn_sched_barrier(0);
 
   // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
   // 16*kb + 8*hf .. +7 of the 576.  The first kQReg k-blocks stay in VGPRs;
   // the rope k-blocks go to LDS (the register file holds O, Q and the
-  // pipeline's fragments, and no more).  Issued before the block-table reads
-  // below, so that the two latencies overlap.
+  // pipeline's fragments, and no more).
   bf16x8_t qf[kQReg];
   bf16x8_t qpe[kQLds];
   {
@@ -272,30 +333,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < kQLds; ++j) qpe[j] = *reinterpret_cast<const bf16x8_t*>(q + 16 * (kQReg + j));
   }
+  __builtin_amdgcn_sched_barrier(0);
+  issue_tile_from(0, base_src(tile_row(0, blk0)));
+  issue_tile_from(1, ntiles > 1 ? base_src(tile_row(1, blk1)) : pool);
 
-  // Physical first row of every tile of this split; -1 marks a bad table entry
-  // (or a query whose sequence index is out of range).
-  const int sq = a.q_seq ? a.q_seq[b] : b;
-  const bool seq_ok = sq >= 0 && sq < a.num_seqs;
-  const int32_t* trow = a.table + (size_t)(seq_ok ? sq : 0) * a.max_blocks;
+  // The first row of every tile of this split, for the later copies.
   int bad_tile = 0;
   for (int i = tid; i < ntiles; i += kThreads) {
-    const int t0 = row_begin + i * kTile;
-    const int blk = seq_ok ? trow[t0 / a.block] : -1;
-    const bool ok = blk >= 0 && blk < a.num_blocks;
-    tile_base[i] = ok ? blk * a.block + (t0 % a.block) : -1;
-    bad_tile |= !ok;
-  }
-  // Byte offset, inside a tile of 32 consecutive rows, of granule copy k of
-  // this thread: LDS slot p = (k*4 + wave)*64 + lane holds granule
-  // (p % 72) ^ swizzle(row) of row p / 72.
-#pragma unroll
-  for (int k = 0; k < kLoads; ++k) {
-    const int p = (k * 4 + wave) * 64 + lane;
-    const int r = p / kGran;
-    const int x = p - r * kGran;
-    const int j = (r >> 1) & 7;
-    goff_lds[k * kThreads + tid] = (uint32_t)(r * (kW * 2) + (x ^ (((j & 1) << 2) | (j >> 1))) * 16);
+    const int r = tile_row(i, tile_blk(i));
+    tile_base[i] = r;
+    bad_tile |= r < 0;
   }
 
 #pragma unroll
@@ -312,9 +359,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // any bad table entry in the split makes its outputs NaN
   const bool bad = __syncthreads_or(bad_tile) != 0;
 
-  const char* pool = static_cast<const char*>(a.pool);
-  const uint32_t tiles_lds = (uint32_t)(uintptr_t)tiles;
-
   // Loop-invariant parts of the LDS read addresses (bytes inside a tile); the
   // others follow by XOR (the swizzle touches granule bits 1..2 only):
   //   K rows for k-block kb:   qk0 ^ ((kb & 3) << 5), + (kb >> 2) * 128
@@ -327,31 +371,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   }
   const uint32_t p_row = (uint32_t)(l32 * kPRow + hf * 16);  // + head block * 32 * kPRow
 
-  // Source of tile i: the address of its first row (a bad table entry reads
-  // row 0 and makes the output NaN).  A tile never crosses a block, so all its
-  // 32 rows lie inside the pool even where the split ends first.
-  auto base_src = [&](int raw) -> const char* {
-    const int base = __builtin_amdgcn_readfirstlane(raw);
-    return pool + (size_t)(base < 0 ? 0 : base) * (kW * 2);
-  };
   auto tile_src = [&](int i) -> const char* { return base_src(tile_base[i]); };
-  // Copy granule k of tile i: 16 bytes per lane straight into LDS at
-  // M0 + 16 * lane.  Issued from asm so that the compiler does not treat every
-  // later LDS read as aliasing the copy; the explicit vmcnt waits order them.
-  auto issue_load = [&](int i, int k, uint32_t off, const char* src) {
-    const uint32_t lds = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes + (k * 4 + wave) * 1024);
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(src), "s"(lds)
-                 : "memory");
-  };
   // Tiles past the split's end (the pipeline's look-ahead) re-read the pool's
   // first 32 rows into the buffer they would use.
-  auto issue_tile = [&](int i) {
-    const char* src = i < ntiles ? tile_src(i) : pool;
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) issue_load(i, k, goff_lds[k * kThreads + tid], src);
-  };
+  auto issue_tile = [&](int i) { issue_tile_from(i, i < ntiles ? tile_src(i) : pool); };
   // Rows of tile i past the split's end hold whatever the pool has there
   // (possibly NaN).  They get probability 0, but 0 * NaN would still reach O
   // through P*V, so once this wave's copies of the tile have landed it
@@ -420,10 +443,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 
   // One MFMA phase of the pipeline, after the barrier that published tile
   // `it` and the P of tile it - 1:
-  //   scores of tile it: S^T = K Q^T, 36 MFMAs in one accumulator chain;
-  //   P*V of tile it - 1 (kMode > 0): O^T += V^T P^T, 32 MFMAs; 16 of them
-  //     one after every second score MFMA, the other 16 after the score chain
-  //     has ended, with the softmax of tile it issued between them (its VALU
+  //   scores of tile it: S^T = K Q^T, 36 MFMAs in one accumulator chain with
+  //     nothing else between its links but their K reads (two ahead), the
+  //     copies and the rope-query reads;
+  //   P*V of tile it - 1 (kMode > 0): O^T += V^T P^T, 32 MFMAs after the
+  //     chain, with the softmax of tile it in slices between them (its VALU
   //     work runs while they execute); head block outer, so one P fragment
   //     serves four MFMAs in a row;
   //   the nine copies of tile it + 2 into the buffer tile it - 1 has left;
@@ -500,7 +524,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       if (n + 2 < kW / 16) kf[n % 2] = *kaddr(qa, n + 2);
       if (n >= 24 && n < 24 + 2 * kQLds && (n & 1) == 0) qp[(n - 24) >> 1] = qsrc[((n - 24) >> 1) * 64];
       if (kMode == 0 && n < 32) pv_step(n);  // the V^T reads only
-      if (kMode > 0 && (n & 1) && n < 32) pv_step(n >> 1);
       if ((n & 3) == 3) {  // copy n / 4 of tile it + 2; the next copy's offset
         const int k = n >> 2;
         const uint32_t off = noff;
@@ -516,9 +539,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       src2 = it + 3 < ntiles ? base_src(raw3) : pool;
       return s;
     } else {
-      // softmax() of tile it in slices between the last 16 P*V steps (the
+      // softmax() of tile it in slices between the 32 P*V steps (the
       // reference max is fixed after a (re)start's first tile, so it is read
-      // here, never raised).  u = s * scale * log2e - m_ref is the exponent of
+      // here, never raised); the maxima use v_max3 directly (fmaxf would add a
+      // canonicalising max per input, and v_max3 drops a quiet NaN the same way).  u = s * scale * log2e - m_ref is the exponent of
       // every numerator; rows past the split's end get u = -inf (numerator 0,
       // no part in the maximum).  The tile's largest u only feeds the restart
       // vote and the reference of a restart.
@@ -528,52 +552,81 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       float u[16];
       float p[16];
       bf16x8_t pb[2];
+      float q01 = 0.f, q23 = 0.f, q45 = 0.f, q67 = 0.f;
+      float mx[5];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        pv_step(16 + t);
-        if (t == 0) {
-          asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
+      for (int t = 0; t < 32; ++t) {
+        pv_step(t);
+        // Each slice is pinned to its step: its inputs pass through an empty
+        // asm at the step's start and its results at the step's end, so no
+        // pass can gather the slices into one long VALU run between two MFMAs.
+        if (t == 1) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
+        if (t >= 2 && t < 6) {
+          asm volatile("" : "+v"(s));
 #pragma unroll
-          for (int j = 0; j < 8; ++j) u[j] = fmaf(s[j], c, -m_ref);
-        }
-        if (t == 1) {
-#pragma unroll
-          for (int j = 8; j < 16; ++j) u[j] = fmaf(s[j], c, -m_ref);
-          if (tail) {
-            int l = lim - 4 * hf;
-            asm volatile("" : "+v"(l));
-#pragma unroll
-            for (int j = 0; j < 16; ++j) u[j] = (j >> 2) * 8 + (j & 3) < l ? u[j] : -INFINITY;
+          for (int j = 4 * (t - 2); j < 4 * (t - 2) + 4; ++j) {
+            u[j] = fmaf(s[j], c, -m_ref);
+            asm volatile("" : "+v"(u[j]));
           }
         }
-        if (t == 2) {
-          e = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(u[4], u[5]), fmaxf(u[6], u[7])));
-          e = fmaxf(e, fmaxf(fmaxf(fmaxf(u[8], u[9]), fmaxf(u[10], u[11])),
-                             fmaxf(fmaxf(u[12], u[13]), fmaxf(u[14], u[15]))));
+        if (t == 5 && tail) {
+          int l = lim - 4 * hf;
+          asm volatile("" : "+v"(l));
+#pragma unroll
+          for (int j = 0; j < 16; ++j) u[j] = (j >> 2) * 8 + (j & 3) < l ? u[j] : -INFINITY;
         }
-        if (t == 3) {
+        if (t == 6) {
+          asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx[0]) : "v"(u[0]), "v"(u[1]), "v"(u[2]));
+          asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx[1]) : "v"(u[3]), "v"(u[4]), "v"(u[5]));
+          asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx[2]) : "v"(u[6]), "v"(u[7]), "v"(u[8]));
+        }
+        if (t == 7) {
+          asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx[3]) : "v"(u[9]), "v"(u[10]), "v"(u[11]));
+          asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx[4]) : "v"(u[12]), "v"(u[13]), "v"(u[14]));
+          asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx[0]) : "v"(mx[0]), "v"(mx[1]), "v"(u[15]));
+        }
+        if (t == 8) {
+          asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(e) : "v"(mx[2]), "v"(mx[3]), "v"(mx[4]));
+          asm volatile("v_max_f32 %0, %1, %2" : "=v"(e) : "v"(e), "v"(mx[0]));
+        }
+        if (t == 9) {
           float lo, hi;
           wave_halves(e, &lo, &hi);
-          e = fmaxf(lo, hi);
+          asm volatile("v_max_f32 %0, %1, %2" : "=v"(e) : "v"(lo), "v"(hi));
           vote = __builtin_amdgcn_readfirstlane((int)vv);
           keep = keep && vote == 0;
           if (keep) m_seen = fmaxf(m_seen, e + m_ref);
+          asm volatile("" : "+v"(m_seen), "+v"(e));
         }
-        if (t >= 4 && t < 12) {
-          const int j = 2 * (t - 4);
-          p[j] = __builtin_amdgcn_exp2f(u[j]);
-          p[j + 1] = __builtin_amdgcn_exp2f(u[j + 1]);
-        }
-        if (t == 12) {
+        if (t >= 10 && t < 18) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)p[j];
+          for (int j = 2 * (t - 10); j < 2 * (t - 10) + 2; ++j) {
+            asm volatile("" : "+v"(u[j]));
+            p[j] = __builtin_amdgcn_exp2f(u[j]);
+            asm volatile("" : "+v"(p[j]));
+          }
         }
-        if (t == 13) {
-          const float q0 = (p[0] + p[1]) + (p[2] + p[3]), q1 = (p[4] + p[5]) + (p[6] + p[7]);
-          const float q2 = (p[8] + p[9]) + (p[10] + p[11]), q3 = (p[12] + p[13]) + (p[14] + p[15]);
-          if (keep) l_run += (q0 + q1) + (q2 + q3);
+        if (t == 18 || t == 19) {
+          const int h0 = 8 * (t - 18);
+#pragma unroll
+          for (int j = h0; j < h0 + 8; ++j) pb[t - 18][j - h0] = (__bf16)p[j];
+          asm volatile("" : "+v"(pb[t - 18]));
         }
-        if (t == 14) {
+        if (t == 20) {
+          q01 = (p[0] + p[1]) + (p[2] + p[3]);
+          q23 = (p[4] + p[5]) + (p[6] + p[7]);
+          asm volatile("" : "+v"(q01), "+v"(q23));
+        }
+        if (t == 21) {
+          q45 = (p[8] + p[9]) + (p[10] + p[11]);
+          q67 = (p[12] + p[13]) + (p[14] + p[15]);
+          asm volatile("" : "+v"(q45), "+v"(q67));
+        }
+        if (t == 22) {
+          if (keep) l_run += (q01 + q23) + (q45 + q67);
+          asm volatile("" : "+v"(l_run));
+        }
+        if (t == 23) {
           MLA_LDS char* prow = p_lds + p_row + (uint32_t)((it & 1) * kPBuf) + wave * (32 * kPRow);
           *(MLA_LDS bf16x8_t*)prow = pb[0];
           *(MLA_LDS bf16x8_t*)(prow + 32) = pb[1];
@@ -668,8 +721,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
           "=a"(o[6]), "=a"(o[7]), "=a"(o[8]), "=a"(o[9]), "=a"(o[10]), "=a"(o[11]),
           "=a"(o[12]), "=a"(o[13]), "=a"(o[14]), "=a"(o[15])
         : "v"(zf));
-    issue_tile(0);
-    issue_tile(1);
+    if (restarts > 0) {  // the first pass's copies went out in the prologue
+      issue_tile(0);
+      issue_tile(1);
+    }
     src2 = 2 < ntiles ? tile_src(2) : pool;
     asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 (tile 1's copies are newer)
     zero_tail(0);
