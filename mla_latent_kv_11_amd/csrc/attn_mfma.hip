@@ -454,12 +454,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   //   the V^T fragments of tile it, each read as soon as the P*V MFMAs of
   //     tile it - 1 are done with its registers.
   // kMode 0: no P*V (the first tile of a (re)start); returns the scores for
-  // softmax().  kMode 2: with the P*V and tile it's softmax; `keep` is false
-  // for the look-ahead tile past the split's end and when a restart was voted,
-  // and then the numerators are formed but no state is updated; `pend` gets
-  // softmax()'s result.  Tiles past the split's end are read and scored like
-  // any other (their copies re-read the pool's first rows into the free
-  // buffer), so the sequence has no branch.
+  // softmax().  kMode 2: with the P*V and tile it's softmax; when a restart
+  // was voted the numerators are formed but no state is updated; `pend` gets
+  // softmax()'s result.  kMode 1: the phase after the split's last tile, its
+  // P*V alone and the vote it acts on.  The copies always look two tiles
+  // ahead, past the split's end too (they re-read the pool's first rows into
+  // the free buffer), so every phase but the last issues the same nine.
   auto mfma_phase = [&](auto mode, int it, bool keep, bool& pend, int& vote) -> f32x16_t {
     constexpr int kMode = decltype(mode)::value;
     const uint32_t tile = tiles_lds + (uint32_t)((it % kBufs) * kTileBytes);
@@ -473,7 +473,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     uint32_t vv = 0;
     if (kMode > 0) vv = votes[(it - 1) & 1];
     uint32_t qa[4];
-    kbases(tile, qa);
+    if constexpr (kMode != 1) kbases(tile, qa);
     uint32_t va[4];
 #pragma unroll
     for (int c1 = 0; c1 < 2; ++c1)
@@ -486,8 +486,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       return *(const MLA_LDS bf16x8_t*)(p_lds + pbuf + x * (32 * kPRow) + kb * 32);
     };
     bf16x8_t kf[2];
+    if constexpr (kMode != 1) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) kf[kb] = *kaddr(qa, kb);
+      for (int kb = 0; kb < 2; ++kb) kf[kb] = *kaddr(qa, kb);
+    }
     bf16x8_t pf[2];  // P fragments (k-block, head block) in MFMA order, two in flight
     if (kMode > 0) {
       pf[0] = pread(0, 0);
@@ -504,16 +506,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       }
       // the P fragment two steps on replaces the one just finished
       if (kMode > 0 && cbl == 3 && m + 8 < 32) pf[f] = pread(((m >> 2) + 2) & 3, (m + 8) >> 4);
-      if (hb == 3) vf[kb][cbl] = vread(va, cbl, kb);
+      if (kMode != 1 && hb == 3) vf[kb][cbl] = vread(va, cbl, kb);
     };
-    uint32_t noff = goff_lds[tid];
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8_t qp[kQLds];  // the LDS-resident query k-blocks, read in the phase's last quarter
-    const MLA_LDS bf16x8_t* qsrc = qpe_lds + wave * (kQLds * 64) + lane;
     // The score MFMAs are asm too (an exact-register accumulate chain needs
     // no wait states between its links), which keeps the compiler from moving
     // the resident query between registers around the P*V asm.
-    f32x16_t s;
+    f32x16_t s = f32x16_t{};
+    if constexpr (kMode != 1) {
+    uint32_t noff = goff_lds[tid];
+    bf16x8_t qp[kQLds];  // the LDS-resident query k-blocks, read in the phase's last quarter
+    const MLA_LDS bf16x8_t* qsrc = qpe_lds + wave * (kQLds * 64) + lane;
 #pragma unroll
     for (int n = 0; n < kW / 16; ++n) {
       const bf16x8_t qn = n < kQReg ? qf[n < kQReg ? n : 0] : qp[n < kQReg ? 0 : n - kQReg];
@@ -531,6 +534,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
         issue_load(it + 2, k, off, nsrc);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
     if constexpr (kMode == 0) {
       // VALU reads of an MFMA result wait 18 cycles after a 16-pass MFMA; the
@@ -557,6 +561,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 32; ++t) {
         pv_step(t);
+        if constexpr (kMode == 1) {  // no tile of its own: only the vote it acts on
+          if (t == 0) vote = __builtin_amdgcn_readfirstlane((int)vv);
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
         // Each slice is pinned to its step: its inputs pass through an empty
         // asm at the step's start and its results at the step's end, so no
         // pass can gather the slices into one long VALU run between two MFMAs.
@@ -734,19 +743,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     f32x16_t s = mfma_phase(std::integral_constant<int, 0>{}, 0, true, pending, vote);
     pending = softmax(s, 0);
     bool restart = false;
-    for (int it = 1;; ++it) {
-      // the ballot runs in every lane (inside the branch it would see lane 0 only)
+    // the restart vote of tile it - 1 (a byte per wave, by parity; the ballot
+    // runs in every lane: inside the branch it would see lane 0 only)
+    auto publish_vote = [&](int it) {
       const bool wave_vote = __ballot(pending) != 0;
       if (lane == 0) ((MLA_LDS uint8_t*)(votes + ((it - 1) & 1)))[wave] = wave_vote ? 1 : 0;
+    };
+    for (int it = 1; it < ntiles; ++it) {
+      publish_vote(it);
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's copies of tile it
       zero_tail(it);
       __syncthreads();
-      mfma_phase(std::integral_constant<int, 2>{}, it, it < ntiles, pending, vote);
+      mfma_phase(std::integral_constant<int, 2>{}, it, true, pending, vote);
       if (vote != 0) {
         restart = true;
         break;
       }
-      if (it == ntiles) break;
+    }
+    if (!restart) {  // past the last tile: its P*V alone (no copy of this tile is read)
+      publish_vote(ntiles);
+      __syncthreads();
+      mfma_phase(std::integral_constant<int, 1>{}, ntiles, false, pending, vote);
+      restart = vote != 0;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!restart) break;
