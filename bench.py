@@ -4,8 +4,9 @@
 A step is one pass of the whole decode path over one batch: kv_a projection +
 latent RMSNorm + YaRN RoPE + paged append, the q chain + absorb, decode
 attention over the paged latent cache, the W_UV expansion and o_proj.  The
-step is one mla_decode_layer call (9 kernels on one stream), replayed as one
-HIP graph (``--eager``: the call launched every step); the same step as the
+step is one mla_decode_layer call (9 kernels on one stream), replayed from HIP
+graphs that hold up to 10 steps each, as a multi-layer model's graph holds one
+step per layer (``--eager``: the call launched every step); the same step as the
 four separate calls (append and absorb on two streams, one graph) is timed
 beside it.  The attention call is then timed where the step runs it (HIP events
 around decode_attn inside eager steps of the four calls, between
@@ -392,29 +393,32 @@ def main():
     B = case.batch
     rows = int(case.lens.sum())
     # One step = one mla_decode_layer call (the fused front, attention with its
-    # merge, W_UV and o_proj: 9 kernels on one stream), replayed as one HIP
-    # graph (--eager: the call launched every step).
+    # merge, W_UV and o_proj: 9 kernels on one stream), replayed from HIP graphs
+    # of step_graph steps (--eager: the call launched every step).
     def timed_steps(step):
-        for _ in range(args.warmup):
+        g = getattr(step, "per_graph", 1)  # steps per run
+        for _ in range(max(1, args.warmup // g)):
             step.run(eager=True)
         torch.cuda.synchronize()
         if not args.eager:
             step.capture()
-            for _ in range(args.warmup):
+            for _ in range(max(1, args.warmup // g)):
                 step.run()
         torch.cuda.synchronize()
-        settled = settle(lambda: step.run(eager=args.eager), torch)
+        settle_ms_, runs = settle(lambda: step.run(eager=args.eager), torch)
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(args.steps // g):
             step.run(eager=args.eager)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / args.steps, settled
+        return (time.perf_counter() - t0) * 1e3 / args.steps, (settle_ms_, runs * g)
 
-    ms_step, (settle_ms, settle_steps) = timed_steps(D.LayerStep(case, ns))
+    # Steps per graph: the largest of 10, 5, 4, 2, 1 that divides --steps.
+    step_graph = next(g for g in (10, 5, 4, 2, 1) if args.steps % g == 0)
+    ms_step, (settle_ms, settle_steps) = timed_steps(D.LayerStep(case, ns, per_graph=step_graph))
     assert int(ns.status.cpu()[0]) == 0
     ms_step_rm = None
     if ns is not ns_rm:
-        ms_step_rm, _ = timed_steps(D.LayerStep(case, ns_rm))
+        ms_step_rm, _ = timed_steps(D.LayerStep(case, ns_rm, per_graph=step_graph))
     # The same step as the four calls: cache_append and absorb_q on two streams
     # (independent), then decode_attn, then out_proj, replayed as one HIP graph
     # (--eager: launched one by one on one stream).
@@ -485,8 +489,8 @@ def main():
                         "kv_lora 512 + rope 64, hidden 7168, q_lora 1536, 4-bit g64 projections, "
                         "bf16 paged cache (64-row blocks)",
             "launch": "one mla_decode_layer call per step, eager" if args.eager else
-                      "one HIP graph per step holding one mla_decode_layer call (9 kernels, "
-                      "one stream)",
+                      f"HIP graphs of {step_graph} steps, each step one mla_decode_layer call "
+                      "(9 kernels, one stream)",
             "weights": "4-bit g64 as given (row-major)" if ns is ns_rm else
                        "4-bit g64 repacked once before timing into the tiled layout "
                        "(mla_repack_q4g64, MLA_Q4G64_T; same values, same results)",

@@ -219,11 +219,14 @@ class GraphStep:
 
 
 class LayerStep:
-    """One decode step as one decode_layer call (on the 4-bit layer: 9 kernels
-    on one stream), replayable as one HIP graph.  Library calls only."""
+    """Decode steps as decode_layer calls (on the 4-bit layer: 9 kernels on one
+    stream each), ``per_graph`` of them per run: one HIP graph holds that many
+    steps, as a multi-layer model's graph holds one step per layer, so the
+    gap between graph launches is paid once per run.  Library calls only."""
 
-    def __init__(self, case: Case, ns, split_rows: int = 0):
+    def __init__(self, case: Case, ns, split_rows: int = 0, per_graph: int = 1):
         self.case, self.ns, self.split_rows = case, ns, split_rows
+        self.per_graph = per_graph
         self.ws = layer_workspace(ns, split_rows)
         self.graph = None
 
@@ -231,15 +234,18 @@ class LayerStep:
         run_layer(self.case, self.ns, self.split_rows, self.ws)
 
     def capture(self):
-        """Record the call (run it eagerly at least once before)."""
+        """Record per_graph calls (run the call eagerly at least once before)."""
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
-            self.call()
+            for _ in range(self.per_graph):
+                self.call()
         torch.cuda.synchronize()
 
     def run(self, eager=False):
+        """per_graph steps."""
         if eager:
-            self.call()
+            for _ in range(self.per_graph):
+                self.call()
         else:
             self.graph.replay()
