@@ -312,50 +312,88 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) issue_load(i, k, goff_lds[k * kThreads + tid], src);
   };
-  // The table entries of tiles 0 and 1 are read before the query, and their
-  // copies go out right after the query's loads, so the three latencies
-  // (table, query, first tiles) overlap instead of following each other.
+  // Block-table entries first: tiles 0 and 1, and this thread's share of
+  // every tile's (consumed after the query, so their latency hides under it).
   const int blk0 = tile_blk(0);
   const int blk1 = ntiles > 1 ? tile_blk(1) : 0;
+  int tblk[kMaxSplitTiles / kThreads];
+#pragma unroll
+  for (int j = 0; j < kMaxSplitTiles / kThreads; ++j) {
+    const int i = tid + j * kThreads;
+    tblk[j] = i < ntiles ? tile_blk(i) : 0;
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
   // 16*kb + 8*hf .. +7 of the 576.  The first kQReg k-blocks stay in VGPRs;
   // the rope k-blocks go to LDS (the register file holds O, Q and the
-  // pipeline's fragments, and no more).
+  // pipeline's fragments, and no more).  Loaded straight into that layout, a
+  // load instruction would touch 32 rows, 32 bytes from each, and the wave's
+  // 36 of them take thousands of cycles to issue; instead the rows (36 KB per
+  // wave, contiguous) come through the still idle tile buffers in four rounds
+  // of 9 k-blocks: round r's copies (9 per lane, each 1 KB of 3-4 rows) put
+  // head h's bytes 288 r .. +287 at granule 18 h + g of the wave's slots
+  // (granule G = 64 k + lane of copy k), and each lane reads its 9
+  // fragments back (two-way bank conflicts at most).  Rounds 0-2 go out
+  // together into buffers 0-2; once rounds 0 and 1 are read, tiles 0 and 1's
+  // copies take those buffers and round 3 follows round 2 in buffer 2.
+  const char* qrow = static_cast<const char*>(a.q_abs) + ((size_t)b * kH + wave * 32) * (kW * 2);
+  uint32_t qoff[9], qrd[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int G = 64 * k + lane;
+    qoff[k] = (uint32_t)((G / 18) * (kW * 2) + (G % 18) * 16);
+    const int R = 18 * l32 + 2 * k + hf;  // this lane's fragment k of a round
+    qrd[k] = (uint32_t)((((R >> 6) * 4 + wave) * 1024) + (R & 63) * 16);
+  }
+  auto q_round = [&](int r, int buf) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) issue_load(buf, k, qoff[k], qrow + 288 * r);
+  };
+  auto q_read = [&](int buf, int k) {
+    return *(const MLA_LDS bf16x8_t*)(tiles + buf * kTileBytes + qrd[k]);
+  };
+  q_round(0, 0);
+  q_round(1, 1);
+  q_round(2, 2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table entries too (issued first)
   bf16x8_t qf[kQReg];
   bf16x8_t qpe[kQLds];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q_abs) + ((size_t)b * kH + head) * kW + 8 * hf;
 #pragma unroll
-    for (int kb = 0; kb < kQReg; ++kb)
-      qf[kb] = *reinterpret_cast<const bf16x8_t*>(q + 16 * kb);
+  for (int k = 0; k < 9; ++k) qf[k] = q_read(0, k);
 #pragma unroll
-    for (int j = 0; j < kQLds; ++j) qpe[j] = *reinterpret_cast<const bf16x8_t*>(q + 16 * (kQReg + j));
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  for (int k = 0; k < 9; ++k) qf[9 + k] = q_read(1, k);
+  // this wave's reads of buffers 0 and 1 are done before its copies land there;
+  // the other waves' reads of their own slots need no wait (copy slot k*4 + wave)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   issue_tile_from(0, base_src(tile_row(0, blk0)));
   issue_tile_from(1, ntiles > 1 ? base_src(tile_row(1, blk1)) : pool);
+#pragma unroll
+  for (int k = 0; k < 9; ++k) qf[18 + k] = q_read(2, k);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  q_round(3, 2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // round 3 (and the first tiles' copies)
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const bf16x8_t v = q_read(2, k);
+    if (27 + k < kQReg) qf[27 + k < kQReg ? 27 + k : 0] = v;
+    else qpe[27 + k - kQReg < kQLds ? 27 + k - kQReg : 0] = v;
+  }
+  static_assert(kQReg == 32 && kQLds == 4, "four rounds of 9 k-blocks cover the 576 columns");
 
   // The first row of every tile of this split, for the later copies.
   int bad_tile = 0;
-  for (int i = tid; i < ntiles; i += kThreads) {
-    const int r = tile_row(i, tile_blk(i));
-    tile_base[i] = r;
-    bad_tile |= r < 0;
+#pragma unroll
+  for (int j = 0; j < kMaxSplitTiles / kThreads; ++j) {
+    const int i = tid + j * kThreads;
+    if (i < ntiles) {
+      const int r = tile_row(i, tblk[j]);
+      tile_base[i] = r;
+      bad_tile |= r < 0;
+    }
   }
-
 #pragma unroll
   for (int j = 0; j < kQLds; ++j) qpe_lds[(wave * kQLds + j) * 64 + lane] = qpe[j];
-  // Consume the Q loads here, so that the only vector-memory operations in
-  // flight inside the tile loop are the tile copies counted by hand below.
-  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
-               "v"(qf[6]), "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]),
-               "v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]));
-  asm volatile("" ::"v"(qf[16]), "v"(qf[17]), "v"(qf[18]), "v"(qf[19]), "v"(qf[20]), "v"(qf[21]),
-               "v"(qf[22]), "v"(qf[23]), "v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]),
-               "v"(qf[28]), "v"(qf[29]), "v"(qf[30]), "v"(qf[31]));
-  static_assert(kQReg == 32, "the asm above names every register-resident k-block");
   // any bad table entry in the split makes its outputs NaN
   const bool bad = __syncthreads_or(bad_tile) != 0;
 
