@@ -118,11 +118,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     // ceil(len_b / rows) non-empty splits; an exclusive scan over the queries
     // finds this workgroup's pair, whose index is also its partial slot.
     const int w = blockIdx.y * gridDim.x + blockIdx.x;
-    MLA_LDS int* scan = (MLA_LDS int*)p_lds;  // [4] wave totals, [2] the pair; free until the loop
-    const int nchunks = (a.B + kThreads - 1) / kThreads;
-    int lens[kMaxPacked / kThreads];  // all lengths read up front: one latency, not one per chunk
+    // [4] wave totals, the pair, block sums: the tile table's area, free
+    // until the end of the prologue (the query's copies use the P area)
+    MLA_LDS int* scan = tile_base;
+    const int nchunks = (a.B + kThreads - 1) / kThreads;  // uniform
+    // All lengths read up front (one latency, not one per chunk).  Only the
+    // chunks that hold queries are loaded and divided: the loops below leave
+    // at the first empty chunk by a uniform branch, since every chunk costs
+    // a few divisions per thread and the plan runs before any copy goes out.
+    int lens[kMaxPacked / kThreads];
+#pragma unroll
+    for (int i = 0; i < kMaxPacked / kThreads; ++i) lens[i] = 0;
 #pragma unroll
     for (int i = 0; i < kMaxPacked / kThreads; ++i) {
+      if (i >= nchunks) break;
       const int q = i * kThreads + tid;
       const int lq = q < a.B ? a.seq_lens[q] : 0;
       lens[i] = lq < a.max_len ? lq : a.max_len;
@@ -130,8 +139,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     auto pairs_of = [&](int r) -> int {  // this thread's non-empty splits at r rows
       int n = 0;
 #pragma unroll
-      for (int i = 0; i < kMaxPacked / kThreads; ++i)
-        n += (i < nchunks && lens[i] > 0) ? (lens[i] + r - 1) / r : 0;
+      for (int i = 0; i < kMaxPacked / kThreads; ++i) {
+        if (i >= nchunks) break;
+        n += lens[i] > 0 ? (lens[i] + r - 1) / r : 0;
+      }
       return n;
     };
     // block-wide sum; each call k uses its own LDS slots, so no barrier is
@@ -155,7 +166,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     float tot = 0.f;
     if (a.auto_slots > 0) {
 #pragma unroll
-      for (int i = 0; i < kMaxPacked / kThreads; ++i) tot += i < nchunks ? (float)lens[i] : 0.f;
+      for (int i = 0; i < kMaxPacked / kThreads; ++i) {
+        if (i >= nchunks) break;
+        tot += (float)lens[i];
+      }
     }
     // the host plan's number of non-empty splits (and the total rows)
     int total = block_sum(tot, pairs_of(rows), &tot);
@@ -188,7 +202,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     if (a.auto_slots > 0 && w == 0 && tid == 0) a.part_first[a.B] = rows;  // for the merge
     int cnts[kMaxPacked / kThreads];
 #pragma unroll
-    for (int i = 0; i < kMaxPacked / kThreads; ++i) cnts[i] = lens[i] > 0 ? (lens[i] + rows - 1) / rows : 0;
+    for (int i = 0; i < kMaxPacked / kThreads; ++i) cnts[i] = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPacked / kThreads; ++i) {
+      if (i >= nchunks) break;
+      cnts[i] = lens[i] > 0 ? (lens[i] + rows - 1) / rows : 0;
+    }
     // Workgroups go to the XCDs round robin (w % 8 on this chip).  The
     // workgroups w < total take the pairs: XCD x's n_x = ceil((total - x) / 8)
     // of them take one contiguous run of pairs, so the splits of a query share
@@ -272,19 +291,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 
   // Byte offset, inside a tile of 32 consecutive rows, of granule copy k of
   // this thread: LDS slot p = (k*4 + wave)*64 + lane holds granule
-  // (p % 72) ^ swizzle(row) of row p / 72.  Only this thread reads its entries.
+  // (p % 72) ^ swizzle(row) of row p / 72.  In registers for the first two
+  // tiles' copies; in LDS (read by this thread only) for the later ones.
+  uint32_t goff[kLoads];
 #pragma unroll
   for (int k = 0; k < kLoads; ++k) {
     const int p = (k * 4 + wave) * 64 + lane;
     const int r = p / kGran;
     const int x = p - r * kGran;
     const int j = (r >> 1) & 7;
-    goff_lds[k * kThreads + tid] = (uint32_t)(r * (kW * 2) + (x ^ (((j & 1) << 2) | (j >> 1))) * 16);
+    goff[k] = (uint32_t)(r * (kW * 2) + (x ^ (((j & 1) << 2) | (j >> 1))) * 16);
   }
 
   // Physical first row of tile i from the block table; -1 marks a bad table
   // entry (or a query whose sequence index is out of range).
-  const int sq = a.q_seq ? a.q_seq[b] : b;
+  const int sq = __builtin_amdgcn_readfirstlane(a.q_seq ? a.q_seq[b] : b);  // uniform
   const bool seq_ok = sq >= 0 && sq < a.num_seqs;
   const int32_t* trow = a.table + (size_t)(seq_ok ? sq : 0) * a.max_blocks;
   auto tile_blk = [&](int i) -> int { return seq_ok ? trow[(row_begin + i * kTile) / a.block] : -1; };
@@ -298,31 +319,41 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     const int base = __builtin_amdgcn_readfirstlane(raw);
     return pool + (size_t)(base < 0 ? 0 : base) * (kW * 2);
   };
-  // Copy granule k of tile i: 16 bytes per lane straight into LDS at
-  // M0 + 16 * lane.  Issued from asm so that the compiler does not treat every
-  // later LDS read as aliasing the copy; the explicit vmcnt waits order them.
-  auto issue_load = [&](int i, int k, uint32_t off, const char* src) {
-    const uint32_t lds = tiles_lds + (uint32_t)((i % kBufs) * kTileBytes + (k * 4 + wave) * 1024);
+  // Copy k of this wave into a 36 KB LDS area: 16 bytes per lane straight
+  // into the area's 1 KB slot k*4 + wave, at M0 + 16 * lane.  Issued from asm
+  // so that the compiler does not treat every later LDS read as aliasing the
+  // copy; the explicit vmcnt waits order them.
+  auto copy_to = [&](uint32_t area, int k, uint32_t off, const char* src) {
+    const uint32_t lds = area + (uint32_t)((k * 4 + wave) * 1024);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(off), "s"(src), "s"(lds)
                  : "memory");
   };
+  auto issue_load = [&](int i, int k, uint32_t off, const char* src) {
+    copy_to(tiles_lds + (uint32_t)((i % kBufs) * kTileBytes), k, off, src);
+  };
   auto issue_tile_from = [&](int i, const char* src) {
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) issue_load(i, k, goff_lds[k * kThreads + tid], src);
   };
-  // Block-table entries first: tiles 0 and 1, and this thread's share of
-  // every tile's (consumed after the query, so their latency hides under it).
-  const int blk0 = tile_blk(0);
-  const int blk1 = ntiles > 1 ? tile_blk(1) : 0;
+  // Table entries of tiles 0 and 1 as scalar loads: they are waited for with
+  // lgkmcnt, so their wait does not also wait for the query's copies issued
+  // after them (vector loads complete in order).
+  // No branch around them (a branch would make the compiler wait at its
+  // end): a load that is not needed reads a valid word instead (tile 0's
+  // entry for a missing tile 1, a length for a query without a sequence).
+  typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+  const int32_t* e0 = seq_ok ? trow + row_begin / a.block : a.seq_lens;
+  const int32_t* e1 = seq_ok && ntiles > 1 ? trow + (row_begin + kTile) / a.block : e0;
+  const int blk0_raw = *(const_i32p)e0, blk1_raw = *(const_i32p)e1;
+  // this thread's share of every tile's entry (consumed at the prologue's end)
   int tblk[kMaxSplitTiles / kThreads];
 #pragma unroll
   for (int j = 0; j < kMaxSplitTiles / kThreads; ++j) {
     const int i = tid + j * kThreads;
     tblk[j] = i < ntiles ? tile_blk(i) : 0;
   }
-  __builtin_amdgcn_sched_barrier(0);
 
   // The wave's 32 query rows as MFMA B operands: lane -> head l32, columns
   // 16*kb + 8*hf .. +7 of the 576.  The first kQReg k-blocks stay in VGPRs;
@@ -330,13 +361,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   // pipeline's fragments, and no more).  Loaded straight into that layout, a
   // load instruction would touch 32 rows, 32 bytes from each, and the wave's
   // 36 of them take thousands of cycles to issue; instead the rows (36 KB per
-  // wave, contiguous) come through the still idle tile buffers in four rounds
-  // of 9 k-blocks: round r's copies (9 per lane, each 1 KB of 3-4 rows) put
-  // head h's bytes 288 r .. +287 at granule 18 h + g of the wave's slots
-  // (granule G = 64 k + lane of copy k), and each lane reads its 9
-  // fragments back (two-way bank conflicts at most).  Rounds 0-2 go out
-  // together into buffers 0-2; once rounds 0 and 1 are read, tiles 0 and 1's
-  // copies take those buffers and round 3 follows round 2 in buffer 2.
+  // wave, contiguous) come through LDS in four rounds of 9 k-blocks: round
+  // r's copies (9 per lane, each 1 KB of 3-4 rows) put head h's bytes
+  // 288 r .. +287 at granule 18 h + g of the wave's slots (granule
+  // G = 64 k + lane of copy k), and each lane reads its 9 fragments back
+  // (two-way bank conflicts at most).  Rounds go through tile buffer 2 and
+  // the 36 KB from the P buffers on (P, copy offsets, rope query: written
+  // only after the barrier below), so tiles 0 and 1 take buffers 0 and 1 at
+  // once: their copies go out as soon as their table entries are in, and the
+  // query's rounds arrive meanwhile.  Each wave reads only its own slots.
+  const uint32_t qarea[2] = {tiles_lds + 2u * kTileBytes, (uint32_t)(uintptr_t)p_lds};
+  static_assert(2 * kPBuf + kLoads * kThreads * 4 + kQLds * kThreads * 16 >= kTileBytes,
+                "the P, offset and rope-query areas hold one round of the query");
   const char* qrow = static_cast<const char*>(a.q_abs) + ((size_t)b * kH + wave * 32) * (kW * 2);
   uint32_t qoff[9], qrd[9];
 #pragma unroll
@@ -346,40 +382,49 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     const int R = 18 * l32 + 2 * k + hf;  // this lane's fragment k of a round
     qrd[k] = (uint32_t)((((R >> 6) * 4 + wave) * 1024) + (R & 63) * 16);
   }
-  auto q_round = [&](int r, int buf) {
+  auto q_round = [&](int r, int area) {
 #pragma unroll
-    for (int k = 0; k < 9; ++k) issue_load(buf, k, qoff[k], qrow + 288 * r);
+    for (int k = 0; k < 9; ++k) copy_to(qarea[area], k, qoff[k], qrow + 288 * r);
   };
-  auto q_read = [&](int buf, int k) {
-    return *(const MLA_LDS bf16x8_t*)(tiles + buf * kTileBytes + qrd[k]);
+  auto q_read = [&](int area, int k) {
+    return *(const MLA_LDS bf16x8_t*)(uintptr_t)(qarea[area] + qrd[k]);
   };
   q_round(0, 0);
   q_round(1, 1);
-  q_round(2, 2);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table entries too (issued first)
+  // the table entries are used (and waited for) only once the rounds are out
+  __builtin_amdgcn_sched_barrier(0);
+  const char* src0 = base_src(tile_row(0, seq_ok ? blk0_raw : -1));
+  const char* src1 = ntiles > 1 ? base_src(tile_row(1, seq_ok ? blk1_raw : -1)) : pool;
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) issue_load(0, k, goff[k], src0);
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) issue_load(1, k, goff[k], src1);
+  asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // rounds 0 and 1, the table entries (older)
   bf16x8_t qf[kQReg];
   bf16x8_t qpe[kQLds];
 #pragma unroll
   for (int k = 0; k < 9; ++k) qf[k] = q_read(0, k);
 #pragma unroll
   for (int k = 0; k < 9; ++k) qf[9 + k] = q_read(1, k);
-  // this wave's reads of buffers 0 and 1 are done before its copies land there;
-  // the other waves' reads of their own slots need no wait (copy slot k*4 + wave)
+  // this wave's reads of its slots are done before its next copies land there
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  issue_tile_from(0, base_src(tile_row(0, blk0)));
-  issue_tile_from(1, ntiles > 1 ? base_src(tile_row(1, blk1)) : pool);
+  q_round(2, 0);
+  q_round(3, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // rounds 2 and 3 (and tiles 0 and 1)
 #pragma unroll
-  for (int k = 0; k < 9; ++k) qf[18 + k] = q_read(2, k);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  q_round(3, 2);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // round 3 (and the first tiles' copies)
+  for (int k = 0; k < 9; ++k) qf[18 + k] = q_read(0, k);
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
-    const bf16x8_t v = q_read(2, k);
+    const bf16x8_t v = q_read(1, k);
     if (27 + k < kQReg) qf[27 + k < kQReg ? 27 + k : 0] = v;
     else qpe[27 + k - kQReg < kQLds ? 27 + k - kQReg : 0] = v;
   }
   static_assert(kQReg == 32 && kQLds == 4, "four rounds of 9 k-blocks cover the 576 columns");
+  // every wave has read its query (and, in a packed plan, the scan in the
+  // tile table's area) before the areas below are written
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) goff_lds[k * kThreads + tid] = goff[k];
 
   // The first row of every tile of this split, for the later copies.
   int bad_tile = 0;
@@ -823,10 +868,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
 
   // ---- finish: this wave's 128 columns of every head, normalised by the
   // head's denominator (owned by the lanes that computed its scores) ----
+  // The lane's coordinates again, from its position in the wave, so that
+  // nothing derived from the thread index stays live across the tile loop
+  // (which holds every register; a value kept across it is spilled, and a
+  // reload here would wait for every store in flight).
+  {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int hf = lane >> 5, l32 = lane & 31, head = wave * 32 + l32;
   float l_lo, l_hi;
   wave_halves(l_run, &l_lo, &l_hi);
   const float l = l_lo + l_hi;
   if (hf == 0) l_heads[head] = l;
+  {  // the head's lse, before the outputs (nothing of it stays live past here)
+    float* out_lse = a.num_splits == 1 ? (a.lse ? a.lse + (size_t)b * kH + head : nullptr)
+                                       : a.part_lse + bs0 * kH + head;
+    if (out_lse && hf == 0) *out_lse = bad ? NAN : (m_ref + log2f(l)) * kLn2;
+  }
   __syncthreads();
   const size_t bs = (size_t)__builtin_amdgcn_readfirstlane(votes[8]);  // the partial slot
   // The outputs leave through LDS, one head block at a time: each wave
@@ -923,7 +980,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
       }
     }
   }
-  if (out_lse && hf == 0) *out_lse = bad ? NAN : (m_ref + log2f(l)) * kLn2;
+  }
 }
 
 // Merge the normalised partials of every split: lse = log sum_s exp(lse_s),
