@@ -334,6 +334,23 @@ def S_sub(case, seqs):
     return sub
 
 
+class Turns:
+    """Several steps run in turn, one per run (each captures its own graph)."""
+
+    per_graph = 1
+
+    def __init__(self, steps):
+        self.steps, self.k = steps, 0
+
+    def capture(self):
+        for s in self.steps:
+            s.capture()
+
+    def run(self, eager=False):
+        self.steps[self.k % len(self.steps)].run(eager=eager)
+        self.k += 1
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +370,10 @@ def main():
                          "object of them; not the benchmark line)")
     ap.add_argument("--row-major-weights", action="store_true",
                     help="time the step on the 4-bit weights as given (no tiled repack)")
+    ap.add_argument("--weight-sets", type=int, default=4,
+                    help="copies of the layer's weights used in turn, one per step (4 x 105 MB "
+                         "exceed the 256 MB last-level cache, so each step reads its weights "
+                         "from HBM, as in a model whose layers each bring their own)")
     ap.add_argument("--attn-cfg", type=int, choices=(2, 3, 4), default=None,
                     help="with --attn-only: just this workload (2: 1 x 4096, 3: 64 ragged "
                          "paged sequences, 4: 4 x 131072), e.g. for counter passes")
@@ -414,16 +435,27 @@ def main():
 
     # Steps per graph: the largest of 10, 5, 4, 2, 1 that divides --steps.
     step_graph = next(g for g in (10, 5, 4, 2, 1) if args.steps % g == 0)
-    ms_step, (settle_ms, settle_steps) = timed_steps(D.LayerStep(case, ns, per_graph=step_graph))
+    # Consecutive steps use the copies of the weights in turn: one set reused
+    # by every step would stay in the 256 MB last-level cache, since the cache
+    # rows' copies are non-temporal, and the projections would then be timed
+    # on cached weights, as no model with several layers runs them.
+    n_sets = max(1, args.weight_sets)
+    sets = D.weight_copies(ns, n_sets)
+    ms_step, (settle_ms, settle_steps) = timed_steps(
+        D.LayerStep(case, ns, per_graph=step_graph, sets=sets))
     assert int(ns.status.cpu()[0]) == 0
     ms_step_rm = None
     if ns is not ns_rm:
-        ms_step_rm, _ = timed_steps(D.LayerStep(case, ns_rm, per_graph=step_graph))
+        sets_rm = D.weight_copies(ns_rm, n_sets)
+        ms_step_rm, _ = timed_steps(D.LayerStep(case, ns_rm, per_graph=step_graph, sets=sets_rm))
+        del sets_rm
     # The same step as the four calls: cache_append and absorb_q on two streams
     # (independent), then decode_attn, then out_proj, replayed as one HIP graph
-    # (--eager: launched one by one on one stream).
-    step = D.GraphStep(case, ns, two_streams=not args.eager)
-    ms_step_calls, _ = timed_steps(step)
+    # per step (--eager: launched one by one on one stream); the weight sets in
+    # turn, one graph each.
+    four = [D.GraphStep(case, w, two_streams=not args.eager) for w in sets]
+    step = four[0]
+    ms_step_calls, _ = timed_steps(Turns(four))
     assert int(ns.status.cpu()[0]) == 0
 
     # The attention call timed where the step runs it: eager steps (the same
@@ -494,6 +526,8 @@ def main():
             "weights": "4-bit g64 as given (row-major)" if ns is ns_rm else
                        "4-bit g64 repacked once before timing into the tiled layout "
                        "(mla_repack_q4g64, MLA_Q4G64_T; same values, same results)",
+            "weight_sets": f"{n_sets} copies of the layer's weights (105 MB each) used in turn, "
+                           "one per step, so that each step reads its weights from HBM",
             "ms_per_step_row_major_weights": None if ms_step_rm is None else round(ms_step_rm, 4),
             "ms_per_step_four_calls": round(ms_step_calls, 4),
             "four_calls_launch": "eager, one stream" if args.eager else

@@ -4,6 +4,8 @@ Pure data movement (numpy -> torch device memory); no arithmetic of the method.
 """
 from __future__ import annotations
 
+import copy
+import dataclasses
 import types
 
 import numpy as np
@@ -90,6 +92,28 @@ def stage(case: Case, device="cuda", tiled: bool = False) -> types.SimpleNamespa
     if tiled:
         tile_weights(ns)
     return ns
+
+
+WEIGHT_NAMES = ("kv_a", "kv_a_norm", "q_a", "q_a_norm", "q_b", "kv_b", "o_proj")
+
+
+def weight_copies(ns, n: int) -> list:
+    """``ns`` and n - 1 copies of it whose weights live in buffers of their
+    own (the same values; every other buffer shared): steps that use them in
+    turn read their weights from memory as the layers of a model do, where a
+    single set reused every step would stay in the device caches."""
+    out = [ns]
+    for _ in range(n - 1):
+        c = copy.copy(ns)
+        for name in WEIGHT_NAMES:
+            w = getattr(ns, name)
+            if w is not None:
+                setattr(c, name, dataclasses.replace(
+                    w, data=w.data.clone(),
+                    scales=w.scales.clone() if w.scales is not None else None,
+                    biases=w.biases.clone() if w.biases is not None else None))
+        out.append(c)
+    return out
 
 
 def workspace(ns, split_rows: int = 0, device="cuda") -> torch.Tensor:
@@ -222,21 +246,27 @@ class LayerStep:
     """Decode steps as decode_layer calls (on the 4-bit layer: 9 kernels on one
     stream each), ``per_graph`` of them per run: one HIP graph holds that many
     steps, as a multi-layer model's graph holds one step per layer, so the
-    gap between graph launches is paid once per run.  Library calls only."""
+    gap between graph launches is paid once per run.  ``sets`` (from
+    weight_copies; default [ns]) are used in turn, one per step.  Library
+    calls only."""
 
-    def __init__(self, case: Case, ns, split_rows: int = 0, per_graph: int = 1):
+    def __init__(self, case: Case, ns, split_rows: int = 0, per_graph: int = 1, sets=None):
         self.case, self.ns, self.split_rows = case, ns, split_rows
         self.per_graph = per_graph
+        self.sets = list(sets) if sets else [ns]
         self.ws = layer_workspace(ns, split_rows)
         self.graph = None
+        self.i = 0
 
     def call(self):
-        run_layer(self.case, self.ns, self.split_rows, self.ws)
+        run_layer(self.case, self.sets[self.i % len(self.sets)], self.split_rows, self.ws)
+        self.i += 1
 
     def capture(self):
         """Record per_graph calls (run the call eagerly at least once before)."""
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
+        self.i = 0
         with torch.cuda.graph(self.graph):
             for _ in range(self.per_graph):
                 self.call()
