@@ -90,10 +90,14 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs a) {
 // consecutive outputs per token.  In a unit, lane-half hh holds k = 128u + 64hh
 // + 8st + (0..7) at MFMA step st; register r of a step pairs k-offsets r and
 // r + 4, which are the two nibbles ((word >> 4r) & 0x000F000F) of packed word
-// st, and the packed activations hold the same pairs.  A nibble becomes fp16
-// 1024 + q through the exponent bits 0x6400, then q * scale + bias in packed
-// fp16 arithmetic.  The next unit's loads are issued before the current unit
-// is multiplied.  The nw partial tiles are added in LDS in a fixed order.
+// st, and the packed activations hold the same pairs.  A nibble becomes an
+// exact fp16 integer plus q by bit operations alone: at mantissa bits 0-3
+// under the exponent bits 0x6400 it reads 1024 + q, at bits 4-7 under 0x5400
+// it reads 64 + q, so pairs 0 and 1 come from the word itself and pairs 2
+// and 3 from the word shifted by 8, one mask-and-or each; then q * scale +
+// bias in packed fp16 arithmetic.  The next unit's loads are issued before
+// the current unit is multiplied.  The nw partial tiles are added in LDS in a
+// fixed order.
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -106,16 +110,29 @@ struct Unit {  // one lane's share of a unit: 64 nibbles of its row, 64 activati
   uint4 x[8];
 };
 
+// (word & mask) | bits as one v_and_or_b32: gfx950's VOP3 form takes no
+// literal and one scalar operand, so the mask comes in a VGPR and the
+// exponent bits in an SGPR (the compiler emits a separate and and or).
+__device__ __forceinline__ uint32_t and_or(uint32_t word, uint32_t mask_v, uint32_t bits_s) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(word), "v"(mask_v), "s"(bits_s));
+  return r;
+}
+
 __device__ __forceinline__ f16x8_t dequant8(uint32_t word, f16x2_t s2, f16x2_t b2) {
   const f16x2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-  uint32_t r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-    const f16x2_t q = __builtin_bit_cast(f16x2_t, t) - k1024;
-    r[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
-  }
-  return __builtin_bit_cast(f16x8_t, uint4{r[0], r[1], r[2], r[3]});
+  const f16x2_t k64 = {(_Float16)64.f, (_Float16)64.f};
+  const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;  // nibbles 0 and 4, 1 and 5 of a word
+  const uint32_t w8 = word >> 8;                      // nibbles 2 and 6, 3 and 7 at those bits
+  const f16x2_t q0 = __builtin_bit_cast(f16x2_t, and_or(word, lo, 0x64006400u)) - k1024;
+  const f16x2_t q1 = __builtin_bit_cast(f16x2_t, and_or(word, hi, 0x54005400u)) - k64;
+  const f16x2_t q2 = __builtin_bit_cast(f16x2_t, and_or(w8, lo, 0x64006400u)) - k1024;
+  const f16x2_t q3 = __builtin_bit_cast(f16x2_t, and_or(w8, hi, 0x54005400u)) - k64;
+  const uint32_t r0 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q0, s2, b2));
+  const uint32_t r1 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q1, s2, b2));
+  const uint32_t r2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, b2));
+  const uint32_t r3 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q3, s2, b2));
+  return __builtin_bit_cast(f16x8_t, uint4{r0, r1, r2, r3});
 }
 
 // Q8_0: a lane's share of a unit is two 34-byte blocks of its row (64 of the
