@@ -1043,15 +1043,21 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
 
 // The same merge for the MFMA kernel's partials (H = 128, C = 512), stored as
 // fp16 times 2^-e_s: O_s = 2^e_s * (stored value), and 2^e_s folds into the
-// split's weight.  One wave per (sequence, head), 8 consecutive latent columns
-// per lane, so every split's partial row is one 1 KB coalesced read per wave;
-// four heads per workgroup.  Lane s % 64 forms split s's weight; the split
-// loop reads eight partial rows at a time, so a long context's many splits
-// are not one serial chain of loads.
+// split's weight.  A wave covers one (sequence, head), 8 consecutive latent
+// columns per lane, so every split's partial row is one 1 KB coalesced read;
+// the rows go eight at a time, one memory round trip per batch of 8 splits.
+// A query with more than 8 splits gets W = 2 or 4 waves per head (W from its
+// own number of splits, so a query's result does not depend on the rest of
+// the batch): wave w takes batches w, w + W, ..., and the W sums meet in LDS
+// and are added in wave order.  With up to 8 splits the workgroup's four
+// waves take four heads.  The grid holds 32 * W workgroups per query for the
+// W of the host's plan; a query with more waves per head than that (a device
+// plan with shorter splits) takes its heads in several rounds.  Lane s % 64
+// forms split s's weight.
 __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
+  __shared__ f32x4_t wsums[4][2][64];  // each wave's batch sums (columns 0-3, 4-7 of a lane)
   const int b = blockIdx.y;
-  const int h = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // Query b's ceil(len / rows) partials sit in consecutive slots from
   // part_first[b] (rows, chosen by the split kernel, in part_first[B]); no
   // workgroup wrote the slots of empty splits, so they are not read.
@@ -1063,96 +1069,133 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
     rows = a.part_first[a.B];
     first_raw = a.part_first[b];  // both loads in flight together
   }
-  const int S = len > 0 ? (len + rows - 1) / rows : 0;
+  const int S = __builtin_amdgcn_readfirstlane(len > 0 ? (len + rows - 1) / rows : 0);
+  const int nb = (S + 7) / 8;                         // batches of 8 splits
+  const int W = nb <= 1 ? 1 : (nb == 2 ? 2 : 4);      // waves per head (uniform)
   const size_t first = S > 0 ? (size_t)first_raw : 0;
-  const float* lse_s = a.part_lse + first * kH + h;  // stride kH over s
-  const float* exp_s = a.part_exp + first * kH + h;
-  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-  const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
-  const size_t sstride = (size_t)kH * kC;
+  // rounds of 4 (head, wave) tasks: the W waves of a head share a workgroup
+  for (int xb = blockIdx.x; xb < kH * W / 4; xb += gridDim.x) {
+    const int h = __builtin_amdgcn_readfirstlane((xb * 4 + wave) / W);
+    const int w = wave % W;
+    const float* lse_s = a.part_lse + first * kH + h;  // stride kH over s
+    const float* exp_s = a.part_exp + first * kH + h;
+    typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+    const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
+    const size_t sstride = (size_t)kH * kC;
 
-  // One memory round trip for everything that needs only the slot range: the
-  // first eight partial rows (the last one repeated past the end; slot 0 for
-  // an empty query, never used) and this lane's split lse and exponent.
-  f16x8_t v0[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int sj = j < S ? j : (S > 0 ? S - 1 : 0);  // uniform
-    v0[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * sstride);
-  }
-  const float ls0 = lane < S ? lse_s[(size_t)lane * kH] : -INFINITY;
-  const float ex0 = lane < S ? exp_s[(size_t)lane * kH] : 0.f;
-
-  float m = ls0;
-  bool nan_lse = ls0 != ls0;  // a bad table entry: NaN through the merge, as above
-  for (int s = 64 + lane; s < S; s += 64) {
-    const float l = lse_s[(size_t)s * kH];
-    m = fmaxf(m, l);
-    nan_lse |= l != l;
-  }
-  m = wave_max(m);
-  if (__ballot(nan_lse) != 0) m = NAN;
-  float* dst = a.v_combine + ((size_t)b * kH + h) * kC + lane * 8;
-  // the packed fp16 copy: this lane's 8 columns are one 16-byte chunk, in
-  // the pair order c0 c4 c1 c5 c2 c6 c3 c7
-  auto put_packed = [&](f32x4_t lo4, f32x4_t hi4) {
-    if (!a.vc_pk) return;
-    const f16x8_t hv = {(_Float16)lo4[0], (_Float16)hi4[0], (_Float16)lo4[1], (_Float16)hi4[1],
-                        (_Float16)lo4[2], (_Float16)hi4[2], (_Float16)lo4[3], (_Float16)hi4[3]};
-    *reinterpret_cast<f16x8_t*>(a.vc_pk + packed_index(h, b, lane * 8, a.B, kC)) = hv;
-  };
-  if (m == -INFINITY) {  // empty sequence
-    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    put_packed(f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f});
-    if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = -INFINITY;
-    return;
-  }
-  float wsum = expf(ls0 - m);  // 0 for lanes past the splits (ls0 = -inf)
-  for (int s = 64 + lane; s < S; s += 64) wsum += expf(lse_s[(size_t)s * kH] - m);
-  wsum = wave_sum(wsum);
-  const float inv = 1.0f / wsum;
-
-  f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    // this lane's split s0 + lane: its weight, 0 for an empty split (whose
-    // partial is never written and is not read)
-    float w = 0.f;
-    if (s0 + lane < S) {
-      const float ls = s0 == 0 ? ls0 : lse_s[(size_t)(s0 + lane) * kH];
-      const float ex = s0 == 0 ? ex0 : exp_s[(size_t)(s0 + lane) * kH];
-      if (ls != -INFINITY) w = ldexpf(expf(ls - m), (int)ex);
+    // One memory round trip for everything that needs only the slot range: this
+    // wave's first eight partial rows (batch w; the last row repeated past the
+    // end; slot 0 for an empty query, never used) and this lane's split lse and
+    // exponent.
+    f16x8_t v0[8];
+  #pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = 8 * w + j;
+      const int sj = s < S ? s : (S > 0 ? S - 1 : 0);  // uniform
+      v0[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * sstride);
     }
-    const int n = S - s0 < 64 ? S - s0 : 64;
-    for (int j0 = 0; j0 < n; j0 += 8) {
-      // eight loads in flight, no branches: a split past the end re-reads
-      // the last row and an empty split's unwritten row is read too, and
-      // both are dropped by a select (not multiplied by 0, which keeps NaN);
-      // the first eight rows were read with the lse
-      f16x8_t v[8];
-      float wj[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sj = j0 + j < n ? j0 + j : n - 1;  // uniform
-        wj[j] = j0 + j < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sj)) : 0.f;
-        v[j] = s0 + j0 == 0 ? v0[j] : *reinterpret_cast<const f16x8_t*>(src + (size_t)(s0 + sj) * sstride);
+    const float ls0 = lane < S ? lse_s[(size_t)lane * kH] : -INFINITY;
+    const float ex0 = lane < S ? exp_s[(size_t)lane * kH] : 0.f;
+
+    float m = ls0;
+    bool nan_lse = ls0 != ls0;  // a bad table entry: NaN through the merge, as above
+    for (int s = 64 + lane; s < S; s += 64) {
+      const float l = lse_s[(size_t)s * kH];
+      m = fmaxf(m, l);
+      nan_lse |= l != l;
+    }
+    m = wave_max(m);
+    if (__ballot(nan_lse) != 0) m = NAN;
+    const bool empty = m == -INFINITY;  // an empty sequence (the same for every head of it)
+    float wsum = empty ? 1.f : expf(ls0 - m);  // 0 for lanes past the splits (ls0 = -inf)
+    if (!empty)
+      for (int s = 64 + lane; s < S; s += 64) wsum += expf(lse_s[(size_t)s * kH] - m);
+    wsum = wave_sum(wsum);
+    const float inv = 1.0f / wsum;
+
+    f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
+    int chunk = -1;  // the 64 splits whose weights the lanes hold
+    float wl = 0.f;
+    // batch jb of this wave (eight rows v of splits 8 jb ...): the lane's
+    // weight for the batch's 64-split chunk, then the rows added in order;
+    // a split past the end re-read the last row and an empty split's
+    // unwritten row is read too, and both are dropped by a select (not
+    // multiplied by 0, which keeps NaN)
+    auto add_batch = [&](int jb, const f16x8_t (&v)[8]) {
+      const int s0 = 8 * jb;
+      if (s0 / 64 != chunk) {
+        // this lane's split 64 * chunk + lane: its weight, 0 for an empty split
+        chunk = s0 / 64;
+        const int sl = 64 * chunk + lane;
+        wl = 0.f;
+        if (sl < S) {
+          const float ls = chunk == 0 ? ls0 : lse_s[(size_t)sl * kH];
+          const float ex = chunk == 0 ? ex0 : exp_s[(size_t)sl * kH];
+          if (ls != -INFINITY) wl = ldexpf(expf(ls - m), (int)ex);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const f32x4_t l4 = lo + wj[j] * f32x4_t{(float)v[j][0], (float)v[j][1], (float)v[j][2], (float)v[j][3]};
-        const f32x4_t h4 = hi + wj[j] * f32x4_t{(float)v[j][4], (float)v[j][5], (float)v[j][6], (float)v[j][7]};
-        const bool use = wj[j] != 0.f;
+        const int sj = s0 + j;  // uniform
+        const float wj =
+            sj < S ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), sj & 63)) : 0.f;
+        const f32x4_t l4 = lo + wj * f32x4_t{(float)v[j][0], (float)v[j][1], (float)v[j][2], (float)v[j][3]};
+        const f32x4_t h4 = hi + wj * f32x4_t{(float)v[j][4], (float)v[j][5], (float)v[j][6], (float)v[j][7]};
+        const bool use = wj != 0.f;
         lo = use ? l4 : lo;
         hi = use ? h4 : hi;
       }
+    };
+    // the first batch came with the lse; the later ones, eight loads in
+    // flight each, no branches
+    if (!empty && w < nb) add_batch(w, v0);
+    for (int jb = w + W; jb < nb && !empty; jb += W) {
+      f16x8_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sj = 8 * jb + j < S ? 8 * jb + j : S - 1;  // uniform
+        v[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * sstride);
+      }
+      add_batch(jb, v);
     }
+    if (W > 1) {  // the head's W sums, added in wave order by its first wave
+      wsums[wave][0][lane] = lo;
+      wsums[wave][1][lane] = hi;
+      __syncthreads();
+      if (w == 0) {
+        lo = wsums[wave][0][lane];
+        hi = wsums[wave][1][lane];
+        for (int q = 1; q < W; ++q) {
+          lo = lo + wsums[wave + q][0][lane];
+          hi = hi + wsums[wave + q][1][lane];
+        }
+      }
+      __syncthreads();  // read before the next round writes them
+      if (w != 0) continue;
+    }
+    float* dst = a.v_combine + ((size_t)b * kH + h) * kC + lane * 8;
+    // the packed fp16 copy: this lane's 8 columns are one 16-byte chunk, in
+    // the pair order c0 c4 c1 c5 c2 c6 c3 c7
+    auto put_packed = [&](f32x4_t lo4, f32x4_t hi4) {
+      if (!a.vc_pk) return;
+      const f16x8_t hv = {(_Float16)lo4[0], (_Float16)hi4[0], (_Float16)lo4[1], (_Float16)hi4[1],
+                          (_Float16)lo4[2], (_Float16)hi4[2], (_Float16)lo4[3], (_Float16)hi4[3]};
+      *reinterpret_cast<f16x8_t*>(a.vc_pk + packed_index(h, b, lane * 8, a.B, kC)) = hv;
+    };
+    if (empty) {  // empty sequence
+      *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      put_packed(f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = -INFINITY;
+      continue;
+    }
+    lo = lo * inv;
+    hi = hi * inv;
+    *reinterpret_cast<f32x4_t*>(dst) = lo;
+    *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
+    put_packed(lo, hi);
+    if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = m + logf(wsum);
   }
-  lo = lo * inv;
-  hi = hi * inv;
-  *reinterpret_cast<f32x4_t*>(dst) = lo;
-  *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
-  put_packed(lo, hi);
-  if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = m + logf(wsum);
 }
 
 }  // namespace
@@ -1181,10 +1224,14 @@ hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
-  if (a.part_oh)
-    hipLaunchKernelGGL(attn_combine_f16_kernel, dim3(kH / 4, a.B), dim3(256), 0, s, a);
-  else
+  if (a.part_oh) {
+    // 32 * W workgroups per query for the waves per head of the host plan's
+    // splits (a query with more splits takes its heads in rounds)
+    const int nb = (a.num_splits + 7) / 8, W = nb <= 1 ? 1 : (nb == 2 ? 2 : 4);
+    hipLaunchKernelGGL(attn_combine_f16_kernel, dim3(kH / 4 * W, a.B), dim3(256), 0, s, a);
+  } else {
     hipLaunchKernelGGL(attn_combine_kernel, dim3((a.H + 1) / 2, a.B), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
