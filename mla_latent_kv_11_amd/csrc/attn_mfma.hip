@@ -1088,7 +1088,7 @@ __global__ void __launch_bounds__(256) attn_combine_f16_kernel(AttnArgs a) {
     // end; slot 0 for an empty query, never used) and this lane's split lse and
     // exponent.
     f16x8_t v0[8];
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int s = 8 * w + j;
       const int sj = s < S ? s : (S > 0 ? S - 1 : 0);  // uniform
