@@ -100,6 +100,36 @@ def test_attn_more_splits_than_one_weight_chunk():
     attn_check(vc, lse, rvc, rlse, "attention")
 
 
+@pytest.mark.parametrize("lens", [[1100, 300], [2300, 64]], ids=["w2", "w4"])
+def test_attn_merge_waves_per_head(lens):
+    # 128-row splits: 9 splits for the first sequence (two merge waves per
+    # head, one batch of 8 partial rows each after the first) and 18 (four
+    # waves, the third batch on the first wave)
+    case = S.make_case(4, lens=lens, paged=True, seed=29)
+    ns = D.stage(case)
+    print(f"merge waves per head: lens {lens}", flush=True)
+    vc, lse = attn_only(case, ns, 128)
+    rvc, rlse = oracle_attn(case)
+    attn_check(vc, lse, rvc, rlse, f"lens {lens}")
+
+
+def test_attn_merge_rounds_under_the_device_plan():
+    # the automatic plan on one long sequence among short ones: the host plan
+    # (sized for 64 sequences of the longest length) gives each query 4 splits,
+    # so the merge's grid has one wave per head; the device plan cuts 128-row
+    # splits from the lengths, 64 of them for the long sequence, whose heads
+    # then take four rounds of four-wave groups
+    lens = [8192] + [64] * 63
+    case = S.make_case(4, lens=lens, paged=True, seed=31)
+    ns = D.stage(case)
+    r_host, s_host = mla.attn_plan(ns.dims, len(lens), max(lens), 0)
+    assert s_host <= 8, (r_host, s_host)
+    print(f"merge rounds: host plan {r_host} rows x {s_host}", flush=True)
+    vc, lse = attn_only(case, ns, 0)
+    rvc, rlse = oracle_attn(case)
+    attn_check(vc, lse, rvc, rlse, "one long sequence among short ones")
+
+
 def repage(case, block, seed):
     """The same logical rows in a pool of ``block``-row blocks, randomly permuted."""
     import dataclasses
