@@ -543,6 +543,8 @@ static int absorb_impl(const mla_dims* d, int32_t B, const float* q_in, const ml
                                              g2.xp ? r.q_lat_pk : nullptr,
                                              g2.xp ? r.q_lat_exp : nullptr, s))))
       return st;
+    const AbsorbArgs ab = absorb_args(d, B, r.q_full, kv_b, rope, positions, q_abs);
+    if (qb_absorb_ok(g2, ab)) return hip_status(launch_qb_absorb(g2, ab, s));
     if ((st = hip_status(launch_gemm_nt(g2, 1, &splits, s)))) return st;
     q = r.q_full;
   }
@@ -823,8 +825,10 @@ static int layer_front_fused(const mla_dims* d, int32_t B, const float* x, const
   a.kv_splits = splits;
   qn.S = splits;
   if ((st = hip_status(launch_append_qnorm(a, qn, s)))) return st;
+  const AbsorbArgs ab = absorb_args(d, B, r.q_full, w->kv_b, w->rope, positions, q_abs);
+  if (qb_absorb_ok(g2, ab)) return hip_status(launch_qb_absorb(g2, ab, s));
   if ((st = hip_status(launch_gemm_nt(g2, 1, &splits, s)))) return st;
-  return hip_status(launch_absorb(absorb_args(d, B, r.q_full, w->kv_b, w->rope, positions, q_abs), s));
+  return hip_status(launch_absorb(ab, s));
 }
 
 size_t mla_layer_workspace_bytes(const mla_dims* d, int32_t B, int32_t max_len, int32_t split_rows) {

@@ -252,3 +252,9 @@ struct AbsorbArgs {
   int32_t B, H, N, R, V, C, cache_dtype;
 };
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s);
+// q_b (g: the 4-bit product of the packed q latent) and the absorb (a, reading
+// q from LDS instead of a.q) in one launch; qb_absorb_ok tells whether the
+// shapes and formats take it (4-bit q_b and W_UK, N 128, R 64, C <= 512,
+// q LoRA rank <= 1536).
+bool qb_absorb_ok(const GemmArgs& g, const AbsorbArgs& a);
+hipError_t launch_qb_absorb(const GemmArgs& g, const AbsorbArgs& a, hipStream_t s);

@@ -12,6 +12,7 @@
 //                     (turbospark deepseek2/attn.rs, encode_mla_absorb_q).
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "mla_common.h"
@@ -926,6 +927,283 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// q_b and the absorb of one head in one workgroup, for 4-bit q_b and W_UK with
+// q_nope 128, q_pe 64, a latent of at most 512 and a q LoRA rank of at most
+// 1536: q of the head never leaves LDS, and the q latent of a token tile is
+// read once per head instead of once per 32 rows of q_b.  grid (H, token
+// tiles of 32), 1024 threads, 160 KB of LDS:
+//   [0, 96 KB)       the token tile's packed q latent (LDS DMA), then
+//   [96, 120 KB)     the second K half's q_b tiles; from the absorb on
+//   [0, 128 KB)      W_UK of the head, fp16 [c][n]: 256 bytes per column, its
+//                    16-byte chunk k (n = 8k .. 8k + 7) at chunk k ^ (c % 16)
+//   [128, 152 KB)    q of the head, fp32 [token][192] (the first word of a
+//                    token's row later holds its q_nope exponent)
+//   [152, 160 KB)    x_exp of the tile's tokens, then q_nope times 2^-qe in
+//                    fp16, in the MFMA layout [step][lane][8]
+// The q latent is copied first, alone, so q_b starts as soon as it lands; the
+// weights stream in meanwhile.  Waves 0-11 compute q_b: wave w owns rows
+// 32 (w % 6) .. +31 of the head's 192 and K half w / 6 (the first half takes
+// the extra unit of an odd count), each unit multiplied as in the GEMM body.
+// The halves are added (first + second) and multiplied by 2^x_exp.  Then
+// waves 0-7 rotate q_pe, waves 8-11 find each token's q_nope exponent (as the
+// absorb kernel does) and pack the scaled fp16 operand, and every thread
+// dequantises its share of W_UK (rows 2 lane and 2 lane + 1 of columns
+// 32 wave .. +31, loaded with the q_b weights): one byte of each row (two
+// columns) becomes two fp16 pairs (row 2 lane, row 2 lane + 1) with one byte
+// permute, the nibble-under-exponent trick of the GEMM and one packed fma per
+// pair.  Last, wave w multiplies columns 32w .. 32w + 31 for the 32 tokens
+// with the W_UK columns as the M operand, so each lane holds four consecutive
+// columns of one token per MFMA row group and stores them in one 8- or
+// 16-byte write.
+// ---------------------------------------------------------------------------
+constexpr int kQaRows = 192, kQaMaxUnits = 12, kQaMaxC = 512;
+constexpr uint32_t kQaRed = kQaMaxUnits * 8192u;         // second-half q_b tiles
+constexpr uint32_t kQaQf = (uint32_t)kQaMaxC * 256u;     // q fp32 [32][192]
+constexpr uint32_t kQaA = kQaQf + 32u * kQaRows * 4u;    // x_exp, then the A operand
+constexpr uint32_t kQaLds = kQaA + 8192u;                // 163840
+
+// Byte offset in the W_UK area of the fp16 pair (n = 2np, 2np + 1) of column c.
+__device__ __forceinline__ uint32_t qa_wt_off(uint32_t c, uint32_t np) {
+  return c * 256u + (((np >> 2) ^ (c & 15u)) << 4) + ((np & 3u) << 2);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  MLA_LDS char* L = (MLA_LDS char*)smem;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)L;
+  const int h = blockIdx.x, b0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int units = g.K >> 7, u0 = (units + 1) >> 1;
+  const int W = a.C + a.R;
+  const bool qb = wave < 12;
+  const int t = wave % 6, half = wave / 6;  // q_b waves: row tile, K half
+  const int ub = half ? u0 : 0, nu = half ? units - u0 : u0;
+
+  // rope operands of waves 0-7: token tid / 16, pairs 2 (tid % 16) and +1
+  int pos = 0;
+  float if0 = 0.f, if1 = 0.f;
+  if (wave < 8) {
+    const int bb = b0 + (tid >> 4), i0 = 2 * (tid & 15);
+    pos = a.positions[bb < a.B ? bb : a.B - 1];
+    if0 = a.inv_freq[i0];
+    if1 = a.inv_freq[i0 + 1];
+  }
+  // The tile's packed activations are one contiguous run of units x 8 KB; copy
+  // c (1 KB, c = wave + 16 k) lands at LDS byte 1024 c (M0 + 16 * lane).
+  {
+    const char* src = reinterpret_cast<const char*>(g.xp) + (size_t)blockIdx.y * units * 8192;
+    for (int c = wave; c < units * 8; c += 16) {
+      const uint32_t m0 = lds0 + (uint32_t)c * 1024u, off = (uint32_t)c * 1024u + 16u * lane;
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :
+                   : "v"(off), "s"(src), "s"(m0)
+                   : "memory");
+    }
+  }
+  // The copies first have the memory system to themselves: q_b starts as
+  // soon as they land, while its weights stream in.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (wave == 15 && lane < 32) {
+    const int bb = b0 + lane;
+    *(MLA_LDS int*)(L + kQaA + 4u * lane) = bb < a.B ? g.x_exp[bb] : 0;
+  }
+  __syncthreads();  // the activations and x_exp are in LDS
+
+  // q_b weights of the wave's units (offsets as in the GEMM body; a unit past
+  // the wave's range re-reads its last one and is never used), then W_UK.
+  uint4 wq[6][2];
+  uint16_t sc[6], bi[6];
+  if (qb) {
+    const uint32_t wrow = (uint32_t)(h * kQaRows + 32 * t + l32);
+    const bool tiled = g.w.dtype == MLA_Q4G64_T;
+    const uint32_t tblk = (wrow >> 5) * (uint32_t)(g.w.cols >> 7), tlane = (wrow & 31u) + 32u * hh;
+    const uint32_t woff = tiled ? tblk * 2048u + 16u * tlane : wrow * (uint32_t)(g.w.cols >> 1) + 32u * hh;
+    const uint32_t soff = tiled ? tblk * 128u + 2u * tlane : wrow * (uint32_t)(g.w.cols >> 6) * 2u + 2u * hh;
+    const uint32_t wstep = tiled ? 2048u : 64u, whalf = tiled ? 1024u : 16u, sstep = tiled ? 128u : 4u;
+    const char* wbase = static_cast<const char*>(g.w.data);
+    const char* sbase = reinterpret_cast<const char*>(g.w.scales);
+    const char* bbase = reinterpret_cast<const char*>(g.w.biases);
+    const int ulast = nu > 0 ? ub + nu - 1 : 0;  // a half without units re-reads unit 0
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const uint32_t u = (uint32_t)(ub + i < ulast ? ub + i : ulast);
+      sc[i] = *reinterpret_cast<const uint16_t*>(sbase + soff + sstep * u);
+      bi[i] = *reinterpret_cast<const uint16_t*>(bbase + soff + sstep * u);
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const uint32_t u = (uint32_t)(ub + i < ulast ? ub + i : ulast);
+      wq[i][0] = *reinterpret_cast<const uint4*>(wbase + woff + wstep * u);
+      wq[i][1] = *reinterpret_cast<const uint4*>(wbase + woff + wstep * u + whalf);
+    }
+  }
+  // W_UK: thread (np = lane, cq = wave) owns rows 2np, 2np + 1 of columns
+  // 32 cq .. 32 cq + 31 (a wave past the latent re-reads the last columns).
+  uint4 wv[2];
+  uint16_t ws[2], wb[2];
+  {
+    const int cst = 32 * wave < a.C ? 32 * wave : a.C - 32;
+    const int64_t row0 = (int64_t)h * (a.N + a.V);
+    const bool tiled = a.kv_b.dtype == MLA_Q4G64_T;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int64_t row = row0 + 2 * lane + rr;
+      int64_t wqi, gi;  // uint4 index of the 32 columns, index of their group's scale
+      if (tiled) {
+        const int64_t blk = (row >> 5) * (a.kv_b.cols >> 7) + (cst >> 7);
+        const int64_t Ln = (row & 31) + 32 * ((cst >> 6) & 1);
+        wqi = blk * 128 + ((cst >> 5) & 1) * 64 + Ln;
+        gi = blk * 64 + Ln;
+      } else {
+        wqi = (row * (a.kv_b.cols >> 3) + (cst >> 3)) >> 2;
+        gi = row * (a.kv_b.cols >> 6) + (cst >> 6);
+      }
+      ws[rr] = a.kv_b.scales[gi];
+      wb[rr] = a.kv_b.biases[gi];
+      wv[rr] = static_cast<const uint4*>(a.kv_b.data)[wqi];
+    }
+  }
+
+  f32x16_t acc = f32x16_t{};
+  if (qb) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      if (i >= nu) break;
+      const uint32_t ubase = (uint32_t)(ub + i) * 8192u + 16u * lane;
+      // the empty asm keeps the conversions here, so that the compiler does
+      // not wait for the scale loads right after issuing them
+      uint32_t sr = sc[i], br = bi[i];
+      asm volatile("" : "+v"(sr), "+v"(br));
+      const _Float16 sh = (_Float16)bf16_to_f32((uint16_t)sr), bh = (_Float16)bf16_to_f32((uint16_t)br);
+      const f16x2_t s2 = {sh, sh}, b2 = {bh, bh};
+      const uint32_t words[8] = {wq[i][0].x, wq[i][0].y, wq[i][0].z, wq[i][0].w,
+                                 wq[i][1].x, wq[i][1].y, wq[i][1].z, wq[i][1].w};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const f16x8_t x = *(const MLA_LDS f16x8_t*)(L + ubase + 1024u * st);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, dequant8(words[st], s2, b2), acc, 0, 0, 0);
+      }
+    }
+    if (half) {
+      MLA_LDS float* red = (MLA_LDS float*)(L + kQaRed);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[(t * 16 + j) * 64 + lane] = acc[j];
+    }
+  }
+  __syncthreads();  // second halves written
+  if (qb && !half) {
+    const MLA_LDS float* red = (const MLA_LDS float*)(L + kQaRed);
+    const MLA_LDS int* xe = (const MLA_LDS int*)(L + kQaA);
+    MLA_LDS float* qf = (MLA_LDS float*)(L + kQaQf);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int tok = (j >> 2) * 8 + hh * 4 + (j & 3);
+      const float v = ldexpf(acc[j] + red[(t * 16 + j) * 64 + lane], xe[tok]);
+      qf[tok * kQaRows + 32 * t + l32] = b0 + tok < a.B ? v : 0.f;
+    }
+  }
+  __syncthreads();  // q of the head complete; the activation and q_b areas are free
+
+  float ro[4] = {0.f, 0.f, 0.f, 0.f};  // rotated q_pe of waves 0-7
+  if (wave < 8) {
+    const int tt = tid >> 4, i0 = 2 * (tid & 15);
+    const f32x4_t v = *(const MLA_LDS f32x4_t*)(L + kQaQf + (uint32_t)(tt * kQaRows + 128 + 2 * i0) * 4u);
+    rope_pair(v.x, v.y, pos, if0, a.rope_mscale, &ro[0], &ro[1]);
+    rope_pair(v.z, v.w, pos, if1, a.rope_mscale, &ro[2], &ro[3]);
+  } else if (wave < 12) {
+    // token tt's q_nope n = 16 gq .. 16 gq + 15; the 8 threads of a token
+    // are 8 consecutive lanes
+    const int q = tid - 512, tt = q >> 3, gq = q & 7;
+    const MLA_LDS f32x4_t* row = (const MLA_LDS f32x4_t*)(L + kQaQf + (uint32_t)(tt * kQaRows + 16 * gq) * 4u);
+    f32x4_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = row[e];
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      m = fmaxf(fmaxf(m, fmaxf(fabsf(v[e].x), fabsf(v[e].y))), fmaxf(fabsf(v[e].z), fabsf(v[e].w)));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    const int qe = f16_range_exp(m);
+    const float qsc = pow2f(-qe);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f32x4_t x0 = v[2 * e], x1 = v[2 * e + 1];
+      const f16x8_t qa = {(_Float16)(x0.x * qsc), (_Float16)(x0.y * qsc), (_Float16)(x0.z * qsc),
+                          (_Float16)(x0.w * qsc), (_Float16)(x1.x * qsc), (_Float16)(x1.y * qsc),
+                          (_Float16)(x1.z * qsc), (_Float16)(x1.w * qsc)};
+      const int st = 2 * (gq & 3) + e, hp = gq >> 2;  // n = 64 hp + 8 st + (0..7)
+      *(MLA_LDS f16x8_t*)(L + kQaA + (uint32_t)((st * 64 + 32 * hp + tt) * 16)) = qa;
+    }
+    // this thread alone read word 0 of the row, above
+    if (gq == 0) *(MLA_LDS int*)(L + kQaQf + (uint32_t)(tt * kQaRows) * 4u) = qe;
+  }
+  if (32 * wave < a.C) {
+    const f16x2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+    const f16x2_t k64 = {(_Float16)64.f, (_Float16)64.f};
+    uint32_t r0 = ws[0], r1 = ws[1], r2 = wb[0], r3 = wb[1];
+    asm volatile("" : "+v"(r0), "+v"(r1), "+v"(r2), "+v"(r3));
+    const f16x2_t s2 = {(_Float16)bf16_to_f32((uint16_t)r0), (_Float16)bf16_to_f32((uint16_t)r1)};
+    const f16x2_t b2 = {(_Float16)bf16_to_f32((uint16_t)r2), (_Float16)bf16_to_f32((uint16_t)r3)};
+    const uint32_t w0[4] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w};
+    const uint32_t w1[4] = {wv[1].x, wv[1].y, wv[1].z, wv[1].w};
+#pragma unroll
+    for (int kw = 0; kw < 4; ++kw)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        // bytes: row 2np's byte bb twice, then row 2np + 1's twice
+        const uint32_t sel = (uint32_t)bb * 0x0101u + (uint32_t)(4 + bb) * 0x01010000u;
+        const uint32_t p = __builtin_amdgcn_perm(w1[kw], w0[kw], sel);
+        const f16x2_t e0 = __builtin_bit_cast(f16x2_t, and_or(p, 0x000F000Fu, 0x64006400u)) - k1024;
+        const f16x2_t e1 = __builtin_bit_cast(f16x2_t, and_or(p, 0x00F000F0u, 0x54005400u)) - k64;
+        const uint32_t c = (uint32_t)(32 * wave + 8 * kw + 2 * bb);
+        *(MLA_LDS uint32_t*)(L + qa_wt_off(c, (uint32_t)lane)) =
+            __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(e0, s2, b2));
+        *(MLA_LDS uint32_t*)(L + qa_wt_off(c + 1u, (uint32_t)lane)) =
+            __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(e1, s2, b2));
+      }
+  }
+  __syncthreads();  // W_UK, the A operand and the exponents in LDS
+
+  // Four consecutive elements of a q_abs row at element e (16 or 8 bytes).
+  auto store4 = [&](int bb, int e, float v0, float v1, float v2, float v3) {
+    char* dst = static_cast<char*>(a.q_abs) + (((size_t)bb * a.H + h) * W + e) * sizeof(T);
+    if constexpr (std::is_same<T, float>::value) {
+      *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v0, v1, v2, v3};
+    } else {
+      const uint32_t lo = f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+      const uint32_t hi = f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16);
+      *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+    }
+  };
+  if (wave < 8) {
+    const int bb = b0 + (tid >> 4);
+    if (bb < a.B) store4(bb, a.C + 4 * (tid & 15), ro[0], ro[1], ro[2], ro[3]);
+  }
+  if (32 * wave >= a.C) return;
+  // W_UK rows are the M operand and the tokens N, so a lane ends with 16
+  // columns of its token l32: 32 wave + 8 (j / 4) + 4 hh + (j % 4).
+  const uint32_t c = (uint32_t)(32 * wave + l32);
+  acc = f32x16_t{};
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const f16x8_t wa = *(const MLA_LDS f16x8_t*)(L + c * 256u + ((((uint32_t)(8 * hh + st)) ^ (c & 15u)) << 4));
+    const f16x8_t qb8 = *(const MLA_LDS f16x8_t*)(L + kQaA + (uint32_t)((st * 64 + lane) * 16));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, qb8, acc, 0, 0, 0);
+  }
+  const int bb = b0 + l32;
+  if (bb >= a.B) return;
+  const int qe = *(const MLA_LDS int*)(L + kQaQf + (uint32_t)(l32 * kQaRows) * 4u);
+#pragma unroll
+  for (int jg = 0; jg < 4; ++jg)
+    store4(bb, 32 * wave + 8 * jg + 4 * hh, ldexpf(acc[4 * jg], qe), ldexpf(acc[4 * jg + 1], qe),
+           ldexpf(acc[4 * jg + 2], qe), ldexpf(acc[4 * jg + 3], qe));
+}
+
 }  // namespace
 
 namespace {
@@ -1200,5 +1478,43 @@ hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(absorb_kernel<float>, grid, dim3(kAbsC), smem, s, a);
   else
     hipLaunchKernelGGL(absorb_kernel<uint16_t>, grid, dim3(kAbsC), smem, s, a);
+  return hipGetLastError();
+}
+
+bool qb_absorb_ok(const GemmArgs& g, const AbsorbArgs& a) {
+  auto q4 = [](const WeightView& w) {
+    return w.dtype == MLA_Q4G64 || (w.dtype == MLA_Q4G64_T && w.rows % 32 == 0 && w.cols % 128 == 0);
+  };
+  return q4(g.w) && q4(a.kv_b) && gemm_mfma_ok(g) && g.xp && g.x_exp && !g.yp && g.Z == 1 &&
+         g.w_row0 == 0 && g.B == a.B && a.B > 0 && g.O == a.H * kQaRows && a.N == 128 &&
+         a.R == 64 && a.C >= 32 && a.C <= kQaMaxC && a.C % 32 == 0 && a.kv_b.cols == a.C &&
+         g.K >= 128 && g.K <= kQaMaxUnits * 128 && (reinterpret_cast<uintptr_t>(g.xp) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.kv_b.data) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.q_abs) & 15) == 0 &&
+         (a.cache_dtype == MLA_F32 || a.cache_dtype == MLA_BF16);
+}
+
+hipError_t launch_qb_absorb(const GemmArgs& g, const AbsorbArgs& a, hipStream_t s) {
+  if (!qb_absorb_ok(g, a)) return hipErrorInvalidValue;
+  const bool f32 = a.cache_dtype == MLA_F32;
+  const void* fn = f32 ? (const void*)qb_absorb_kernel<float> : (const void*)qb_absorb_kernel<uint16_t>;
+  // The dynamic LDS limit is raised once per device and instantiation.
+  static std::mutex mu;
+  static bool attr_set[64][2] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!attr_set[dev][f32]) {
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQaLds);
+      if (e != hipSuccess) return e;
+      attr_set[dev][f32] = true;
+    }
+  }
+  const dim3 grid(a.H, (a.B + 31) / 32);
+  if (f32) hipLaunchKernelGGL(qb_absorb_kernel<float>, grid, dim3(1024), kQaLds, s, g, a);
+  else hipLaunchKernelGGL(qb_absorb_kernel<uint16_t>, grid, dim3(1024), kQaLds, s, g, a);
   return hipGetLastError();
 }

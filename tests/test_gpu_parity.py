@@ -507,6 +507,51 @@ def test_absorb_q_latent_beyond_fp16_range():
     close_bf16(got * 2.0 ** -20, res["q_abs64"] * 2.0 ** -20, "q_abs / 2^20")
 
 
+def q_chain_case(heads, kv_lora, q_lora, batch, cache_dtype, seed):
+    """A 4-bit q chain with q_nope 128 and q_pe 64 at a latent width and q LoRA
+    rank other than the full-size ones (q_b and the absorb then run as one
+    launch over any rank of 1 to 12 units of 128 and any latent of 32 to 512)."""
+    rng = np.random.default_rng(seed)
+    H, N, R, V, C = heads, 128, 64, 128, kv_lora
+    d = S.Dims(num_heads=H, qk_nope=N, qk_rope=R, v_head=V, kv_lora=C, hidden=256,
+               q_lora=q_lora, cache_dtype=cache_dtype)
+    L = rng.integers(40, 400, size=batch).astype(np.int32)
+    pool, table = S.build_pool(rng, d, L, std=1.0, paged=True)
+    return S.Case("q-chain", d, S.Yarn(), batch, L, pool, table, None,
+                  x=rng.standard_normal((batch, d.hidden), dtype=np.float32),
+                  kv_a=S.draw_q4(rng, C + R, d.hidden),
+                  kv_a_norm=S.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(C)),
+                  q_a=S.draw_q4(rng, q_lora, d.hidden),
+                  q_a_norm=S.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(q_lora)),
+                  q_b=S.draw_q4(rng, H * (N + R), q_lora),
+                  kv_b=S.draw_q4(rng, H * (N + V), C),
+                  o_proj=S.draw_q4(rng, d.hidden, H * V))
+
+
+# (heads, latent, q LoRA rank, batch, cache dtype, tiled weights): one unit (the
+# second K half empty), an odd count (halves of 2 and 1), 5 units, two token
+# tiles with a ragged second one, a latent that leaves half the absorb's
+# waves without columns
+@pytest.mark.parametrize("H,C,ql,B,dt,tiled", [(16, 256, 128, 37, S.F32, False),
+                                               (16, 512, 384, 37, S.BF16, True),
+                                               (8, 256, 640, 5, S.BF16, False),
+                                               (8, 128, 1536, 33, S.F32, True)])
+def test_absorb_q_chain_other_shapes(H, C, ql, B, dt, tiled):
+    case = q_chain_case(H, C, ql, B, dt, seed=H + C + ql + B)
+    print(f"q chain: H {H} C {C} q_lora {ql} batch {B} tiled {tiled}", flush=True)
+    ns = D.stage(case, tiled=tiled)
+    ws = D.workspace(ns)
+    mla.absorb_q(ns.dims, ns.x, ns.kv_b, ns.inv_freq, ns.rope_mscale, ns.positions, ns.q_abs,
+                 ns.q_a, ns.q_a_norm, ns.q_b, ws)
+    sync()
+    res = O.decode_step(case)
+    got = O.widen(host(ns.q_abs), dt)
+    assert np.isfinite(got).all()
+    # the 4-bit chain multiplies fp16 operands whatever the cache dtype, so
+    # the bf16 bar is the one that applies to an fp32 q_abs as well
+    close_bf16(got, res["q_abs64"], "q_abs")
+
+
 @pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(lens=[50, 10], batch=2)),
                                     (5, dict(lens=[70, 200], batch=2)),
                                     (5, dict(lens=[64] * 40, batch=40))])
