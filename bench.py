@@ -4,7 +4,7 @@
 A step is one pass of the whole decode path over one batch: kv_a projection +
 latent RMSNorm + YaRN RoPE + paged append, the q chain + absorb, decode
 attention over the paged latent cache, the W_UV expansion and o_proj.  The
-step is one mla_decode_layer call (8 kernels on one stream), replayed from HIP
+step is one mla_decode_layer call (7 kernels on one stream), replayed from HIP
 graphs that hold up to 10 steps each, as a multi-layer model's graph holds one
 step per layer (``--eager``: the call launched every step); the same step as the
 four separate calls (append and absorb on two streams, one graph) is timed
@@ -414,7 +414,7 @@ def main():
     B = case.batch
     rows = int(case.lens.sum())
     # One step = one mla_decode_layer call (the fused front, attention with its
-    # merge, W_UV and o_proj: 8 kernels on one stream), replayed from HIP graphs
+    # merge, W_UV and o_proj: 7 kernels on one stream), replayed from HIP graphs
     # of step_graph steps (--eager: the call launched every step).
     def timed_steps(step):
         g = getattr(step, "per_graph", 1)  # steps per run
@@ -522,7 +522,7 @@ def main():
                         "bf16 paged cache (64-row blocks)",
             "launch": "one mla_decode_layer call per step, eager" if args.eager else
                       f"HIP graphs of {step_graph} steps, each step one mla_decode_layer call "
-                      "(8 kernels, one stream)",
+                      "(7 kernels, one stream)",
             "weights": "4-bit g64 as given (row-major)" if ns is ns_rm else
                        "4-bit g64 repacked once before timing into the tiled layout "
                        "(mla_repack_q4g64, MLA_Q4G64_T; same values, same results)",

@@ -562,13 +562,17 @@ int mla_absorb_q(const mla_dims* d, int32_t B, const float* q_in, const mla_weig
 // token_seq null: query b reads table row b (num_seqs = B).  dry: validate
 // only.  vc_pk: where the merge of the MFMA kernel's split partials also
 // writes v_combine in the packed fp16 layout of W_UV's input (*vc_written
-// says whether it did: only with more than one split on a bf16 cache).
+// says whether it did: only with more than one split on a bf16 cache).  uv:
+// W_UV of the step, which the merge then applies itself where the shapes
+// allow (*uv_done).
 static int attn_impl(const mla_dims* d, int32_t B, const void* q_abs, const mla_cache* cache,
                      const int32_t* token_seq, int32_t num_seqs, const int32_t* seq_lens,
                      int32_t max_len, float softmax_scale, int32_t split_rows, float* v_combine,
                      float* lse, void* ws, size_t ws_bytes, void* stream, bool dry,
-                     _Float16* vc_pk = nullptr, bool* vc_written = nullptr) {
+                     _Float16* vc_pk = nullptr, bool* vc_written = nullptr,
+                     const GemmArgs* uv = nullptr, bool* uv_done = nullptr) {
   if (vc_written) *vc_written = false;
+  if (uv_done) *uv_done = false;
   int st = dims_status(d);
   if (st) return st;
   if (B < 0 || max_len < 0) return MLA_ERR_DIMS;
@@ -636,7 +640,14 @@ static int attn_impl(const mla_dims* d, int32_t B, const void* q_abs, const mla_
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   st = hip_status(bf16 ? launch_attn_mfma_bf16(a, s) : launch_attn_generic_f32(a, s));
   if (st) return st;
-  if (splits > 1) st = hip_status(launch_attn_combine(a, s));
+  if (splits > 1) {
+    if (uv && uv_done && merge_uv_ok(a, *uv)) {
+      st = hip_status(launch_merge_uv(a, *uv, s));
+      *uv_done = st == MLA_OK;
+    } else {
+      st = hip_status(launch_attn_combine(a, s));
+    }
+  }
   return st;
 }
 
@@ -721,10 +732,12 @@ static void out_gemms(const mla_dims* d, int32_t B, const float* v_combine, cons
 }
 
 // dry: validate only.  vc_ready: the packed v_combine is already at the start
-// of the workspace (written by the attention merge).
+// of the workspace (written by the attention merge); uv_done: so are W_UV's
+// outputs, and only o_proj runs.
 static int out_proj_impl(const mla_dims* d, int32_t B, const float* v_combine,
                          const mla_weight* kv_b, const mla_weight* o_proj, float* out, void* ws,
-                         size_t ws_bytes, void* stream, bool dry, bool vc_ready) {
+                         size_t ws_bytes, void* stream, bool dry, bool vc_ready,
+                         bool uv_done = false) {
   int st = dims_status(d);
   if (st) return st;
   if (B < 0) return MLA_ERR_DIMS;
@@ -743,13 +756,13 @@ static int out_proj_impl(const mla_dims* d, int32_t B, const float* v_combine,
   if (mfma && (!ws || ws_bytes < ws_out(d, B))) return MLA_ERR_WORKSPACE;
   if (dry) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mfma && !vc_ready) {
+  if (mfma && !vc_ready && !uv_done) {
     if ((st = hip_status(launch_pack_f16(v_combine, (int64_t)H * C, C, H, B, C,
                                          const_cast<_Float16*>(g.xp), s))))
       return st;
   }
   int splits = 1;
-  if ((st = hip_status(launch_gemm_nt(g, 1, &splits, s)))) return st;
+  if (!uv_done && (st = hip_status(launch_gemm_nt(g, 1, &splits, s)))) return st;
   if (o_proj) st = hip_status(launch_gemm_nt(g2, 1, &splits, s));
   return st;
 }
@@ -880,15 +893,17 @@ int mla_decode_layer(const mla_dims* d, int32_t B, const float* x, const float* 
                        ws_b, wb, stream, false);
   }
   if (st) return st;
-  // the merge writes W_UV's packed input itself when W_UV runs on the MFMA path
+  // the merge writes W_UV's packed input itself when W_UV runs on the MFMA path,
+  // and applies W_UV too where merge_uv_ok allows
   GemmArgs g, g2;
   out_gemms(d, B, v_combine, w->kv_b, w->o_proj, out, ws_o, &g, &g2);
   _Float16* vc_pk = gemm_mfma_ok(g) ? const_cast<_Float16*>(g.xp) : nullptr;
-  bool packed = false;
+  bool packed = false, uv_done = false;
   if ((st = attn_impl(d, B, q_abs, cache, nullptr, B, seq_lens, max_len, softmax_scale, split_rows,
-                      v_combine, lse, ws_c, wc, stream, false, vc_pk, &packed)))
+                      v_combine, lse, ws_c, wc, stream, false, vc_pk, &packed, &g, &uv_done)))
     return st;
-  return out_proj_impl(d, B, v_combine, w->kv_b, w->o_proj, out, ws_o, wo, stream, false, packed);
+  return out_proj_impl(d, B, v_combine, w->kv_b, w->o_proj, out, ws_o, wo, stream, false, packed,
+                       uv_done);
 }
 
 }  // extern "C"

@@ -21,10 +21,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 // float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // to nearest, ties to even
+  const uint32_t quiet = (u >> 16) | 0x40u;                          // NaN: quieted, sign and payload kept
+  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 // Element loaders for the storage types a cache row / q_abs may have.
@@ -257,4 +257,9 @@ hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s);
 // shapes and formats take it (4-bit q_b and W_UK, N 128, R 64, C <= 512,
 // q LoRA rank <= 1536).
 bool qb_absorb_ok(const GemmArgs& g, const AbsorbArgs& a);
+// The attention merge of the MFMA kernel's split partials (a) and W_UV (g, one
+// unit of 128 k per wave, packed fp16 output for o_proj) in one launch, with
+// the same results as the merge kernel followed by the W_UV GEMM.
+bool merge_uv_ok(const AttnArgs& a, const GemmArgs& g);
+hipError_t launch_merge_uv(const AttnArgs& a, const GemmArgs& g, hipStream_t s);
 hipError_t launch_qb_absorb(const GemmArgs& g, const AbsorbArgs& a, hipStream_t s);

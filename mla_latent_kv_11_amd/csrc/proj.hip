@@ -1204,6 +1204,213 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
            ldexpf(acc[4 * jg + 2], qe), ldexpf(acc[4 * jg + 3], qe));
 }
 
+// ---------------------------------------------------------------------------
+// The attention merge and W_UV of one head in one workgroup (the decode layer
+// with more than one split, the MFMA kernel's fp16 partials, latent 512, 128
+// heads, 4-bit W_UV of 128 rows per head feeding o_proj on the MFMA path).
+// grid (128 heads, token tiles of 32), 1024 threads, 96 KB of LDS:
+//   [0, 32 KB)    the tile's merged v_combine of the head in fp16, in the
+//                 packed MFMA layout W_UV reads (unit, step, lane, 8 values)
+//   [32, 96 KB)   the 16 waves' W_UV partial tiles
+// Wave w merges queries b0 + w and b0 + w + 16 exactly as the merge kernel
+// does for one (query, head), also where that kernel gives a query of more
+// than 8 splits W = 2 or 4 waves per head: here one wave forms the W sums in
+// turn and adds them in the same order, so v_combine, lse and the fp16 values
+// carry the same bits.  Then wave w = 4t + u multiplies row tile t of the
+// head's W_UV by unit u of the packed values (its weights loaded before the
+// merge), and the four unit sums are added in unit order, as the GEMM with one
+// unit per wave adds its waves' tiles; the results go to o_proj's packed input.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMuvRed = 32768u, kMuvLds = kMuvRed + 16u * 4096u;
+
+__global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) {
+  constexpr int kH = 128, kC = 512;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  MLA_LDS char* L = (MLA_LDS char*)smem;
+  const int h = blockIdx.x, b0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = wave >> 2, u = wave & 3;
+
+  // W_UV weights of row tile t, unit u (offsets as in the GEMM body)
+  uint4 wq[2];
+  uint16_t sc, bi;
+  {
+    const uint32_t wrow = (uint32_t)(g.w_row0 + (int64_t)h * g.w_zrows + 32 * t + l32);
+    const bool tiled = g.w.dtype == MLA_Q4G64_T;
+    const uint32_t tblk = (wrow >> 5) * (uint32_t)(g.w.cols >> 7), tlane = (wrow & 31u) + 32u * hh;
+    const uint32_t woff = tiled ? tblk * 2048u + 16u * tlane : wrow * (uint32_t)(g.w.cols >> 1) + 32u * hh;
+    const uint32_t soff = tiled ? tblk * 128u + 2u * tlane : wrow * (uint32_t)(g.w.cols >> 6) * 2u + 2u * hh;
+    const uint32_t wo = woff + (tiled ? 2048u : 64u) * u, so = soff + (tiled ? 128u : 4u) * u;
+    const char* wbase = static_cast<const char*>(g.w.data);
+    wq[0] = *reinterpret_cast<const uint4*>(wbase + wo);
+    wq[1] = *reinterpret_cast<const uint4*>(wbase + wo + (tiled ? 1024u : 16u));
+    sc = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(g.w.scales) + so);
+    bi = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(g.w.biases) + so);
+  }
+
+  // this lane's 8 latent columns c = 8 lane sit in unit lane / 16, step lane % 8,
+  // lane half (lane / 8) % 2 of the packed layout
+  const uint32_t pk_off = (uint32_t)((((lane >> 4) * 8 + (lane & 7)) * 64 + 32 * ((lane >> 3) & 1)) * 16);
+  // Two memory round trips for both queries: their lengths (and the device
+  // plan's slots), then their split lse, exponents and first 8 partial rows.
+  int qS[2], qfirst[2];
+  {
+    const int rows = a.auto_slots > 0 ? a.part_first[a.B] : a.split_rows;
+    int len[2] = {0, 0}, fr[2] = {0, 0};
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      const int b = b0 + wave + 16 * qi;
+      if (b >= a.B) continue;
+      len[qi] = a.seq_lens[b];
+      fr[qi] = a.auto_slots > 0 ? a.part_first[b] : b * a.num_splits;
+    }
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      const int l = len[qi] < a.max_len ? len[qi] : a.max_len;
+      qS[qi] = __builtin_amdgcn_readfirstlane(l > 0 ? (l + rows - 1) / rows : 0);
+      qfirst[qi] = __builtin_amdgcn_readfirstlane(qS[qi] > 0 ? fr[qi] : 0);
+    }
+  }
+  float qls0[2], qex0[2];
+  f16x8_t qv0[2][8];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int S = qS[qi];
+    const size_t first = (size_t)qfirst[qi];
+    qls0[qi] = lane < S ? a.part_lse[(first + lane) * kH + h] : -INFINITY;
+    qex0[qi] = lane < S ? a.part_exp[(first + lane) * kH + h] : 0.f;
+    if (b0 + wave + 16 * qi >= a.B) continue;
+    const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sj = j < S ? j : (S > 0 ? S - 1 : 0);  // uniform
+      qv0[qi][j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * kH * kC);
+    }
+  }
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int tok = wave + 16 * qi, b = b0 + tok;
+    MLA_LDS f16x8_t* pk = (MLA_LDS f16x8_t*)(L + pk_off + 16u * tok);
+    if (b >= a.B) {
+      *pk = f16x8_t{};
+      continue;
+    }
+    const int S = qS[qi];
+    const int nb = (S + 7) / 8;
+    const int W = nb <= 1 ? 1 : (nb == 2 ? 2 : 4);  // the merge kernel's waves per head
+    const size_t first = (size_t)qfirst[qi];
+    const float* lse_s = a.part_lse + first * kH + h;
+    const float* exp_s = a.part_exp + first * kH + h;
+    const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
+    const size_t sstride = (size_t)kH * kC;
+
+    const float ls0 = qls0[qi], ex0 = qex0[qi];
+    float m = ls0;
+    bool nan_lse = ls0 != ls0;
+    for (int s = 64 + lane; s < S; s += 64) {
+      const float l = lse_s[(size_t)s * kH];
+      m = fmaxf(m, l);
+      nan_lse |= l != l;
+    }
+    m = wave_max(m);
+    if (__ballot(nan_lse) != 0) m = NAN;
+    const bool empty = m == -INFINITY;
+    float wsum = empty ? 1.f : expf(ls0 - m);
+    if (!empty)
+      for (int s = 64 + lane; s < S; s += 64) wsum += expf(lse_s[(size_t)s * kH] - m);
+    wsum = wave_sum(wsum);
+    const float inv = 1.0f / wsum;
+
+    f32x4_t lo_t{0.f, 0.f, 0.f, 0.f}, hi_t{0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < W && !empty; ++w) {
+      f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
+      int chunk = -1;
+      float wl = 0.f;
+      for (int jb = w; jb < nb; jb += W) {
+        // batch 0 came with the lse (and is visited first); later batches
+        // reuse its registers
+        f16x8_t (&v)[8] = qv0[qi];
+        if (jb > 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int sj = 8 * jb + j < S ? 8 * jb + j : S - 1;  // uniform
+            v[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * sstride);
+          }
+        }
+        const int s0 = 8 * jb;
+        if (s0 / 64 != chunk) {
+          chunk = s0 / 64;
+          const int sl = 64 * chunk + lane;
+          wl = 0.f;
+          if (sl < S) {
+            const float ls = chunk == 0 ? ls0 : lse_s[(size_t)sl * kH];
+            const float ex = chunk == 0 ? ex0 : exp_s[(size_t)sl * kH];
+            if (ls != -INFINITY) wl = ldexpf(expf(ls - m), (int)ex);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int sj = s0 + j;
+          const float wj =
+              sj < S ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), sj & 63)) : 0.f;
+          const f32x4_t l4 = lo + wj * f32x4_t{(float)v[j][0], (float)v[j][1], (float)v[j][2], (float)v[j][3]};
+          const f32x4_t h4 = hi + wj * f32x4_t{(float)v[j][4], (float)v[j][5], (float)v[j][6], (float)v[j][7]};
+          const bool use = wj != 0.f;
+          lo = use ? l4 : lo;
+          hi = use ? h4 : hi;
+        }
+      }
+      if (w == 0) {
+        lo_t = lo;
+        hi_t = hi;
+      } else {
+        lo_t = lo_t + lo;
+        hi_t = hi_t + hi;
+      }
+    }
+    float* dst = a.v_combine + ((size_t)b * kH + h) * kC + lane * 8;
+    if (empty) {
+      lo_t = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      hi_t = lo_t;
+      if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = -INFINITY;
+    } else {
+      lo_t = lo_t * inv;
+      hi_t = hi_t * inv;
+      if (a.lse && lane == 0) a.lse[(size_t)b * kH + h] = m + logf(wsum);
+    }
+    *reinterpret_cast<f32x4_t*>(dst) = lo_t;
+    *reinterpret_cast<f32x4_t*>(dst + 4) = hi_t;
+    *pk = f16x8_t{(_Float16)lo_t[0], (_Float16)hi_t[0], (_Float16)lo_t[1], (_Float16)hi_t[1],
+                  (_Float16)lo_t[2], (_Float16)hi_t[2], (_Float16)lo_t[3], (_Float16)hi_t[3]};
+  }
+  __syncthreads();  // the tile's packed v_combine is in LDS
+
+  uint32_t sr = sc, br = bi;
+  asm volatile("" : "+v"(sr), "+v"(br));
+  const _Float16 sh = (_Float16)bf16_to_f32((uint16_t)sr), bh = (_Float16)bf16_to_f32((uint16_t)br);
+  const f16x2_t s2 = {sh, sh}, b2 = {bh, bh};
+  const uint32_t words[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
+  f32x16_t acc = f32x16_t{};
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const f16x8_t x = *(const MLA_LDS f16x8_t*)(L + (uint32_t)(((u * 8 + st) * 64 + lane) * 16));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, dequant8(words[st], s2, b2), acc, 0, 0, 0);
+  }
+  MLA_LDS float* red = (MLA_LDS float*)(L + kMuvRed);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) red[((t * 4 + u) * 16 + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  for (int e = tid; e < 4096; e += 1024) {
+    const int tt = e >> 10, ln = e & 63, j = (e >> 6) & 15;
+    float v = 0.f;
+    for (int uu = 0; uu < 4; ++uu) v += red[((tt * 4 + uu) * 16 + j) * 64 + ln];
+    const int o = 32 * tt + (ln & 31);
+    const int tk = b0 + (j >> 2) * 8 + (ln >> 5) * 4 + (j & 3);
+    if (tk < g.B) g.yp[packed_index(0, tk, (int64_t)h * g.y_z + o, g.B, g.yp_K)] = (_Float16)v;
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -1516,5 +1723,34 @@ hipError_t launch_qb_absorb(const GemmArgs& g, const AbsorbArgs& a, hipStream_t 
   const dim3 grid(a.H, (a.B + 31) / 32);
   if (f32) hipLaunchKernelGGL(qb_absorb_kernel<float>, grid, dim3(1024), kQaLds, s, g, a);
   else hipLaunchKernelGGL(qb_absorb_kernel<uint16_t>, grid, dim3(1024), kQaLds, s, g, a);
+  return hipGetLastError();
+}
+
+bool merge_uv_ok(const AttnArgs& a, const GemmArgs& g) {
+  const bool q4 = g.w.dtype == MLA_Q4G64 ||
+                  (g.w.dtype == MLA_Q4G64_T && g.w.rows % 32 == 0 && g.w.cols % 128 == 0);
+  return q4 && a.part_oh && a.part_lse && a.part_exp && a.num_splits > 1 && a.H == 128 &&
+         a.C == 512 && g.Z == 128 && g.O == 128 && g.K == 512 && g.B == a.B && a.B > 0 && g.yp &&
+         g.xp && g.y_z == 128 && g.yp_K == 128 * 128 && gemm_mfma_ok(g);
+}
+
+hipError_t launch_merge_uv(const AttnArgs& a, const GemmArgs& g, hipStream_t s) {
+  if (!merge_uv_ok(a, g)) return hipErrorInvalidValue;
+  static std::mutex mu;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!attr_set[dev]) {
+      e = hipFuncSetAttribute((const void*)merge_uv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kMuvLds);
+      if (e != hipSuccess) return e;
+      attr_set[dev] = true;
+    }
+  }
+  hipLaunchKernelGGL(merge_uv_kernel, dim3(128, (a.B + 31) / 32), dim3(1024), kMuvLds, s, a, g);
   return hipGetLastError();
 }
