@@ -1208,18 +1208,23 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
 // The attention merge and W_UV of one head in one workgroup (the decode layer
 // with more than one split, the MFMA kernel's fp16 partials, latent 512, 128
 // heads, 4-bit W_UV of 128 rows per head feeding o_proj on the MFMA path).
-// grid (128 heads, token tiles of 32), 1024 threads, 96 KB of LDS:
+// grid (128 heads, 2 x token tiles of 32: each tile's two halves of 16
+// queries), 1024 threads, 96 KB of LDS:
 //   [0, 32 KB)    the tile's merged v_combine of the head in fp16, in the
-//                 packed MFMA layout W_UV reads (unit, step, lane, 8 values)
+//                 packed MFMA layout W_UV reads (unit, step, lane, 8 values);
+//                 the other half's 16 tokens are zeros
 //   [32, 96 KB)   the 16 waves' W_UV partial tiles
-// Wave w merges queries b0 + w and b0 + w + 16 exactly as the merge kernel
-// does for one (query, head), also where that kernel gives a query of more
+// Wave w merges query b0 + 16 half + w exactly as the merge kernel does for
+// one (query, head), also where that kernel gives a query of more
 // than 8 splits W = 2 or 4 waves per head: here one wave forms the W sums in
 // turn and adds them in the same order, so v_combine, lse and the fp16 values
 // carry the same bits.  Then wave w = 4t + u multiplies row tile t of the
 // head's W_UV by unit u of the packed values (its weights loaded before the
 // merge), and the four unit sums are added in unit order, as the GEMM with one
-// unit per wave adds its waves' tiles; the results go to o_proj's packed input.
+// unit per wave adds its waves' tiles; the half's results go to o_proj's
+// packed input (a token's row of the product does not depend on the others).
+// Two workgroups per head halve the partial rows each one reads, which bound
+// the merge; W_UV's 32 KB of weights per head are read twice.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMuvRed = 32768u, kMuvLds = kMuvRed + 16u * 4096u;
 
@@ -1227,7 +1232,7 @@ __global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) 
   constexpr int kH = 128, kC = 512;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   MLA_LDS char* L = (MLA_LDS char*)smem;
-  const int h = blockIdx.x, b0 = blockIdx.y * 32;
+  const int h = blockIdx.x, b0 = (blockIdx.y >> 1) * 32, half = blockIdx.y & 1;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = wave >> 2, u = wave & 3;
@@ -1252,60 +1257,35 @@ __global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) 
   // this lane's 8 latent columns c = 8 lane sit in unit lane / 16, step lane % 8,
   // lane half (lane / 8) % 2 of the packed layout
   const uint32_t pk_off = (uint32_t)((((lane >> 4) * 8 + (lane & 7)) * 64 + 32 * ((lane >> 3) & 1)) * 16);
-  // Two memory round trips for both queries: their lengths (and the device
-  // plan's slots), then their split lse, exponents and first 8 partial rows.
-  int qS[2], qfirst[2];
-  {
+  // the other half's tokens enter W_UV as zeros
+  *(MLA_LDS f16x8_t*)(L + pk_off + 16u * (16 * (1 - half) + wave)) = f16x8_t{};
+  // Two memory round trips: the query's length (and the device plan's
+  // slots), then its split lse, exponents and first 8 partial rows.
+  const int tok = 16 * half + wave, b = b0 + tok;
+  MLA_LDS f16x8_t* pk = (MLA_LDS f16x8_t*)(L + pk_off + 16u * tok);
+  if (b >= a.B) {
+    *pk = f16x8_t{};
+  } else {
+    int len = a.seq_lens[b];
     const int rows = a.auto_slots > 0 ? a.part_first[a.B] : a.split_rows;
-    int len[2] = {0, 0}, fr[2] = {0, 0};
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
-      const int b = b0 + wave + 16 * qi;
-      if (b >= a.B) continue;
-      len[qi] = a.seq_lens[b];
-      fr[qi] = a.auto_slots > 0 ? a.part_first[b] : b * a.num_splits;
-    }
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
-      const int l = len[qi] < a.max_len ? len[qi] : a.max_len;
-      qS[qi] = __builtin_amdgcn_readfirstlane(l > 0 ? (l + rows - 1) / rows : 0);
-      qfirst[qi] = __builtin_amdgcn_readfirstlane(qS[qi] > 0 ? fr[qi] : 0);
-    }
-  }
-  float qls0[2], qex0[2];
-  f16x8_t qv0[2][8];
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    const int S = qS[qi];
-    const size_t first = (size_t)qfirst[qi];
-    qls0[qi] = lane < S ? a.part_lse[(first + lane) * kH + h] : -INFINITY;
-    qex0[qi] = lane < S ? a.part_exp[(first + lane) * kH + h] : 0.f;
-    if (b0 + wave + 16 * qi >= a.B) continue;
+    const int fr = a.auto_slots > 0 ? a.part_first[b] : b * a.num_splits;
+    len = len < a.max_len ? len : a.max_len;
+    const int S = __builtin_amdgcn_readfirstlane(len > 0 ? (len + rows - 1) / rows : 0);
+    const size_t first = (size_t)__builtin_amdgcn_readfirstlane(S > 0 ? fr : 0);
+    const float ls0 = lane < S ? a.part_lse[(first + lane) * kH + h] : -INFINITY;
+    const float ex0 = lane < S ? a.part_exp[(first + lane) * kH + h] : 0.f;
     const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
+    const size_t sstride = (size_t)kH * kC;
+    f16x8_t v[8];  // batch 0, then the later batches in turn
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int sj = j < S ? j : (S > 0 ? S - 1 : 0);  // uniform
-      qv0[qi][j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * kH * kC);
+      v[j] = *reinterpret_cast<const f16x8_t*>(src + (size_t)sj * sstride);
     }
-  }
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    const int tok = wave + 16 * qi, b = b0 + tok;
-    MLA_LDS f16x8_t* pk = (MLA_LDS f16x8_t*)(L + pk_off + 16u * tok);
-    if (b >= a.B) {
-      *pk = f16x8_t{};
-      continue;
-    }
-    const int S = qS[qi];
     const int nb = (S + 7) / 8;
     const int W = nb <= 1 ? 1 : (nb == 2 ? 2 : 4);  // the merge kernel's waves per head
-    const size_t first = (size_t)qfirst[qi];
     const float* lse_s = a.part_lse + first * kH + h;
     const float* exp_s = a.part_exp + first * kH + h;
-    const _Float16* src = a.part_oh + (first * kH + h) * kC + lane * 8;
-    const size_t sstride = (size_t)kH * kC;
-
-    const float ls0 = qls0[qi], ex0 = qex0[qi];
     float m = ls0;
     bool nan_lse = ls0 != ls0;
     for (int s = 64 + lane; s < S; s += 64) {
@@ -1328,10 +1308,7 @@ __global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) 
       int chunk = -1;
       float wl = 0.f;
       for (int jb = w; jb < nb; jb += W) {
-        // batch 0 came with the lse (and is visited first); later batches
-        // reuse its registers
-        f16x8_t (&v)[8] = qv0[qi];
-        if (jb > 0) {
+        if (jb > 0) {  // batch 0 came with the lse and is visited first
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int sj = 8 * jb + j < S ? 8 * jb + j : S - 1;  // uniform
@@ -1406,8 +1383,9 @@ __global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) 
     float v = 0.f;
     for (int uu = 0; uu < 4; ++uu) v += red[((tt * 4 + uu) * 16 + j) * 64 + ln];
     const int o = 32 * tt + (ln & 31);
-    const int tk = b0 + (j >> 2) * 8 + (ln >> 5) * 4 + (j & 3);
-    if (tk < g.B) g.yp[packed_index(0, tk, (int64_t)h * g.y_z + o, g.B, g.yp_K)] = (_Float16)v;
+    const int tl = (j >> 2) * 8 + (ln >> 5) * 4 + (j & 3), tk = b0 + tl;
+    if (tk < g.B && (tl >> 4) == half)
+      g.yp[packed_index(0, tk, (int64_t)h * g.y_z + o, g.B, g.yp_K)] = (_Float16)v;
   }
 }
 
@@ -1751,6 +1729,6 @@ hipError_t launch_merge_uv(const AttnArgs& a, const GemmArgs& g, hipStream_t s) 
       attr_set[dev] = true;
     }
   }
-  hipLaunchKernelGGL(merge_uv_kernel, dim3(128, (a.B + 31) / 32), dim3(1024), kMuvLds, s, a, g);
+  hipLaunchKernelGGL(merge_uv_kernel, dim3(128, 2 * ((a.B + 31) / 32)), dim3(1024), kMuvLds, s, a, g);
   return hipGetLastError();
 }
