@@ -928,40 +928,44 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(AbsorbArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// q_b and the absorb of one head in one workgroup, for 4-bit q_b and W_UK with
-// q_nope 128, q_pe 64, a latent of at most 512 and a q LoRA rank of at most
-// 1536: q of the head never leaves LDS, and the q latent of a token tile is
-// read once per head instead of once per 32 rows of q_b.  grid (H, token
-// tiles of 32), 1024 threads, 160 KB of LDS:
-//   [0, 96 KB)       the token tile's packed q latent (LDS DMA), then
-//   [96, 120 KB)     the second K half's q_b tiles; from the absorb on
-//   [0, 128 KB)      W_UK of the head, fp16 [c][n]: 256 bytes per column, its
-//                    16-byte chunk k (n = 8k .. 8k + 7) at chunk k ^ (c % 16)
-//   [128, 152 KB)    q of the head, fp32 [token][192] (the first word of a
-//                    token's row later holds its q_nope exponent)
-//   [152, 160 KB)    x_exp of the tile's tokens, then q_nope times 2^-qe in
-//                    fp16, in the MFMA layout [step][lane][8]
-// The q latent is copied first, alone, so q_b starts as soon as it lands; the
-// weights stream in meanwhile.  Waves 0-11 compute q_b: wave w owns rows
-// 32 (w % 6) .. +31 of the head's 192 and K half w / 6 (the first half takes
-// the extra unit of an odd count), each unit multiplied as in the GEMM body.
-// The halves are added (first + second) and multiplied by 2^x_exp.  Then
-// waves 0-7 rotate q_pe, waves 8-11 find each token's q_nope exponent (as the
-// absorb kernel does) and pack the scaled fp16 operand, and every thread
-// dequantises its share of W_UK (rows 2 lane and 2 lane + 1 of columns
+// q_b and the absorb of one head, for 4-bit q_b and W_UK with q_nope 128, q_pe
+// 64, a latent of at most 512 and a q LoRA rank of at most 1536: q of the head
+// never leaves LDS, and the q latent of a token tile is read twice per head
+// instead of once per 32 rows of q_b.  grid (H, 2 x token tiles of 32), 1024
+// threads, 160 KB of LDS.  Each head has two workgroups: role A (even
+// blockIdx.y) computes q_nope (q_b's first four 32-row tiles) and the absorb,
+// role B (odd) q_pe (the last two tiles) and its rotation.  Both first copy
+// the token tile's packed q latent into LDS by LDS DMA, alone, so q_b starts
+// as soon as it lands while the weights stream in.  LDS, role A:
+//   [0, 96 KB)        the packed q latent, then
+//   [0, 64 KB)        the 16 waves' partial q_b tiles; from the absorb on
+//   [0, 128 KB)       W_UK of the head, fp16 [c][n]: 256 bytes per column, its
+//                     16-byte chunk k (n = 8k .. 8k + 7) at chunk k ^ (c % 16)
+//   [128, 136 KB)     x_exp of the tile's tokens, then q_nope times 2^-qe in
+//                     fp16, MFMA layout [step][lane][8]
+//   [144, 160 KB)     q_nope fp32 [token][128] (word 0 of a token's row later
+//                     holds its exponent)
+// role B: the packed q latent, the partial tiles at [0, 64 KB), x_exp at 128
+// KB, q_pe fp32 [token][64] at [64, 72 KB).
+// Wave w of role A owns rows 32 (w % 4) .. +31 of q_nope and K quarter w / 4
+// (of B: rows 128 + 32 (w % 2) and K eighth w / 2), each unit multiplied as in
+// the GEMM body; a tile's K parts are added in K order and multiplied by
+// 2^x_exp, by all threads (4 or 2 outputs each).  Role A then finds each token's q_nope exponent (as the absorb
+// kernel does) and packs the scaled fp16 operand on waves 0-3 while every
+// thread dequantises its share of W_UK (rows 2 lane and 2 lane + 1 of columns
 // 32 wave .. +31, loaded with the q_b weights): one byte of each row (two
 // columns) becomes two fp16 pairs (row 2 lane, row 2 lane + 1) with one byte
 // permute, the nibble-under-exponent trick of the GEMM and one packed fma per
 // pair.  Last, wave w multiplies columns 32w .. 32w + 31 for the 32 tokens
 // with the W_UK columns as the M operand, so each lane holds four consecutive
-// columns of one token per MFMA row group and stores them in one 8- or
-// 16-byte write.
+// columns of one token per MFMA row group and stores them in one 8- or 16-byte
+// write.  Role B rotates one (token, pair) per thread and stores it.
 // ---------------------------------------------------------------------------
 constexpr int kQaRows = 192, kQaMaxUnits = 12, kQaMaxC = 512;
-constexpr uint32_t kQaRed = kQaMaxUnits * 8192u;         // second-half q_b tiles
-constexpr uint32_t kQaQf = (uint32_t)kQaMaxC * 256u;     // q fp32 [32][192]
-constexpr uint32_t kQaA = kQaQf + 32u * kQaRows * 4u;    // x_exp, then the A operand
-constexpr uint32_t kQaLds = kQaA + 8192u;                // 163840
+constexpr uint32_t kQaPe = 65536u;                     // role B: q_pe fp32 [32][64]
+constexpr uint32_t kQaAop = (uint32_t)kQaMaxC * 256u;  // the absorb's q operand (8 KB)
+constexpr uint32_t kQaQf = kQaAop + 16384u;            // q_nope fp32 [32][128]
+constexpr uint32_t kQaLds = kQaQf + 32u * 128u * 4u;   // 163840
 
 // Byte offset in the W_UK area of the fp16 pair (n = 2np, 2np + 1) of column c.
 __device__ __forceinline__ uint32_t qa_wt_off(uint32_t c, uint32_t np) {
@@ -973,28 +977,33 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   MLA_LDS char* L = (MLA_LDS char*)smem;
   const uint32_t lds0 = (uint32_t)(uintptr_t)L;
-  const int h = blockIdx.x, b0 = blockIdx.y * 32;
+  const int h = blockIdx.x, tile = blockIdx.y >> 1, b0 = tile * 32;
+  const bool roleA = (blockIdx.y & 1) == 0;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int units = g.K >> 7, u0 = (units + 1) >> 1;
+  const int units = g.K >> 7;
   const int W = a.C + a.R;
-  const bool qb = wave < 12;
-  const int t = wave % 6, half = wave / 6;  // q_b waves: row tile, K half
-  const int ub = half ? u0 : 0, nu = half ? units - u0 : u0;
+  // this wave's q_b rows (of the head's 192) and K part
+  const int nparts = roleA ? 4 : 8;
+  const int t = roleA ? (wave & 3) : (wave & 1);
+  const int part = roleA ? (wave >> 2) : (wave >> 1);
+  const int per = (units + nparts - 1) / nparts;  // at most 3 (A) or 2 (B)
+  const int ub = part * per;
+  const int nu = units - ub < 0 ? 0 : (units - ub < per ? units - ub : per);
+  const int row0 = roleA ? 32 * t : 128 + 32 * t;
 
-  // rope operands of waves 0-7: token tid / 16, pairs 2 (tid % 16) and +1
+  // role B's rope operands: token tid / 32, pair tid % 32
   int pos = 0;
-  float if0 = 0.f, if1 = 0.f;
-  if (wave < 8) {
-    const int bb = b0 + (tid >> 4), i0 = 2 * (tid & 15);
+  float invf = 0.f;
+  if (!roleA) {
+    const int bb = b0 + (tid >> 5);
     pos = a.positions[bb < a.B ? bb : a.B - 1];
-    if0 = a.inv_freq[i0];
-    if1 = a.inv_freq[i0 + 1];
+    invf = a.inv_freq[tid & 31];
   }
   // The tile's packed activations are one contiguous run of units x 8 KB; copy
   // c (1 KB, c = wave + 16 k) lands at LDS byte 1024 c (M0 + 16 * lane).
   {
-    const char* src = reinterpret_cast<const char*>(g.xp) + (size_t)blockIdx.y * units * 8192;
+    const char* src = reinterpret_cast<const char*>(g.xp) + (size_t)tile * units * 8192;
     for (int c = wave; c < units * 8; c += 16) {
       const uint32_t m0 = lds0 + (uint32_t)c * 1024u, off = (uint32_t)c * 1024u + 16u * lane;
       asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -1003,21 +1012,20 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
                    : "memory");
     }
   }
-  // The copies first have the memory system to themselves: q_b starts as
-  // soon as they land, while its weights stream in.
+  // The copies first have the memory system to themselves.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (wave == 15 && lane < 32) {
     const int bb = b0 + lane;
-    *(MLA_LDS int*)(L + kQaA + 4u * lane) = bb < a.B ? g.x_exp[bb] : 0;
+    *(MLA_LDS int*)(L + kQaAop + 4u * lane) = bb < a.B ? g.x_exp[bb] : 0;
   }
   __syncthreads();  // the activations and x_exp are in LDS
 
   // q_b weights of the wave's units (offsets as in the GEMM body; a unit past
-  // the wave's range re-reads its last one and is never used), then W_UK.
-  uint4 wq[6][2];
-  uint16_t sc[6], bi[6];
-  if (qb) {
-    const uint32_t wrow = (uint32_t)(h * kQaRows + 32 * t + l32);
+  // the wave's range re-reads its last one, or unit 0, and is never used)
+  uint4 wq[3][2];
+  uint16_t sc[3], bi[3];
+  {
+    const uint32_t wrow = (uint32_t)(h * kQaRows + row0 + l32);
     const bool tiled = g.w.dtype == MLA_Q4G64_T;
     const uint32_t tblk = (wrow >> 5) * (uint32_t)(g.w.cols >> 7), tlane = (wrow & 31u) + 32u * hh;
     const uint32_t woff = tiled ? tblk * 2048u + 16u * tlane : wrow * (uint32_t)(g.w.cols >> 1) + 32u * hh;
@@ -1026,31 +1034,28 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
     const char* wbase = static_cast<const char*>(g.w.data);
     const char* sbase = reinterpret_cast<const char*>(g.w.scales);
     const char* bbase = reinterpret_cast<const char*>(g.w.biases);
-    const int ulast = nu > 0 ? ub + nu - 1 : 0;  // a half without units re-reads unit 0
+    const int ulast = nu > 0 ? ub + nu - 1 : 0;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const uint32_t u = (uint32_t)(ub + i < ulast ? ub + i : ulast);
-      sc[i] = *reinterpret_cast<const uint16_t*>(sbase + soff + sstep * u);
-      bi[i] = *reinterpret_cast<const uint16_t*>(bbase + soff + sstep * u);
-    }
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const uint32_t u = (uint32_t)(ub + i < ulast ? ub + i : ulast);
-      wq[i][0] = *reinterpret_cast<const uint4*>(wbase + woff + wstep * u);
-      wq[i][1] = *reinterpret_cast<const uint4*>(wbase + woff + wstep * u + whalf);
+    for (int i = 0; i < 3; ++i) {
+      if (!roleA && i == 2) break;
+      const uint32_t uu = (uint32_t)(ub + i < ulast ? ub + i : ulast);
+      sc[i] = *reinterpret_cast<const uint16_t*>(sbase + soff + sstep * uu);
+      bi[i] = *reinterpret_cast<const uint16_t*>(bbase + soff + sstep * uu);
+      wq[i][0] = *reinterpret_cast<const uint4*>(wbase + woff + wstep * uu);
+      wq[i][1] = *reinterpret_cast<const uint4*>(wbase + woff + wstep * uu + whalf);
     }
   }
-  // W_UK: thread (np = lane, cq = wave) owns rows 2np, 2np + 1 of columns
-  // 32 cq .. 32 cq + 31 (a wave past the latent re-reads the last columns).
+  // role A: W_UK, thread (np = lane, cq = wave) owns rows 2np, 2np + 1 of
+  // columns 32 cq .. 32 cq + 31 (a wave past the latent re-reads the last ones)
   uint4 wv[2];
   uint16_t ws[2], wb[2];
-  {
+  if (roleA) {
     const int cst = 32 * wave < a.C ? 32 * wave : a.C - 32;
-    const int64_t row0 = (int64_t)h * (a.N + a.V);
+    const int64_t wrow0 = (int64_t)h * (a.N + a.V);
     const bool tiled = a.kv_b.dtype == MLA_Q4G64_T;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      const int64_t row = row0 + 2 * lane + rr;
+      const int64_t row = wrow0 + 2 * lane + rr;
       int64_t wqi, gi;  // uint4 index of the 32 columns, index of their group's scale
       if (tiled) {
         const int64_t blk = (row >> 5) * (a.kv_b.cols >> 7) + (cst >> 7);
@@ -1068,56 +1073,88 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
   }
 
   f32x16_t acc = f32x16_t{};
-  if (qb) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      if (i >= nu) break;
-      const uint32_t ubase = (uint32_t)(ub + i) * 8192u + 16u * lane;
-      // the empty asm keeps the conversions here, so that the compiler does
-      // not wait for the scale loads right after issuing them
-      uint32_t sr = sc[i], br = bi[i];
-      asm volatile("" : "+v"(sr), "+v"(br));
-      const _Float16 sh = (_Float16)bf16_to_f32((uint16_t)sr), bh = (_Float16)bf16_to_f32((uint16_t)br);
-      const f16x2_t s2 = {sh, sh}, b2 = {bh, bh};
-      const uint32_t words[8] = {wq[i][0].x, wq[i][0].y, wq[i][0].z, wq[i][0].w,
-                                 wq[i][1].x, wq[i][1].y, wq[i][1].z, wq[i][1].w};
+  for (int i = 0; i < 3; ++i) {
+    if (i >= nu) break;
+    const uint32_t ubase = (uint32_t)(ub + i) * 8192u + 16u * lane;
+    // the empty asm keeps the conversions here, so that the compiler does
+    // not wait for the scale loads right after issuing them
+    uint32_t sr = sc[i], br = bi[i];
+    asm volatile("" : "+v"(sr), "+v"(br));
+    const _Float16 sh = (_Float16)bf16_to_f32((uint16_t)sr), bh = (_Float16)bf16_to_f32((uint16_t)br);
+    const f16x2_t s2 = {sh, sh}, b2 = {bh, bh};
+    const uint32_t words[8] = {wq[i][0].x, wq[i][0].y, wq[i][0].z, wq[i][0].w,
+                               wq[i][1].x, wq[i][1].y, wq[i][1].z, wq[i][1].w};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const f16x8_t x = *(const MLA_LDS f16x8_t*)(L + ubase + 1024u * st);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, dequant8(words[st], s2, b2), acc, 0, 0, 0);
-      }
-    }
-    if (half) {
-      MLA_LDS float* red = (MLA_LDS float*)(L + kQaRed);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) red[(t * 16 + j) * 64 + lane] = acc[j];
+    for (int st = 0; st < 8; ++st) {
+      const f16x8_t x = *(const MLA_LDS f16x8_t*)(L + ubase + 1024u * st);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, dequant8(words[st], s2, b2), acc, 0, 0, 0);
     }
   }
-  __syncthreads();  // second halves written
-  if (qb && !half) {
-    const MLA_LDS float* red = (const MLA_LDS float*)(L + kQaRed);
-    const MLA_LDS int* xe = (const MLA_LDS int*)(L + kQaA);
-    MLA_LDS float* qf = (MLA_LDS float*)(L + kQaQf);
+  __syncthreads();  // every product done: the activations are no longer read
+  MLA_LDS float* red = (MLA_LDS float*)L;
+  const int ntiles = roleA ? 4 : 2;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int tok = (j >> 2) * 8 + hh * 4 + (j & 3);
-      const float v = ldexpf(acc[j] + red[(t * 16 + j) * 64 + lane], xe[tok]);
-      qf[tok * kQaRows + 32 * t + l32] = b0 + tok < a.B ? v : 0.f;
+  for (int j = 0; j < 16; ++j) red[((part * ntiles + t) * 16 + j) * 64 + lane] = acc[j];
+  __syncthreads();  // partial tiles written
+  // q of the tile's tokens, K parts added in order, fp32: role A q_nope
+  // [token][128] at kQaQf, role B q_pe [token][64] at kQaPe.  Output o of the
+  // role's ntiles x 1024: tile o / 1024, then the MFMA tile's (j, lane).
+  const MLA_LDS int* xe = (const MLA_LDS int*)(L + kQaAop);
+  auto put_q = [&](int o, float v) {
+    const int tt = o >> 10, ln = o & 63, j = (o >> 6) & 15;
+    const int tok = (j >> 2) * 8 + (ln >> 5) * 4 + (j & 3);
+    MLA_LDS float* q = roleA ? (MLA_LDS float*)(L + kQaQf) : (MLA_LDS float*)(L + kQaPe);
+    const int pitch = roleA ? 128 : 64;
+    q[tok * pitch + 32 * tt + (ln & 31)] = b0 + tok < a.B ? ldexpf(v, xe[tok]) : 0.f;
+  };
+  auto slot = [&](int p, int o) {  // part p's value of output o
+    return red[(((p * ntiles + (o >> 10)) * 16 + ((o >> 6) & 15)) * 64) + (o & 63)];
+  };
+  if (roleA) {
+    float v[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) v[k][p] = slot(p, tid + 1024 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) put_q(tid + 1024 * k, ((v[k][0] + v[k][1]) + v[k][2]) + v[k][3]);
+  } else {
+    float v[2][8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) v[k][p] = slot(p, tid + 1024 * k);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float x = v[k][0];
+#pragma unroll
+      for (int p = 1; p < 8; ++p) x += v[k][p];
+      put_q(tid + 1024 * k, x);
     }
   }
-  __syncthreads();  // q of the head complete; the activation and q_b areas are free
+  __syncthreads();  // q complete; the activation and partial areas are free
 
-  float ro[4] = {0.f, 0.f, 0.f, 0.f};  // rotated q_pe of waves 0-7
-  if (wave < 8) {
-    const int tt = tid >> 4, i0 = 2 * (tid & 15);
-    const f32x4_t v = *(const MLA_LDS f32x4_t*)(L + kQaQf + (uint32_t)(tt * kQaRows + 128 + 2 * i0) * 4u);
-    rope_pair(v.x, v.y, pos, if0, a.rope_mscale, &ro[0], &ro[1]);
-    rope_pair(v.z, v.w, pos, if1, a.rope_mscale, &ro[2], &ro[3]);
-  } else if (wave < 12) {
+  if (!roleA) {
+    const int tt = tid >> 5, i = tid & 31, bb = b0 + tt;
+    if (bb >= a.B) return;
+    const float x = ((const MLA_LDS float*)(L + kQaPe))[tt * 64 + 2 * i];
+    const float y = ((const MLA_LDS float*)(L + kQaPe))[tt * 64 + 2 * i + 1];
+    float ox, oy;
+    rope_pair(x, y, pos, invf, a.rope_mscale, &ox, &oy);
+    char* dst = static_cast<char*>(a.q_abs) + (((size_t)bb * a.H + h) * W + a.C + 2 * i) * sizeof(T);
+    if constexpr (std::is_same<T, float>::value)
+      *reinterpret_cast<float2*>(dst) = float2{ox, oy};
+    else
+      *reinterpret_cast<uint32_t*>(dst) = f32_to_bf16(ox) | ((uint32_t)f32_to_bf16(oy) << 16);
+    return;
+  }
+
+  if (wave < 4) {
     // token tt's q_nope n = 16 gq .. 16 gq + 15; the 8 threads of a token
     // are 8 consecutive lanes
-    const int q = tid - 512, tt = q >> 3, gq = q & 7;
-    const MLA_LDS f32x4_t* row = (const MLA_LDS f32x4_t*)(L + kQaQf + (uint32_t)(tt * kQaRows + 16 * gq) * 4u);
+    const int tt = tid >> 3, gq = tid & 7;
+    const MLA_LDS f32x4_t* row = (const MLA_LDS f32x4_t*)(L + kQaQf + (uint32_t)(tt * 128 + 16 * gq) * 4u);
     f32x4_t v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = row[e];
@@ -1137,10 +1174,10 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
                           (_Float16)(x0.w * qsc), (_Float16)(x1.x * qsc), (_Float16)(x1.y * qsc),
                           (_Float16)(x1.z * qsc), (_Float16)(x1.w * qsc)};
       const int st = 2 * (gq & 3) + e, hp = gq >> 2;  // n = 64 hp + 8 st + (0..7)
-      *(MLA_LDS f16x8_t*)(L + kQaA + (uint32_t)((st * 64 + 32 * hp + tt) * 16)) = qa;
+      *(MLA_LDS f16x8_t*)(L + kQaAop + (uint32_t)((st * 64 + 32 * hp + tt) * 16)) = qa;
     }
     // this thread alone read word 0 of the row, above
-    if (gq == 0) *(MLA_LDS int*)(L + kQaQf + (uint32_t)(tt * kQaRows) * 4u) = qe;
+    if (gq == 0) *(MLA_LDS int*)(L + kQaQf + (uint32_t)(tt * 128) * 4u) = qe;
   }
   if (32 * wave < a.C) {
     const f16x2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
@@ -1167,23 +1204,8 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
             __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(e1, s2, b2));
       }
   }
-  __syncthreads();  // W_UK, the A operand and the exponents in LDS
+  __syncthreads();  // W_UK, the q operand and the exponents in LDS
 
-  // Four consecutive elements of a q_abs row at element e (16 or 8 bytes).
-  auto store4 = [&](int bb, int e, float v0, float v1, float v2, float v3) {
-    char* dst = static_cast<char*>(a.q_abs) + (((size_t)bb * a.H + h) * W + e) * sizeof(T);
-    if constexpr (std::is_same<T, float>::value) {
-      *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v0, v1, v2, v3};
-    } else {
-      const uint32_t lo = f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
-      const uint32_t hi = f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16);
-      *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
-    }
-  };
-  if (wave < 8) {
-    const int bb = b0 + (tid >> 4);
-    if (bb < a.B) store4(bb, a.C + 4 * (tid & 15), ro[0], ro[1], ro[2], ro[3]);
-  }
   if (32 * wave >= a.C) return;
   // W_UK rows are the M operand and the tokens N, so a lane ends with 16
   // columns of its token l32: 32 wave + 8 (j / 4) + 4 hh + (j % 4).
@@ -1192,16 +1214,26 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
     const f16x8_t wa = *(const MLA_LDS f16x8_t*)(L + c * 256u + ((((uint32_t)(8 * hh + st)) ^ (c & 15u)) << 4));
-    const f16x8_t qb8 = *(const MLA_LDS f16x8_t*)(L + kQaA + (uint32_t)((st * 64 + lane) * 16));
+    const f16x8_t qb8 = *(const MLA_LDS f16x8_t*)(L + kQaAop + (uint32_t)((st * 64 + lane) * 16));
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, qb8, acc, 0, 0, 0);
   }
   const int bb = b0 + l32;
   if (bb >= a.B) return;
-  const int qe = *(const MLA_LDS int*)(L + kQaQf + (uint32_t)(l32 * kQaRows) * 4u);
+  const int qe = *(const MLA_LDS int*)(L + kQaQf + (uint32_t)(l32 * 128) * 4u);
 #pragma unroll
-  for (int jg = 0; jg < 4; ++jg)
-    store4(bb, 32 * wave + 8 * jg + 4 * hh, ldexpf(acc[4 * jg], qe), ldexpf(acc[4 * jg + 1], qe),
-           ldexpf(acc[4 * jg + 2], qe), ldexpf(acc[4 * jg + 3], qe));
+  for (int jg = 0; jg < 4; ++jg) {
+    const float v0 = ldexpf(acc[4 * jg], qe), v1 = ldexpf(acc[4 * jg + 1], qe);
+    const float v2 = ldexpf(acc[4 * jg + 2], qe), v3 = ldexpf(acc[4 * jg + 3], qe);
+    char* dst = static_cast<char*>(a.q_abs) +
+                (((size_t)bb * a.H + h) * W + 32 * wave + 8 * jg + 4 * hh) * sizeof(T);
+    if constexpr (std::is_same<T, float>::value) {
+      *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v0, v1, v2, v3};
+    } else {
+      const uint32_t lo = f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+      const uint32_t hi = f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16);
+      *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1698,7 +1730,7 @@ hipError_t launch_qb_absorb(const GemmArgs& g, const AbsorbArgs& a, hipStream_t 
       attr_set[dev][f32] = true;
     }
   }
-  const dim3 grid(a.H, (a.B + 31) / 32);
+  const dim3 grid(a.H, 2 * ((a.B + 31) / 32));
   if (f32) hipLaunchKernelGGL(qb_absorb_kernel<float>, grid, dim3(1024), kQaLds, s, g, a);
   else hipLaunchKernelGGL(qb_absorb_kernel<uint16_t>, grid, dim3(1024), kQaLds, s, g, a);
   return hipGetLastError();
