@@ -304,11 +304,12 @@ typedef struct mla_layer {
  * can be captured into a HIP graph.  With 4-bit kv_a and q_a of one type
  * (hidden > 0, q_a given) the front runs fused: one fp16 pack of x, kv_a and
  * q_a in one launch, the append and the q-latent RMSNorm in one launch; and
- * when W_UV runs on the MFMA path with more than one split the attention
- * merge also writes W_UV's packed input.  On the 4-bit DeepSeek-V3 layer that
- * is 9 kernels: pack, kv_a + q_a, append + norm, q_b, absorb, attention,
- * merge, W_UV, o_proj.  Each fused launch does the same arithmetic as the
- * separate calls.
+ * when W_UV (4-bit, 128 rows per head) runs on the MFMA path with more than
+ * one split, the attention merge and W_UV run as one launch.  On the 4-bit
+ * DeepSeek-V3 layer that is 7 kernels: pack, kv_a + q_a, append + norm,
+ * q_b + absorb (as in mla_absorb_q), attention, merge + W_UV, o_proj.  Each
+ * fused launch does the same arithmetic as the separate calls, so the results
+ * equal theirs bit for bit.
  * Errors: those of the four calls, all checked before anything is enqueued. */
 int mla_decode_layer(const mla_dims* dims, int32_t batch, const float* x, const float* q_in,
                      const mla_layer* layer, const int32_t* positions, const mla_cache* cache,

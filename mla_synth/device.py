@@ -243,7 +243,7 @@ class GraphStep:
 
 
 class LayerStep:
-    """Decode steps as decode_layer calls (on the 4-bit layer: 9 kernels on one
+    """Decode steps as decode_layer calls (on the 4-bit layer: 7 kernels on one
     stream each), ``per_graph`` of them per run: one HIP graph holds that many
     steps, as a multi-layer model's graph holds one step per layer, so the
     gap between graph launches is paid once per run.  ``sets`` (from
