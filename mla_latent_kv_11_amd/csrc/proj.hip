@@ -1268,6 +1268,15 @@ __global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = wave >> 2, u = wave & 3;
+  const int tok = 16 * half + wave, b = b0 + tok;
+  // the query's length (and the device plan's slots) first: loads complete in
+  // issue order, so these do not wait behind the weights
+  int len = 0, fr = 0;
+  const int rows = a.auto_slots > 0 ? a.part_first[a.B] : a.split_rows;
+  if (b < a.B) {
+    len = a.seq_lens[b];
+    fr = a.auto_slots > 0 ? a.part_first[b] : b * a.num_splits;
+  }
 
   // W_UV weights of row tile t, unit u (offsets as in the GEMM body)
   uint4 wq[2];
@@ -1291,16 +1300,12 @@ __global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) 
   const uint32_t pk_off = (uint32_t)((((lane >> 4) * 8 + (lane & 7)) * 64 + 32 * ((lane >> 3) & 1)) * 16);
   // the other half's tokens enter W_UV as zeros
   *(MLA_LDS f16x8_t*)(L + pk_off + 16u * (16 * (1 - half) + wave)) = f16x8_t{};
-  // Two memory round trips: the query's length (and the device plan's
-  // slots), then its split lse, exponents and first 8 partial rows.
-  const int tok = 16 * half + wave, b = b0 + tok;
+  // Two memory round trips: the length, then the query's split lse,
+  // exponents and first 8 partial rows.
   MLA_LDS f16x8_t* pk = (MLA_LDS f16x8_t*)(L + pk_off + 16u * tok);
   if (b >= a.B) {
     *pk = f16x8_t{};
   } else {
-    int len = a.seq_lens[b];
-    const int rows = a.auto_slots > 0 ? a.part_first[a.B] : a.split_rows;
-    const int fr = a.auto_slots > 0 ? a.part_first[b] : b * a.num_splits;
     len = len < a.max_len ? len : a.max_len;
     const int S = __builtin_amdgcn_readfirstlane(len > 0 ? (len + rows - 1) / rows : 0);
     const size_t first = (size_t)__builtin_amdgcn_readfirstlane(S > 0 ? fr : 0);
@@ -1410,14 +1415,26 @@ __global__ void __launch_bounds__(1024) merge_uv_kernel(AttnArgs a, GemmArgs g) 
 #pragma unroll
   for (int j = 0; j < 16; ++j) red[((t * 4 + u) * 16 + j) * 64 + lane] = acc[j];
   __syncthreads();
-  for (int e = tid; e < 4096; e += 1024) {
-    const int tt = e >> 10, ln = e & 63, j = (e >> 6) & 15;
-    float v = 0.f;
-    for (int uu = 0; uu < 4; ++uu) v += red[((tt * 4 + uu) * 16 + j) * 64 + ln];
-    const int o = 32 * tt + (ln & 31);
-    const int tl = (j >> 2) * 8 + (ln >> 5) * 4 + (j & 3), tk = b0 + tl;
-    if (tk < g.B && (tl >> 4) == half)
-      g.yp[packed_index(0, tk, (int64_t)h * g.y_z + o, g.B, g.yp_K)] = (_Float16)v;
+  // Thread e < 256 adds the unit sums (in unit order, from 0) of rows 8 og ..
+  // 8 og + 7 of the half's token tl and writes them as one 16-byte chunk of
+  // o_proj's packed input (pair order k0 k4 k1 k5 k2 k6 k3 k7).
+  if (tid < 256) {
+    const int tl = 16 * half + (tid >> 4), og = tid & 15, tk = b0 + tl;
+    if (tk < g.B) {
+      const int tt = og >> 2, ln0 = 8 * (og & 3) + 32 * ((tl >> 2) & 1);
+      const int j = (tl >> 3) * 4 + (tl & 3);
+      f32x4_t lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const MLA_LDS f32x4_t* rp = (const MLA_LDS f32x4_t*)(red + ((tt * 4 + uu) * 16 + j) * 64 + ln0);
+        lo = lo + rp[0];
+        hi = hi + rp[1];
+      }
+      const f16x8_t hv = {(_Float16)lo[0], (_Float16)hi[0], (_Float16)lo[1], (_Float16)hi[1],
+                          (_Float16)lo[2], (_Float16)hi[2], (_Float16)lo[3], (_Float16)hi[3]};
+      *reinterpret_cast<f16x8_t*>(g.yp + packed_index(0, tk, (int64_t)h * g.y_z + 32 * tt + 8 * (og & 3),
+                                                      g.B, g.yp_K)) = hv;
+    }
   }
 }
 
