@@ -49,8 +49,12 @@ CASES = [
     (3, dict(batch=3, lens=[1024, 1500, 2049])),
     (5, dict(batch=2, lens=[300, 1100])),
     (5, dict(batch=33, lens=[int(v) for v in np.random.default_rng(41).integers(1, 3000, 33)])),
+    # one long query among two: the device plan cuts it into far more than 8
+    # splits, so the layer's merge forms the merge kernel's 4 per-wave sums in
+    # turn, over several batches each and past the first 64 splits
+    (5, dict(batch=2, lens=[8192, 64])),
 ]
-IDS = ["1", "2", "3", "5-b2", "5-b33"]
+IDS = ["1", "2", "3", "5-b2", "5-b33", "5-long"]
 
 
 @pytest.mark.parametrize("cfg,kw", CASES, ids=IDS)
