@@ -10,6 +10,11 @@
 //                     cache row; moeflux mla_attn_forward.rs, the cache append).
 //  absorb_kernel      q' = W_UK^T q_nope and RoPE(q_pe) packed as q_abs rows
 //                     (turbospark deepseek2/attn.rs, encode_mla_absorb_q).
+//  qb_absorb_kernel   q_b and the absorb in one launch, q kept in LDS (moeflux
+//                     mla_attn_forward.rs, the Q chain into mla_q_prime_4bit).
+//  merge_uv_kernel    the split-K merge of decode attention and W_UV in one
+//                     launch (moeflux mla_attn_forward.rs, mla_sdpa_folded's
+//                     output expanded per head).
 #include <math.h>
 
 #include <mutex>
@@ -1237,7 +1242,7 @@ __global__ void __launch_bounds__(1024) qb_absorb_kernel(GemmArgs g, AbsorbArgs 
 }
 
 // ---------------------------------------------------------------------------
-// The attention merge and W_UV of one head in one workgroup (the decode layer
+// The attention merge and W_UV of one head in two workgroups (the decode layer
 // with more than one split, the MFMA kernel's fp16 partials, latent 512, 128
 // heads, 4-bit W_UV of 128 rows per head feeding o_proj on the MFMA path).
 // grid (128 heads, 2 x token tiles of 32: each tile's two halves of 16
